@@ -1,0 +1,14 @@
+"""CPU fp64 oracle for DiT sequence-parallel attention (test infrastructure).
+
+Only tests/, ``__graft_entry__.smoke()`` and bench.py's ``cpu_baseline`` leg
+may import this package.  The HIP library and its Python binding never do.
+"""
+from .ref import (attention, attention_rows, probabilities, split_kv, merge,
+                  ring_attention, shard_tokens, seq2head, head2seq,
+                  unshard_tokens, ulysses_attention, ulysses_send_bytes_per_rank,
+                  default_scale)
+
+__all__ = ["attention", "attention_rows", "probabilities", "split_kv", "merge",
+           "ring_attention", "shard_tokens", "seq2head", "head2seq",
+           "unshard_tokens", "ulysses_attention", "ulysses_send_bytes_per_rank",
+           "default_scale"]

@@ -1,0 +1,196 @@
+"""Plain CPU oracle for one GPU's share of DiT sequence-parallel attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only tests/, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of bench.py use it.  It shares no code with the HIP
+library or its Python binding.
+
+Everything is float64 numpy on the exact input values (bf16 inputs are
+widened exactly; fp32 inputs likewise).  It is written to be checked by eye,
+not to be fast: each function is the plain definition of what the hot path
+computes, with no fusion or reordering beyond what that definition states.
+
+Sources (web pages; sections named, not quoted):
+* "Multi-GPU parallelism: spreading one step over several cards" (AI infra
+  handbook), section "Sequence parallelism: Ulysses and Ring": the four-card
+  Ulysses simulation listing (token partition, ``all_to_all_heads``,
+  per-card attention, ``all_to_all_tokens``, concatenation), and the Ring
+  paragraph (local attention per K/V block, merged with a log-sum-exp).
+* "Feat: USP sequence parallelism (Ulysses x Ring) via SequenceParallelPlan"
+  (miles_diffusion pull request), Design / "Ring kernel selection": ring
+  kernels must return the LSE; "Limitations": no mask, dropout, causal flag
+  or explicit scale under SP, head count divisible by the Ulysses degree,
+  sequence length divisible by the SP degree.
+
+Readings where the pages are silent:
+* LSE is the natural log of sum_j exp(scale * q.k_j) (the scale included).
+* Default scale is 1/sqrt(D), the scaled_dot_product_attention default the
+  simulation relies on.
+* Merge: blocks whose LSE is -inf get weight 0; if every block is -inf the
+  result is O = 0, LSE = -inf (cannot happen without a mask).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)
+
+
+# --------------------------------------------------------------------------
+# Attention (handbook, "Sequence parallelism: Ulysses and Ring": every card
+# runs full, non-causal scaled-dot-product attention over its heads).
+# --------------------------------------------------------------------------
+def attention(q, k, v, scale=None, row_block=256):
+    """softmax(scale * Q K^T) V and its per-row log-sum-exp.
+
+    q: [B,H,Nq,D], k and v: [B,H,Nkv,D].  Returns (O [B,H,Nq,D] float64,
+    LSE [B,H,Nq] float64).  For each row: S = scale * q K^T, m = max S,
+    E = exp(S - m), l = sum E, O = (E V) / l, LSE = m + ln l.  Rows are
+    independent; they are taken ``row_block`` at a time only to bound memory.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, Nq, D = q.shape
+    scale = default_scale(D) if scale is None else float(scale)
+    O = np.empty((B, H, Nq, v.shape[-1]), dtype=np.float64)
+    L = np.empty((B, H, Nq), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, Nq, row_block):
+                r1 = min(Nq, r0 + row_block)
+                S = scale * (q[b, h, r0:r1] @ k[b, h].T)
+                m = S.max(axis=1, keepdims=True)
+                E = np.exp(S - m)
+                l = E.sum(axis=1, keepdims=True)
+                O[b, h, r0:r1] = (E @ v[b, h]) / l
+                L[b, h, r0:r1] = m[:, 0] + np.log(l[:, 0])
+    return O, L
+
+
+def attention_rows(q, k, v, rows, scale=None):
+    """``attention`` for the query rows ``rows`` only (same rows in every head).
+
+    Returns (O [B,H,len(rows),D], LSE [B,H,len(rows)]).
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    return attention(np.asarray(q)[:, :, rows], k, v, scale)
+
+
+def probabilities(q, k, scale=None):
+    """The softmax matrix softmax(scale * Q K^T) itself, [B,H,Nq,Nkv]."""
+    q, k = _f64(q), _f64(k)
+    scale = default_scale(q.shape[-1]) if scale is None else float(scale)
+    S = scale * np.einsum("bhnd,bhmd->bhnm", q, k)
+    E = np.exp(S - S.max(axis=-1, keepdims=True))
+    return E / E.sum(axis=-1, keepdims=True)
+
+
+# --------------------------------------------------------------------------
+# Ring share (handbook, Ring paragraph: attention over each arriving K/V block,
+# merged by log-sum-exp; pull request, "Ring kernel selection": the block
+# kernel returns its LSE so the merge is exact).
+# --------------------------------------------------------------------------
+def split_kv(k, v, nblk):
+    """Contiguous token blocks of K and V: block i holds tokens
+    [i*Nkv/nblk, (i+1)*Nkv/nblk)."""
+    Nkv = k.shape[2]
+    if Nkv % nblk:
+        raise ValueError("Nkv must divide into nblk blocks")
+    s = Nkv // nblk
+    return [(k[:, :, i * s:(i + 1) * s], v[:, :, i * s:(i + 1) * s]) for i in range(nblk)]
+
+
+def merge(o_parts, lse_parts):
+    """Exact log-sum-exp merge of attention over disjoint key blocks.
+
+    o_parts: [nblk,B,H,N,D], lse_parts: [nblk,B,H,N].
+    M = max_i LSE_i; LSE = M + ln sum_i exp(LSE_i - M); O = sum_i exp(LSE_i - LSE) O_i.
+    """
+    o_parts, lse_parts = _f64(o_parts), _f64(lse_parts)
+    M = lse_parts.max(axis=0)
+    finite = np.isfinite(M)
+    Msafe = np.where(finite, M, 0.0)
+    w_un = np.where(np.isfinite(lse_parts), np.exp(lse_parts - Msafe[None]), 0.0)
+    tot = w_un.sum(axis=0)
+    lse = np.where(finite, Msafe + np.log(np.where(finite, tot, 1.0)), -np.inf)
+    w = np.where(finite[None], w_un / np.where(finite, tot, 1.0)[None], 0.0)
+    O = (w[..., None] * o_parts).sum(axis=0)
+    return O, lse
+
+
+def ring_attention(q, k, v, nblk, scale=None):
+    """Attention as a ring rank computes it: per-block partials, then merge."""
+    parts = [attention(q, kb, vb, scale) for kb, vb in split_kv(k, v, nblk)]
+    return merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+
+
+# --------------------------------------------------------------------------
+# Ulysses layout exchange on one device (handbook simulation listing:
+# ``all_to_all_heads`` / ``all_to_all_tokens``).  Buffers are rank-stacked:
+# index 0 is the rank.  Pure data movement, exact in any dtype.
+# --------------------------------------------------------------------------
+def shard_tokens(x, P):
+    """[B,H,N,D] -> [P,B,H,N/P,D]: rank r holds every head of tokens
+    [r*N/P, (r+1)*N/P)."""
+    x = np.asarray(x)
+    N = x.shape[2]
+    if N % P:
+        raise ValueError("N must be divisible by P")
+    s = N // P
+    return np.stack([x[:, :, r * s:(r + 1) * s] for r in range(P)])
+
+
+def seq2head(shards):
+    """[P,B,H,N/P,D] token shards -> [P,B,H/P,N,D] head groups.
+
+    Rank r gathers head group r (heads [r*H/P, (r+1)*H/P)) from every rank s
+    and concatenates them along tokens in rank order s = 0..P-1.
+    """
+    shards = np.asarray(shards)
+    P, B, H = shards.shape[:3]
+    if H % P:
+        raise ValueError("H must be divisible by P")
+    g = H // P
+    return np.stack([np.concatenate([shards[s][:, r * g:(r + 1) * g] for s in range(P)], axis=2)
+                     for r in range(P)])
+
+
+def head2seq(groups):
+    """[P,B,H/P,N,D] head groups -> [P,B,H,N/P,D] token shards (inverse of seq2head).
+
+    Rank s gathers token slice s ([s*N/P, (s+1)*N/P)) from every rank r and
+    concatenates them along heads in rank order r = 0..P-1.
+    """
+    groups = np.asarray(groups)
+    P, B, g, N = groups.shape[:4]
+    if N % P:
+        raise ValueError("N must be divisible by P")
+    s_len = N // P
+    return np.stack([np.concatenate([groups[r][:, :, s * s_len:(s + 1) * s_len] for r in range(P)], axis=1)
+                     for s in range(P)])
+
+
+def unshard_tokens(shards):
+    """[P,B,H,N/P,D] -> [B,H,N,D]: concatenate the token shards in rank order."""
+    return np.concatenate(list(np.asarray(shards)), axis=2)
+
+
+def ulysses_attention(q, k, v, P, scale=None):
+    """The whole simulated Ulysses round trip: shard by tokens, exchange to
+    head groups, attention per rank, exchange back, concatenate tokens."""
+    qh, kh, vh = (seq2head(shard_tokens(t, P)) for t in (q, k, v))
+    outs = np.stack([attention(qh[r], kh[r], vh[r], scale)[0] for r in range(P)])
+    return unshard_tokens(head2seq(outs))
+
+
+def ulysses_send_bytes_per_rank(B, H, N, D, P, elem_bytes, ntensors=3):
+    """Bytes one rank sends in one seq->head exchange of ``ntensors`` tensors:
+    it keeps 1/P of each [B,H,N/P,D] shard and sends the other (P-1)/P."""
+    return ntensors * B * H * (N // P) * D * elem_bytes * (P - 1) // P
