@@ -1,0 +1,223 @@
+"""Benchmark of the DiT sequence-parallel attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-ring]
+
+One step is the Ulysses round trip of one P=4 sequence-parallel attention
+layer of a Wan-shaped tensor [1,40,32768,128] bf16, run on one GPU:
+  1. ulysses_seq2head on q, k and v ([4][1,40,8192,128] -> [4][1,10,32768,128]);
+  2. dit_attn_fwd with LSE on each of the 4 head groups, B1 H10 N32768 D128;
+  3. ulysses_head2seq on the outputs.
+Inputs are resident in HBM before the timed region.  `value` is the
+attention FLOPs of the step (4 * 4*B*H*N^2*D) over the step's wall time.
+
+The ring leg (K/V in 4 blocks of 8192: four dit_attn_fwd_block calls with
+float32 partials, then dit_attn_merge, B1 H40 N32768 D128) is timed after the
+steps and reported under "legs"; it is not part of `value`.
+
+The roofline object is for the dominant kernel, the attention forward: its
+algorithmic FLOPs per launch over its average launch duration, measured with
+events on the launch stream around every attention launch of the timed steps.
+cpu_baseline times the fp64 CPU oracle on a bounded sample of the same
+workload (query rows of the 10-head share against all 32768 keys).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak, B1 H10 N32768 D128 bf16"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBPS = 8000.0
+B, H_FULL, N, D, P = 1, 40, 32768, 128, 4
+H = H_FULL // P
+
+
+def attn_flops(b, h, nq, nkv, d):
+    return 4.0 * b * h * nq * nkv * d
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ring", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(qb, kb, vb, target_s):
+    """Time the fp64 oracle on query rows of the 10-head share (all 32768 keys)."""
+    import concurrent.futures as cf
+
+    import oracle
+    import datagen
+    from threadpoolctl import threadpool_limits
+    cores = min(16, len(os.sched_getaffinity(0)))
+    f64 = lambda b: datagen.bf16_to_f32(b).astype(np.float64)
+    k64 = [f64(kb[:, h:h + 1]) for h in range(H)]
+    v64 = [f64(vb[:, h:h + 1]) for h in range(H)]
+
+    def run(rows_per_head):
+        rows = np.arange(rows_per_head) * (N // rows_per_head)
+        tasks = [(h, rows[i:i + 64]) for h in range(H) for i in range(0, len(rows), 64)]
+
+        def one(task):
+            h, r = task
+            return oracle.attention_rows(f64(qb[:, h:h + 1]), k64[h], v64[h], r)
+
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            with cf.ThreadPoolExecutor(max_workers=cores) as ex:
+                list(ex.map(one, tasks))
+            return time.perf_counter() - t0
+
+    probe = run(64)                      # 64 rows per head: calibrates the sample size
+    rows_per_head = int(min(N, max(64, 64 * round(target_s / max(probe, 1e-3)))))
+    rows_per_head = 64 * max(1, rows_per_head // 64)
+    dt = run(rows_per_head)
+    flops = attn_flops(1, H, rows_per_head, N, D)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows_per_head} query rows x {H} heads against all {N} keys "
+                      f"(fp64 numpy, {len(range(0, rows_per_head, 64)) * H} tasks of 64 rows "
+                      f"on {cores} threads, BLAS 1 thread each), {dt:.1f} s",
+            "seconds": dt, "flops": flops}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(no collectives or multi-GPU sharding are built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import datagen
+    import diffusion_transformer_attention_amd as dta
+    dta.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    print("[bench] generating the seed-2 [1,40,32768,128] draw", file=sys.stderr, flush=True)
+    qb, kb, vb = datagen.workload_inputs("ulysses_share")
+    to_dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+    full = [to_dev(x) for x in (qb, kb, vb)]
+    # rank s's token slice [s*N/P, (s+1)*N/P) of every head: the input each rank holds
+    shards = [torch.stack(t.chunk(P, dim=2)).contiguous() for t in full]
+    groups = [torch.empty((P, B, H, N, D), device=dev, dtype=torch.bfloat16) for _ in range(3)]
+    outs = torch.empty((P, B, H, N, D), device=dev, dtype=torch.bfloat16)
+    lses = torch.empty((P, B, H, N), device=dev, dtype=torch.float32)
+    back = torch.empty((P, B, H_FULL, N // P, D), device=dev, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    ev = []
+
+    def step(record):
+        for s, g in zip(shards, groups):
+            dta.ulysses_seq2head(s, out=g)
+        for r in range(P):
+            if record:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            dta.dit_attn_fwd(groups[0][r], groups[1][r], groups[2][r], out=outs[r], lse=lses[r])
+            if record:
+                e1.record(stream)
+                ev.append((e0, e1))
+        dta.ulysses_head2seq(outs, out=back)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    print("[bench] timed steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    attn_avg_ms = float(np.mean(attn_ms))
+    flops_launch = attn_flops(B, H, N, N, D)
+    value = P * flops_launch / (ms_per_step * 1e-3) / 1e12
+    achieved = flops_launch / (attn_avg_ms * 1e-3) / 1e12
+
+    # permute legs, timed alone (bytes moved = read + write of one tensor)
+    def time_it(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    perm_bytes = 2.0 * B * H_FULL * N * D * 2
+    s2h_ms = time_it(lambda: dta.ulysses_seq2head(shards[0], out=groups[0]))
+    h2s_ms = time_it(lambda: dta.ulysses_head2seq(outs, out=back))
+    legs = {"attn_fwd_ms_avg": attn_avg_ms, "attn_fwd_ms_min": float(np.min(attn_ms)),
+            "seq2head_ms": s2h_ms, "seq2head_GBps": perm_bytes / (s2h_ms * 1e-3) / 1e9,
+            "head2seq_ms": h2s_ms, "head2seq_GBps": perm_bytes / (h2s_ms * 1e-3) / 1e9}
+
+    if not args.no_ring:
+        print("[bench] ring leg", file=sys.stderr, flush=True)
+        nblk, s = 4, N // 4
+        kblk = [full[1][:, :, i * s:(i + 1) * s].contiguous() for i in range(nblk)]
+        vblk = [full[2][:, :, i * s:(i + 1) * s].contiguous() for i in range(nblk)]
+        o_parts = torch.empty((nblk, B, H_FULL, N, D), device=dev, dtype=torch.float32)
+        l_parts = torch.empty((nblk, B, H_FULL, N), device=dev, dtype=torch.float32)
+        o_m = torch.empty((B, H_FULL, N, D), device=dev, dtype=torch.bfloat16)
+        l_m = torch.empty((B, H_FULL, N), device=dev, dtype=torch.float32)
+
+        def blocks():
+            for i in range(nblk):
+                dta.dit_attn_fwd_block(full[0], kblk[i], vblk[i], out=o_parts[i], lse=l_parts[i])
+
+        blk_ms = time_it(blocks, reps=3) / nblk
+        mrg_ms = time_it(lambda: dta.dit_attn_merge(o_parts, l_parts, out=o_m, lse=l_m), reps=5)
+        merge_bytes = nblk * (B * H_FULL * N * D * 4 + B * H_FULL * N * 4) + B * H_FULL * N * (D * 2 + 4)
+        legs.update({"ring_block_fwd_ms": blk_ms,
+                     "ring_block_fwd_TFLOPs": attn_flops(B, H_FULL, N, s, D) / (blk_ms * 1e-3) / 1e12,
+                     "merge_ms": mrg_ms, "merge_GBps": merge_bytes / (mrg_ms * 1e-3) / 1e9})
+        del o_parts, l_parts
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(qb[:, :H], kb[:, :H], vb[:, :H], args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "ulysses_share: P=4 round trip of [1,40,32768,128] bf16; "
+                               "attention per head group B1 H10 N32768 D128 (x4), seed 2",
+                   "B": B, "H": H, "N": N, "D": D, "P": P, "heads_before_split": H_FULL},
+        "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16_kernel<128,false>",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "flops_per_launch": flops_launch, "launches_timed": len(attn_ms)},
+        "cpu_baseline": cpu,
+        "legs": legs,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,214 @@
+"""MI355X-native attention hot path of Ulysses / Ring sequence parallelism.
+
+Thin ctypes binding over libditattn.so (C ABI in include/dit_attn.h).  The
+functions carry the C entry points' names and take torch tensors on the
+current HIP device; they only check shapes, dtypes and contiguity, pass data
+pointers and the current stream, and raise on a non-zero return.  Every step
+of the computation runs in the library's HIP kernels: there is no fallback,
+and importing the binding fails loudly if the library has not been built
+(``python -m diffusion_transformer_attention_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libditattn.so")
+
+DIT_BF16, DIT_F32 = 0, 1
+DIT_OK, DIT_EINVAL, DIT_EUNSUPPORTED, DIT_EALIGN, DIT_ELAUNCH, DIT_ERANGE = 0, -1, -2, -3, -4, -5
+EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_merge", "ulysses_seq2head",
+            "ulysses_head2seq", "dit_strerror", "dit_abi_version")
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libditattn.so and declare its prototypes (no device call is made)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m diffusion_transformer_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.dit_attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P]
+    lib.dit_attn_fwd_block.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, P]
+    lib.dit_attn_merge.argtypes = [P, P, I, P, P, I, I, I, I, I, P]
+    lib.ulysses_seq2head.argtypes = [P, P, I, I, I, I, I, I, P]
+    lib.ulysses_head2seq.argtypes = [P, P, I, I, I, I, I, I, P]
+    for name in ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_merge", "ulysses_seq2head",
+                 "ulysses_head2seq", "dit_abi_version"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.dit_strerror.argtypes = [ctypes.c_int]
+    lib.dit_strerror.restype = ctypes.c_char_p
+    lib.dit_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def dit_strerror(code: int) -> str:
+    return load_library().dit_strerror(int(code)).decode()
+
+
+def dit_abi_version() -> int:
+    return load_library().dit_abi_version()
+
+
+class DitError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {dit_strerror(code)} (code {code})")
+        self.code = code
+
+
+def _check(rc: int, where: str):
+    if rc != DIT_OK:
+        raise DitError(rc, where)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return DIT_BF16
+    if dt == torch.float32:
+        return DIT_F32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _need(t, name, dims):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dims, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def dit_attn_fwd(q, k, v, scale=None, out=None, lse=None, return_lse=True):
+    """Attention over all N tokens of each (b, h): q, k, v [B,H,N,D] (bf16 or f32).
+
+    Returns (O [B,H,N,D] in the input dtype, LSE float32 [B,H,N] or None).
+    """
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, 4)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share shape and dtype")
+    B, H, N, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    _need(o, "out", 4)
+    if o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+    if lse is not None:
+        _need(lse, "lse", 3)
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N):
+            raise ValueError("lse must be float32 [B,H,N]")
+    rc = lib.dit_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, D,
+                          ctypes.c_float(scale), _dtype_code(q.dtype), _stream())
+    _check(rc, "dit_attn_fwd")
+    return o, lse
+
+
+def dit_attn_fwd_block(q, k, v, scale=None, out_dtype=torch.float32, out=None, lse=None):
+    """One Ring step: q [B,H,Nq,D] against one K/V block k, v [B,H,Nkv,D].
+
+    Returns (O [B,H,Nq,D] in out_dtype, LSE float32 [B,H,Nq]).
+    """
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, 4)
+    B, H, Nq, D = q.shape
+    Nkv = k.shape[2]
+    if k.shape != v.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != D:
+        raise ValueError("k, v must be [B,H,Nkv,D] matching q")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share dtype")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o = torch.empty((B, H, Nq, D), device=q.device, dtype=out_dtype) if out is None else out
+    _need(o, "out", 4)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), device=q.device, dtype=torch.float32)
+    _need(lse, "lse", 3)
+    rc = lib.dit_attn_fwd_block(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nkv, D,
+                                ctypes.c_float(scale), _dtype_code(q.dtype),
+                                _dtype_code(o.dtype), _stream())
+    _check(rc, "dit_attn_fwd_block")
+    return o, lse
+
+
+def dit_attn_merge(o_parts, lse_parts, out_dtype=torch.bfloat16, out=None, lse=None,
+                   return_lse=True):
+    """Exact LSE merge: o_parts float32 [nblk,B,H,N,D], lse_parts float32 [nblk,B,H,N].
+
+    Returns (O [B,H,N,D] in out_dtype, LSE float32 [B,H,N] or None).
+    """
+    lib = load_library()
+    _need(o_parts, "o_parts", 5)
+    _need(lse_parts, "lse_parts", 4)
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise ValueError("partials must be float32")
+    nblk, B, H, N, D = o_parts.shape
+    if tuple(lse_parts.shape) != (nblk, B, H, N):
+        raise ValueError("lse_parts must be [nblk,B,H,N]")
+    o = torch.empty((B, H, N, D), device=o_parts.device, dtype=out_dtype) if out is None else out
+    _need(o, "out", 4)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), device=o_parts.device, dtype=torch.float32)
+    rc = lib.dit_attn_merge(_ptr(o_parts), _ptr(lse_parts), nblk, _ptr(o), _ptr(lse), B, H, N, D,
+                            _dtype_code(o.dtype), _stream())
+    _check(rc, "dit_attn_merge")
+    return o, lse
+
+
+def ulysses_seq2head(shards, out=None):
+    """[P,B,H,N/P,D] token shards -> [P,B,H/P,N,D] head groups (bit-exact, any dtype)."""
+    lib = load_library()
+    _need(shards, "shards", 5)
+    P, B, H, Ns, D = shards.shape
+    if P == 0 or H % P:
+        raise ValueError("H must be divisible by P")
+    o = torch.empty((P, B, H // P, Ns * P, D), device=shards.device, dtype=shards.dtype) \
+        if out is None else out
+    _need(o, "out", 5)
+    rc = lib.ulysses_seq2head(_ptr(shards), _ptr(o), P, B, H, Ns * P, D, shards.element_size(),
+                              _stream())
+    _check(rc, "ulysses_seq2head")
+    return o
+
+
+def ulysses_head2seq(groups, out=None):
+    """[P,B,H/P,N,D] head groups -> [P,B,H,N/P,D] token shards (bit-exact, any dtype)."""
+    lib = load_library()
+    _need(groups, "groups", 5)
+    P, B, g, N, D = groups.shape
+    if P == 0 or N % P:
+        raise ValueError("N must be divisible by P")
+    o = torch.empty((P, B, g * P, N // P, D), device=groups.device, dtype=groups.dtype) \
+        if out is None else out
+    _need(o, "out", 5)
+    rc = lib.ulysses_head2seq(_ptr(groups), _ptr(o), P, B, g * P, N, D, groups.element_size(),
+                              _stream())
+    _check(rc, "ulysses_head2seq")
+    return o
+
+
+__all__ = ["dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_merge", "ulysses_seq2head",
+           "ulysses_head2seq", "dit_strerror", "dit_abi_version", "load_library", "DitError",
+           "LIB_PATH", "EXPORTED", "DIT_BF16", "DIT_F32"]

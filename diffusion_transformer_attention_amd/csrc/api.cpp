@@ -1,0 +1,124 @@
+// C ABI of libditattn.so: host-side argument validation, then the launch.
+// Every check runs before any HIP call, so an argument error never touches
+// the device.  Declarations and argument meaning: include/dit_attn.h.
+#include "../../include/dit_attn.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_head_dim(int D) { return D == 32 || D == 64 || D == 128; }
+
+// B*H*N*D must stay well inside int64 (and the kernels' 64-bit offsets).
+bool size_ok(int64_t a, int64_t b, int64_t c, int64_t d) {
+  const int64_t lim = (int64_t)1 << 46;
+  int64_t x = a;
+  for (int64_t y : {b, c, d}) {
+    if (y != 0 && x > lim / y) return false;
+    x *= y;
+  }
+  return true;
+}
+
+int map_launch(hipError_t e) { return e == hipSuccess ? DIT_OK : DIT_ELAUNCH; }
+
+int attn_common(const void* q, const void* k, const void* v, void* o, float* lse, bool lse_required,
+                int B, int H, int Nq, int Nkv, int D, float scale, int in_dtype, int o_dtype,
+                void* stream) {
+  if (B < 0 || H < 0 || Nq < 0 || Nkv < 0 || D <= 0) return DIT_EINVAL;
+  if (!(isfinite(scale) && scale > 0.0f)) return DIT_EINVAL;
+  if (in_dtype != DIT_BF16 && in_dtype != DIT_F32) return DIT_EUNSUPPORTED;
+  if (o_dtype != DIT_BF16 && o_dtype != DIT_F32) return DIT_EUNSUPPORTED;
+  if (in_dtype == DIT_F32 && o_dtype != DIT_F32) return DIT_EUNSUPPORTED;
+  if (!supported_head_dim(D)) return DIT_EUNSUPPORTED;
+  if (!size_ok(B, H, Nq, D) || !size_ok(B, H, Nkv, D)) return DIT_ERANGE;
+  if (B == 0 || H == 0 || Nq == 0) return DIT_OK;
+  if (Nkv == 0) return DIT_EINVAL;  // softmax over an empty key set is undefined
+  if (!q || !k || !v || !o || (lse_required && !lse)) return DIT_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return DIT_EALIGN;
+  if (lse && !aligned(lse, 4)) return DIT_EALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (in_dtype == DIT_BF16)
+    return map_launch(ditattn::launch_attn_bf16(q, k, v, o, lse, B, H, Nq, Nkv, D, scale,
+                                                o_dtype == DIT_F32, s));
+  return map_launch(ditattn::launch_attn_f32(static_cast<const float*>(q),
+                                             static_cast<const float*>(k),
+                                             static_cast<const float*>(v),
+                                             static_cast<float*>(o), lse, B, H, Nq, Nkv, D,
+                                             scale, s));
+}
+
+int permute_common(const void* in, void* out, int P, int B, int H, int N, int D, int elem_bytes,
+                   bool head2seq, void* stream) {
+  if (P < 1 || B < 0 || H < 0 || N < 0 || D < 0) return DIT_EINVAL;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)
+    return DIT_EUNSUPPORTED;
+  if (H % P != 0 || N % P != 0) return DIT_EINVAL;
+  if (!size_ok(B, H, N, (int64_t)D * elem_bytes)) return DIT_ERANGE;
+  if (B == 0 || H == 0 || N == 0 || D == 0) return DIT_OK;
+  if (!in || !out) return DIT_EINVAL;
+  if (!aligned(in, elem_bytes) || !aligned(out, elem_bytes)) return DIT_EALIGN;
+  return map_launch(ditattn::launch_permute(in, out, P, B, H, N, D, elem_bytes, head2seq,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N, int D, float scale, int dtype, void* stream) {
+  return attn_common(q, k, v, o, lse, false, B, H, N, N, D, scale, dtype, dtype, stream);
+}
+
+int dit_attn_fwd_block(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int H, int Nq, int Nkv, int D, float scale, int in_dtype, int o_dtype,
+                       void* stream) {
+  return attn_common(q, k, v, o, lse, true, B, H, Nq, Nkv, D, scale, in_dtype, o_dtype, stream);
+}
+
+int dit_attn_merge(const float* o_parts, const float* lse_parts, int nblk, void* o, float* lse,
+                   int B, int H, int N, int D, int o_dtype, void* stream) {
+  if (nblk < 1 || B < 0 || H < 0 || N < 0 || D <= 0) return DIT_EINVAL;
+  if (o_dtype != DIT_BF16 && o_dtype != DIT_F32) return DIT_EUNSUPPORTED;
+  if (!supported_head_dim(D)) return DIT_EUNSUPPORTED;
+  if (!size_ok((int64_t)nblk * B, H, N, D)) return DIT_ERANGE;
+  if (B == 0 || H == 0 || N == 0) return DIT_OK;
+  if (!o_parts || !lse_parts || !o) return DIT_EINVAL;
+  if (!aligned(o_parts, 16) || !aligned(o, 16)) return DIT_EALIGN;
+  if (!aligned(lse_parts, 4) || (lse && !aligned(lse, 4))) return DIT_EALIGN;
+  return map_launch(ditattn::launch_merge(o_parts, lse_parts, nblk, o, lse,
+                                          (int64_t)B * H * N, D, o_dtype == DIT_F32,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int ulysses_seq2head(const void* in, void* out, int P, int B, int H, int N, int D, int elem_bytes,
+                     void* stream) {
+  return permute_common(in, out, P, B, H, N, D, elem_bytes, false, stream);
+}
+
+int ulysses_head2seq(const void* in, void* out, int P, int B, int H, int N, int D, int elem_bytes,
+                     void* stream) {
+  return permute_common(in, out, P, B, H, N, D, elem_bytes, true, stream);
+}
+
+const char* dit_strerror(int code) {
+  switch (code) {
+    case DIT_OK: return "success";
+    case DIT_EINVAL: return "invalid argument (null pointer, bad size, divisibility or scale)";
+    case DIT_EUNSUPPORTED: return "unsupported head dim, dtype combination or element size";
+    case DIT_EALIGN: return "misaligned pointer";
+    case DIT_ELAUNCH: return "HIP launch failed";
+    case DIT_ERANGE: return "tensor size out of range";
+    default: return "unknown error code";
+  }
+}
+
+int dit_abi_version(void) { return DIT_ABI_VERSION; }
+
+}  // extern "C"

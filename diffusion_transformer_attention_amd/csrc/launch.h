@@ -1,0 +1,25 @@
+// Internal launchers behind the C ABI.  Arguments arrive already validated
+// by api.cpp; each returns a hipError_t from the launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ditattn {
+
+// bf16 q/k/v; o in bf16 (o_f32 == false) or float32.  lse may be null.
+hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int Nq, int Nkv, int D, float scale, bool o_f32,
+                            hipStream_t stream);
+
+// float32 q/k/v/o.  lse may be null.
+hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                           int B, int H, int Nq, int Nkv, int D, float scale, hipStream_t stream);
+
+hipError_t launch_merge(const float* o_parts, const float* lse_parts, int nblk, void* o,
+                        float* lse, int64_t rows, int D, bool o_f32, hipStream_t stream);
+
+// head2seq == false: seq->head; true: head->seq.
+hipError_t launch_permute(const void* in, void* out, int P, int B, int H, int N, int D,
+                          int elem_bytes, bool head2seq, hipStream_t stream);
+
+}  // namespace ditattn

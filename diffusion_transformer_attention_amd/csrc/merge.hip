@@ -1,0 +1,83 @@
+// Exact log-sum-exp merge of attention partials over disjoint key blocks
+// ("Multi-GPU parallelism: spreading one step over several cards", section
+// "Sequence parallelism: Ulysses and Ring", Ring paragraph: each block's
+// local attention is merged with a log-sum-exp).
+//
+//   M = max_i LSE_i,  LSE = M + ln sum_i exp(LSE_i - M),
+//   O = sum_i exp(LSE_i - M) O_i / sum_i exp(LSE_i - M)
+//
+// HBM-bound: every partial is read once and the result written once.  One
+// thread owns four consecutive channels (one 16-byte load per partial) of one
+// row; the D/4 threads of a row read the same nblk LSE values from cache.
+#include <math.h>
+
+#include "launch.h"
+
+namespace ditattn {
+namespace {
+
+constexpr int kThreads = 256;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict__ o_parts,
+                                                         const float* __restrict__ lse_parts,
+                                                         int nblk, void* __restrict__ o,
+                                                         float* __restrict__ lse, int64_t rows,
+                                                         int log2_tpr, int D) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  constexpr float kLn2 = 0.6931471805599453f;
+  const int64_t total = rows << log2_tpr;
+  for (int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x; gid < total;
+       gid += (int64_t)gridDim.x * kThreads) {
+  const int64_t row = gid >> log2_tpr;
+  const int c4 = (int)(gid & ((1 << log2_tpr) - 1)) * 4;
+  float M = -INFINITY;
+  for (int i = 0; i < nblk; ++i) M = fmaxf(M, lse_parts[(int64_t)i * rows + row]);
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
+  if (M != -INFINITY) {
+    for (int i = 0; i < nblk; ++i) {
+      const float li = lse_parts[(int64_t)i * rows + row];
+      const float w = __builtin_amdgcn_exp2f((li - M) * kLog2e);  // li = -inf -> 0
+      const f32x4 x = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4*>(o_parts + ((int64_t)i * rows + row) * D + c4));
+      tot += w;
+      acc += w * x;
+    }
+    acc *= 1.0f / tot;
+  }
+  const int64_t off = row * D + c4;
+  if (OUT_F32) {
+    __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(static_cast<float*>(o) + off));
+  } else {
+    bf16x4 b = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
+    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(o) + off) = b;
+  }
+  if (lse && c4 == 0)
+    lse[row] = (M == -INFINITY) ? -INFINITY : M + __builtin_amdgcn_logf(tot) * kLn2;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_merge(const float* o_parts, const float* lse_parts, int nblk, void* o,
+                        float* lse, int64_t rows, int D, bool o_f32, hipStream_t stream) {
+  const int tpr = D / 4;  // D in {32, 64, 128}: a power of two
+  int log2_tpr = 0;
+  while ((1 << log2_tpr) < tpr) ++log2_tpr;
+  const int64_t threads = rows * tpr;
+  int64_t blocks = (threads + kThreads - 1) / kThreads;
+  if (blocks > (1 << 20)) blocks = 1 << 20;
+  if (o_f32)
+    hipLaunchKernelGGL(merge_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       o_parts, lse_parts, nblk, o, lse, rows, log2_tpr, D);
+  else
+    hipLaunchKernelGGL(merge_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       o_parts, lse_parts, nblk, o, lse, rows, log2_tpr, D);
+  return hipGetLastError();
+}
+
+}  // namespace ditattn

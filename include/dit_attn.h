@@ -1,0 +1,146 @@
+/*
+ * dit_attn.h -- C ABI of libditattn.so: one GPU's share of the attention in
+ * Ulysses / Ring sequence parallelism for diffusion transformers, on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [HB]  "Multi-GPU parallelism: spreading one step over several cards"
+ *         (AI infra handbook), section "Sequence parallelism: Ulysses and
+ *         Ring": the four-card Ulysses simulation (token partition,
+ *         all_to_all_heads, per-card attention, all_to_all_tokens) and the
+ *         Ring paragraph (per-block local attention merged by log-sum-exp).
+ *   [PR]  "Feat: USP sequence parallelism (Ulysses x Ring) via
+ *         SequenceParallelPlan; Wan enabled" (miles_diffusion pull request):
+ *         Design / "Ring kernel selection" (ring kernels return the LSE);
+ *         "Limitations" (everything outside the envelope fails loudly: head
+ *         count divisible by the Ulysses degree, sequence length divisible by
+ *         the SP degree, no mask / dropout / causal flag under SP).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are dense, row-major, with no padding.  q, k, v, o are
+ *    [B, H, N, D] (batch, head, token, channel); lse is float32 [B, H, N].
+ *  - Every pointer is a DEVICE pointer on the current HIP device, allocated
+ *    and owned by the caller.  The library allocates no memory and keeps no
+ *    state between calls; calls are reentrant.  Outputs must not overlap
+ *    inputs.
+ *  - Every call enqueues its kernels on `stream` (a hipStream_t; NULL = the
+ *    legacy default stream) and returns without synchronising.
+ *  - All arguments are validated on the host BEFORE any HIP call, so an
+ *    argument error leaves the device untouched.  Nothing throws across the
+ *    ABI; the return value is DIT_OK or a negative code (dit_strerror).
+ *  - Work with a zero batch, head or query count is a no-op that returns
+ *    DIT_OK without looking at the pointers.
+ *  - bf16 means bfloat16 (1-8-7), stored as 16-bit words; f32 is IEEE binary32.
+ */
+#ifndef DIT_ATTN_H
+#define DIT_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DIT_ABI_VERSION 1
+
+typedef enum { DIT_BF16 = 0, DIT_F32 = 1 } dit_dtype;
+
+enum {
+  DIT_OK = 0,
+  DIT_EINVAL = -1,       /* null pointer, negative size, Nkv == 0, scale not finite or <= 0,
+                            H % P != 0, N % P != 0, nblk < 1, P < 1 */
+  DIT_EUNSUPPORTED = -2, /* D not in {32, 64, 128}, a dtype combination not built, elem_bytes
+                            not in {1, 2, 4, 8} */
+  DIT_EALIGN = -3,       /* q/k/v/o/o_parts not 16-byte aligned, lse not 4-byte aligned,
+                            permute buffers not aligned to elem_bytes */
+  DIT_ELAUNCH = -4,      /* the HIP runtime reported an error at launch */
+  DIT_ERANGE = -5        /* a size product does not fit the 64-bit index space */
+};
+
+/*
+ * Non-causal full-sequence attention with log-sum-exp  ([HB] Ulysses
+ * simulation: each card runs complete attention over all N tokens of its
+ * heads; [PR] "Ring kernel selection": the kernel returns the LSE).
+ *
+ *   O[b,h,i,:]  = sum_j softmax_j(scale * q_i . k_j) v_j
+ *   LSE[b,h,i]  = ln sum_j exp(scale * q_i . k_j)        (natural log, scale included)
+ *
+ *   q, k, v : [B,H,N,D], dtype `dtype` (DIT_BF16 or DIT_F32)
+ *   o       : [B,H,N,D], same dtype as the inputs
+ *   lse     : float32 [B,H,N], or NULL to skip the LSE write
+ *   scale   : finite, > 0 (the usual choice is 1/sqrt(D))
+ *   D       : 32, 64 or 128
+ * bf16 inputs are contracted on the matrix cores with float32 accumulation;
+ * softmax statistics are float32; O is rounded to bf16 (nearest-even) once.
+ * There is no mask, dropout or causal flag, by design ([PR] "Limitations").
+ */
+int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int D, float scale, int dtype, void* stream);
+
+/*
+ * One Ring step: attention of Nq queries against one K/V block of Nkv tokens,
+ * returning the partial output and its LSE so that partials over disjoint
+ * key blocks merge exactly ([HB] Ring paragraph; [PR] "Ring kernel
+ * selection").  Same formula as dit_attn_fwd with separate lengths.
+ *
+ *   q : [B,H,Nq,D] in_dtype;  k, v : [B,H,Nkv,D] in_dtype;  Nkv >= 1
+ *   o : [B,H,Nq,D] o_dtype (DIT_F32 keeps the partial unrounded; DIT_BF16
+ *       allowed for bf16 inputs);  lse : float32 [B,H,Nq], required.
+ * Built combinations: (BF16 -> F32), (BF16 -> BF16), (F32 -> F32).
+ */
+int dit_attn_fwd_block(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int Nq, int Nkv, int D, float scale,
+                       int in_dtype, int o_dtype, void* stream);
+
+/*
+ * Exact log-sum-exp merge of nblk partials over disjoint key blocks ([HB]
+ * Ring paragraph: results of each K/V block merged with a log-sum-exp).
+ *
+ *   M   = max_i LSE_i
+ *   LSE = M + ln sum_i exp(LSE_i - M)
+ *   O   = sum_i exp(LSE_i - LSE) * O_i
+ *
+ *   o_parts   : float32 [nblk,B,H,N,D], the partials stacked contiguously
+ *   lse_parts : float32 [nblk,B,H,N]
+ *   o         : [B,H,N,D] in o_dtype (DIT_BF16 or DIT_F32)
+ *   lse       : float32 [B,H,N], or NULL to skip
+ * A block whose LSE is -inf gets weight 0; a row whose every LSE is -inf
+ * gets O = 0 and LSE = -inf (never NaN).
+ */
+int dit_attn_merge(const float* o_parts, const float* lse_parts, int nblk,
+                   void* o, float* lse, int B, int H, int N, int D, int o_dtype, void* stream);
+
+/*
+ * Ulysses sequence -> head exchange as it lands on one device ([HB] Ulysses
+ * simulation, all_to_all_heads): P token shards become P head groups.
+ *
+ *   in  : [P][B,H,N/P,D]  rank s holds every head of tokens [s*N/P,(s+1)*N/P)
+ *   out : [P][B,H/P,N,D]  rank r holds heads [r*H/P,(r+1)*H/P) of all N tokens
+ *   out[r][b,h',s*N/P+n,d] = in[s][b,r*H/P+h',n,d]
+ * N is the full sequence length.  Pure data movement of elem_bytes-sized
+ * elements (1, 2, 4 or 8): the result is bit-exact for any dtype.
+ * Requires H % P == 0 and N % P == 0 ([PR] "Limitations": no padding).
+ */
+int ulysses_seq2head(const void* in, void* out, int P, int B, int H, int N, int D,
+                     int elem_bytes, void* stream);
+
+/*
+ * Inverse exchange, head -> sequence ([HB] Ulysses simulation,
+ * all_to_all_tokens):
+ *   in  : [P][B,H/P,N,D],  out : [P][B,H,N/P,D]
+ *   out[s][b,r*H/P+h',n,d] = in[r][b,h',s*N/P+n,d]
+ * Same requirements and exactness as ulysses_seq2head.
+ */
+int ulysses_head2seq(const void* in, void* out, int P, int B, int H, int N, int D,
+                     int elem_bytes, void* stream);
+
+/* Static English text for a return code (never NULL). */
+const char* dit_strerror(int code);
+
+/* DIT_ABI_VERSION of the built library. */
+int dit_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_ATTN_H */

@@ -1,0 +1,109 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/dit_attn.h declares, and rejects bad arguments on the host before
+any HIP call (so these calls never reach the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import diffusion_transformer_attention_amd as dta
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dit_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dta.LIB_PATH):
+        pytest.fail("libditattn.so not built: run __graft_entry__.build()")
+    return dta.load_library()
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == sorted(dta.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strerror(lib):
+    assert lib.dit_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, 7):
+        assert lib.dit_strerror(code)
+
+
+V = ctypes.c_void_p
+A = V(0x10000)       # 16-byte aligned stand-in address: never dereferenced here
+MIS = V(0x10008)     # 8-byte aligned, not 16
+NULL = V(0)
+S = V(0)             # stream
+
+
+def fwd(lib, q=A, k=A, v=A, o=A, lse=A, B=1, H=2, N=64, D=128, scale=0.125, dt=0):
+    return lib.dit_attn_fwd(q, k, v, o, lse, B, H, N, D, ctypes.c_float(scale), dt, S)
+
+
+def blk(lib, Nq=64, Nkv=64, ind=0, od=1, lse=A, D=128, scale=0.125):
+    return lib.dit_attn_fwd_block(A, A, A, A, lse, 1, 2, Nq, Nkv, D, ctypes.c_float(scale), ind, od, S)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NULL), dta.DIT_EINVAL), (dict(k=NULL), dta.DIT_EINVAL), (dict(v=NULL), dta.DIT_EINVAL),
+    (dict(o=NULL), dta.DIT_EINVAL), (dict(B=-1), dta.DIT_EINVAL), (dict(N=-5), dta.DIT_EINVAL),
+    (dict(scale=0.0), dta.DIT_EINVAL), (dict(scale=-1.0), dta.DIT_EINVAL),
+    (dict(scale=float("inf")), dta.DIT_EINVAL), (dict(scale=float("nan")), dta.DIT_EINVAL),
+    (dict(D=96), dta.DIT_EUNSUPPORTED), (dict(D=256), dta.DIT_EUNSUPPORTED),
+    (dict(D=0), dta.DIT_EINVAL), (dict(dt=2), dta.DIT_EUNSUPPORTED),
+    (dict(q=MIS), dta.DIT_EALIGN), (dict(o=MIS), dta.DIT_EALIGN), (dict(lse=V(0x10002)), dta.DIT_EALIGN),
+    (dict(B=0), dta.DIT_OK), (dict(H=0, q=NULL), dta.DIT_OK), (dict(N=0), dta.DIT_OK),
+    (dict(B=1 << 30, H=1 << 30), dta.DIT_ERANGE),
+])
+def test_attn_fwd_validation(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+def test_block_validation(lib):
+    assert blk(lib, lse=NULL) == dta.DIT_EINVAL          # the ring partial needs its LSE
+    assert blk(lib, Nkv=0) == dta.DIT_EINVAL             # empty key set
+    assert blk(lib, ind=1, od=0) == dta.DIT_EUNSUPPORTED  # f32 in -> bf16 out not built
+    assert blk(lib, Nq=0) == dta.DIT_OK                  # nothing to compute
+
+
+def test_merge_validation(lib):
+    m = lambda nblk=4, o=A, op=A, lp=A, D=128, od=0, N=64: lib.dit_attn_merge(
+        op, lp, nblk, o, A, 1, 2, N, D, od, S)
+    assert m(nblk=0) == dta.DIT_EINVAL
+    assert m(op=NULL) == dta.DIT_EINVAL
+    assert m(D=48) == dta.DIT_EUNSUPPORTED
+    assert m(od=5) == dta.DIT_EUNSUPPORTED
+    assert m(op=MIS) == dta.DIT_EALIGN
+    assert m(N=0) == dta.DIT_OK
+
+
+@pytest.mark.parametrize("fn", ["ulysses_seq2head", "ulysses_head2seq"])
+def test_permute_validation(lib, fn):
+    f = getattr(lib, fn)
+    call = lambda P=4, H=8, N=64, eb=2, i=A, o=A: f(i, o, P, 1, H, N, 32, eb, S)
+    assert call(H=6) == dta.DIT_EINVAL        # heads not divisible by P
+    assert call(N=66) == dta.DIT_EINVAL       # tokens not divisible by P
+    assert call(P=0) == dta.DIT_EINVAL
+    assert call(eb=3) == dta.DIT_EUNSUPPORTED
+    assert call(i=NULL) == dta.DIT_EINVAL
+    assert call(eb=4, i=V(0x10002)) == dta.DIT_EALIGN
+    assert call(N=0) == dta.DIT_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 32)
+    with pytest.raises(ValueError):
+        dta.dit_attn_fwd(x, x, x)

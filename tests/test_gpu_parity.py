@@ -1,0 +1,288 @@
+"""GPU parity: the HIP library against the fp64 oracle, through the C ABI.
+
+Small cases compare every output element; the full-size workloads compare
+sampled rows the oracle computes one by one, plus properties that hold at
+any size (bit-exact permutes, Ulysses output equal to single-pass output bit
+for bit, ring-merged output equal to single-pass output within tolerance,
+determinism, untouched guard bands).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+import diffusion_transformer_attention_amd as dta
+from _helpers import (F32_MAX_ABS, assert_bf16_close, bits_to_torch_bf16, max_abs, rel_rms,
+                      to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+def f64(bits):
+    return datagen.bf16_to_f32(bits).astype(np.float64)
+
+
+GUARD = 4096
+
+
+def guarded(shape, dtype):
+    """An output tensor inside a larger buffer whose margins hold a sentinel."""
+    n = int(np.prod(shape))
+    buf = torch.full((n + 2 * GUARD,), -12345.0, device="cuda", dtype=dtype)
+    return buf, buf[GUARD:GUARD + n].view(shape)
+
+
+def margins_intact(buf):
+    sentinel = torch.full((GUARD,), -12345.0, device=buf.device, dtype=buf.dtype)
+    return torch.equal(buf[:GUARD], sentinel) and torch.equal(buf[-GUARD:], sentinel)
+
+
+# ------------------------------------------------------------ permutes
+_INT = {1: np.uint8, 2: np.int16, 4: np.int32, 8: np.int64}
+
+
+@pytest.mark.parametrize("P,B,H,N,D,eb", [
+    (4, 1, 8, 256, 32, 4),     # the handbook simulation's shape, float32 words
+    (4, 2, 8, 64, 16, 8),
+    (3, 1, 6, 9, 5, 2),        # 30-byte runs: not a multiple of 16 bytes
+    (2, 2, 6, 10, 3, 1),
+    (1, 1, 2, 4, 8, 2),        # P = 1 is the identity
+    (8, 1, 40, 1024, 128, 2),
+])
+def test_permutes_bit_exact(P, B, H, N, D, eb):
+    say("permute", P, B, H, N, D, eb)
+    rng = np.random.default_rng(100 + P * 7 + eb)
+    x = rng.integers(0, 256, size=(B, H, N, D * eb), dtype=np.uint8).view(_INT[eb])
+    shards = oracle.shard_tokens(x, P)
+    want = oracle.seq2head(shards)
+    got = dta.ulysses_seq2head(torch.from_numpy(np.ascontiguousarray(shards)).cuda())
+    torch.cuda.synchronize()
+    assert tuple(got.shape) == want.shape and np.array_equal(got.cpu().numpy(), want)
+    back = dta.ulysses_head2seq(got)
+    assert np.array_equal(back.cpu().numpy(), shards)
+
+
+def test_permutes_empty_is_noop():
+    x = torch.empty((4, 1, 8, 0, 16), device="cuda", dtype=torch.bfloat16)
+    assert dta.ulysses_seq2head(x).numel() == 0
+
+
+# ------------------------------------------------------------ float32
+def test_f32_tiny_and_ulysses_round_trip():
+    """The handbook's four-card simulation, on its seed-0 float32 data."""
+    say("f32 tiny B1 H8 N256 D32 + P=4 round trip")
+    q, k, v = datagen.tiny_f32()
+    Oref, Lref = oracle.attention(q, k, v)
+    tq, tk, tv = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    O, L = dta.dit_attn_fwd(tq, tk, tv)
+    assert max_abs(to_f64(O), Oref) <= F32_MAX_ABS
+    assert max_abs(to_f64(L), Lref) <= F32_MAX_ABS
+    P = 4
+    shard = lambda t: torch.stack(t.chunk(P, dim=2)).contiguous()   # rank r's token slice
+    qh, kh, vh = (dta.ulysses_seq2head(shard(t)) for t in (tq, tk, tv))
+    outs = torch.stack([dta.dit_attn_fwd(qh[r], kh[r], vh[r], return_lse=False)[0]
+                        for r in range(P)])
+    back = dta.ulysses_head2seq(outs)
+    full = torch.cat(list(back), dim=2)
+    assert torch.equal(full, O)          # heads are independent: bit-identical
+    ref = torch.nn.functional.scaled_dot_product_attention(*(torch.from_numpy(x) for x in (q, k, v)))
+    assert torch.allclose(full.cpu(), ref, atol=1e-5)   # the simulation's printed check
+
+
+@pytest.mark.parametrize("B,H,Nq,Nkv,D", [(1, 2, 130, 130, 32), (2, 1, 77, 200, 64), (1, 1, 1, 1, 128),
+                                          (1, 2, 64, 33, 128)])
+def test_f32_small(B, H, Nq, Nkv, D):
+    say("f32", B, H, Nq, Nkv, D)
+    q, k, v = datagen.small_f32(B, H, Nq, D, seed=Nq + D, Nkv=Nkv)
+    Oref, Lref = oracle.attention(q, k, v)
+    O, L = dta.dit_attn_fwd_block(*(torch.from_numpy(x).cuda() for x in (q, k, v)))
+    assert max_abs(to_f64(O), Oref) <= F32_MAX_ABS
+    assert max_abs(to_f64(L), Lref) <= F32_MAX_ABS
+
+
+# ------------------------------------------------------------ bf16 small
+@pytest.mark.parametrize("B,H,Nq,Nkv,D,out", [
+    (1, 2, 128, 128, 128, "bf16"),
+    (2, 3, 1000, 1000, 128, "bf16"),     # ragged in both directions, several tiles
+    (1, 2, 333, 333, 64, "bf16"),
+    (1, 3, 257, 257, 32, "bf16"),
+    (1, 1, 1, 1, 128, "bf16"),           # one token
+    (1, 2, 300, 77, 128, "f32"),         # ring partial: Nq != Nkv, float32 out
+    (1, 2, 64, 1000, 64, "bf16"),
+    (1, 1, 129, 4097, 128, "f32"),
+])
+def test_bf16_small_full_compare(B, H, Nq, Nkv, D, out):
+    say("bf16", B, H, Nq, Nkv, D, out)
+    qb, kb, vb = datagen.small_bf16(B, H, Nq, D, seed=Nq * 3 + D, Nkv=Nkv)
+    Oref, Lref = oracle.attention(f64(qb), f64(kb), f64(vb))
+    tq, tk, tv = (bits_to_torch_bf16(x) for x in (qb, kb, vb))
+    if Nq == Nkv and out == "bf16":
+        O, L = dta.dit_attn_fwd(tq, tk, tv)
+    else:
+        O, L = dta.dit_attn_fwd_block(tq, tk, tv, out_dtype=torch.float32 if out == "f32" else torch.bfloat16)
+    assert_bf16_close(to_f64(O), to_f64(L), Oref, Lref, f"B{B} H{H} Nq{Nq} Nkv{Nkv} D{D}")
+
+
+def test_bf16_large_scores_and_explicit_scale():
+    """Wide score range (|s| up to ~40): the running max must keep exp finite."""
+    say("bf16 large scores")
+    rng = np.random.default_rng(77)
+    q = rng.standard_normal((1, 2, 300, 128)).astype(np.float32) * 3
+    k = rng.standard_normal((1, 2, 300, 128)).astype(np.float32) * 3
+    v = rng.standard_normal((1, 2, 300, 128)).astype(np.float32)
+    qb, kb, vb = (datagen.bf16_bits(x) for x in (q, k, v))
+    for scale in (0.3, 1 / np.sqrt(128)):
+        Oref, Lref = oracle.attention(f64(qb), f64(kb), f64(vb), scale)
+        O, L = dta.dit_attn_fwd(*(bits_to_torch_bf16(x) for x in (qb, kb, vb)), scale=scale)
+        assert np.isfinite(to_f64(O)).all()
+        ma, rr = max_abs(to_f64(O), Oref), rel_rms(to_f64(O), Oref)
+        assert ma <= 2e-2 and rr <= 1e-2, (scale, ma, rr)
+        # LSE grows with the score range; its absolute bound scales with |LSE|
+        assert max_abs(to_f64(L), Lref) <= 1e-3 * max(1.0, np.abs(Lref).max() / 10)
+
+
+@pytest.mark.parametrize("Nkv", [1000, 4100])
+def test_bf16_score_jump_takes_exact_max_path(Nkv):
+    """One late key scores ~100 (base 2) above the first step's max for some
+    rows: the fixed-reference loop cannot hold it and the exact-max pass must
+    produce the same result as the oracle."""
+    say("bf16 score jump", Nkv)
+    rng = np.random.default_rng(91)
+    q = rng.standard_normal((1, 2, 300, 128)).astype(np.float32)
+    k = rng.standard_normal((1, 2, Nkv, 128)).astype(np.float32)
+    v = rng.standard_normal((1, 2, Nkv, 128)).astype(np.float32)
+    k[0, 0, 700] = 6.0 * q[0, 0, 5]          # row 5 of head 0: s*log2e ~ 98 above typical
+    k[0, 1, Nkv - 3] = 6.0 * q[0, 1, 260]    # head 1: in the partial last tile
+    qb, kb, vb = (datagen.bf16_bits(x) for x in (q, k, v))
+    Oref, Lref = oracle.attention(f64(qb), f64(kb), f64(vb))
+    O, L = dta.dit_attn_fwd_block(*(bits_to_torch_bf16(x) for x in (qb, kb, vb)),
+                                  out_dtype=torch.float32)
+    assert_bf16_close(to_f64(O), to_f64(L), Oref, Lref, f"score jump Nkv{Nkv}")
+    assert abs(to_f64(O)[0, 0, 5] - f64(vb)[0, 0, 700]).max() < 2e-2
+
+
+def test_uniform_v_returns_v():
+    say("bf16 uniform V")
+    qb, kb, _ = datagen.small_bf16(1, 2, 200, 128, seed=5)
+    u = datagen.bf16_bits(np.random.default_rng(6).standard_normal(128).astype(np.float32))
+    vb = np.broadcast_to(u, (1, 2, 200, 128)).copy()
+    O, _ = dta.dit_attn_fwd(*(bits_to_torch_bf16(x) for x in (qb, kb, vb)))
+    # p sums to 1 only up to bf16 rounding of each p; O = u to within that
+    assert max_abs(to_f64(O), np.broadcast_to(f64(u), (1, 2, 200, 128))) <= 2e-2
+
+
+# ------------------------------------------------------------ merge
+@pytest.mark.parametrize("nblk,out", [(1, "f32"), (3, "f32"), (4, "bf16"), (2, "bf16")])
+def test_merge_against_oracle(nblk, out):
+    say("merge", nblk, out)
+    rng = np.random.default_rng(nblk)
+    o = rng.standard_normal((nblk, 2, 3, 257, 128)).astype(np.float32)
+    l = (rng.standard_normal((nblk, 2, 3, 257)) * 4).astype(np.float32)
+    if nblk > 1:
+        l[0, 0, 0, :10] = -np.inf        # a block with zero weight
+        l[:, 0, 0, 10] = -np.inf         # a row with no weight at all
+    Oref, Lref = oracle.merge(o, l)
+    O, L = dta.dit_attn_merge(torch.from_numpy(o).cuda(), torch.from_numpy(l).cuda(),
+                              out_dtype=torch.float32 if out == "f32" else torch.bfloat16)
+    Og, Lg = to_f64(O), to_f64(L)
+    assert np.isfinite(Og).all()
+    fin = np.isfinite(Lref)
+    assert np.array_equal(np.isfinite(Lg), fin)
+    assert max_abs(Lg[fin], Lref[fin]) <= 1e-5
+    assert max_abs(Og, Oref) <= (1e-5 if out == "f32" else 2e-2)
+    if nblk > 1:
+        assert (Og[0, 0, 10] == 0).all()
+
+
+# ------------------------------------------------------------ full-size workloads
+@pytest.fixture(scope="module")
+def wan_draw():
+    say("generating the [1,40,32768,128] seed-2 draw")
+    return datagen.workload_inputs("ulysses_share")
+
+
+def test_image_share_full():
+    say("image share B1 H24 N4096 D128, full compare")
+    qb, kb, vb = datagen.workload_inputs("image_share")
+    Oref, Lref = oracle.attention(f64(qb), f64(kb), f64(vb))
+    tq, tk, tv = (bits_to_torch_bf16(x) for x in (qb, kb, vb))
+    O, L = dta.dit_attn_fwd(tq, tk, tv)
+    assert_bf16_close(to_f64(O), to_f64(L), Oref, Lref, "image share")
+    O2, L2 = dta.dit_attn_fwd(tq, tk, tv)
+    assert torch.equal(O, O2) and torch.equal(L, L2)     # bitwise repeatable
+
+
+def test_ulysses_share(wan_draw):
+    say("ulysses share: permutes of [4][1,40,8192,128] + attention B1 H10 N32768 D128")
+    qb, kb, vb = wan_draw
+    P, rows = 4, datagen.sample_rows(32768, 64, 1002)
+    full = [bits_to_torch_bf16(x) for x in (qb, kb, vb)]
+    shard = lambda t: torch.stack(t.chunk(P, dim=2)).contiguous()   # rank s's token slice
+    groups = [dta.ulysses_seq2head(shard(t)) for t in full]
+    torch.cuda.synchronize()
+    want_q = oracle.seq2head(oracle.shard_tokens(qb, P))
+    assert np.array_equal(groups[0].cpu().view(torch.int16).numpy().view(np.uint16), want_q)
+    del want_q
+    # rank 0's share: heads 0..9 over all tokens
+    O0, L0 = dta.dit_attn_fwd(groups[0][0], groups[1][0], groups[2][0])
+    Oref, Lref = oracle.attention_rows(f64(qb[:, :10]), f64(kb[:, :10]), f64(vb[:, :10]), rows)
+    ri = torch.from_numpy(rows).cuda()
+    assert_bf16_close(to_f64(O0[:, :, ri]), to_f64(L0[:, :, ri]), Oref, Lref, "ulysses share r0")
+    # every rank, exchanged back, equals one pass over all 40 heads bit for bit
+    outs = torch.stack([O0] + [dta.dit_attn_fwd(groups[0][r], groups[1][r], groups[2][r],
+                                                return_lse=False)[0] for r in range(1, P)])
+    back = dta.ulysses_head2seq(outs)
+    O_ul = torch.cat(list(back), dim=2)
+    O_single, _ = dta.dit_attn_fwd(*full, return_lse=False)
+    assert torch.equal(O_ul, O_single)
+
+
+def test_ring_merge(wan_draw):
+    say("ring merge B1 H40 N32768 D128, 4 K/V blocks of 8192")
+    qb, kb, vb = wan_draw
+    tq, tk, tv = (bits_to_torch_bf16(x) for x in (qb, kb, vb))
+    nblk, s = 4, 8192
+    o_parts = torch.empty((nblk, 1, 40, 32768, 128), device="cuda", dtype=torch.float32)
+    l_parts = torch.empty((nblk, 1, 40, 32768), device="cuda", dtype=torch.float32)
+    for i in range(nblk):
+        dta.dit_attn_fwd_block(tq, tk[:, :, i * s:(i + 1) * s].contiguous(),
+                               tv[:, :, i * s:(i + 1) * s].contiguous(),
+                               out=o_parts[i], lse=l_parts[i])
+    Om, Lm = dta.dit_attn_merge(o_parts, l_parts, out_dtype=torch.bfloat16)
+    Os, Ls = dta.dit_attn_fwd(tq, tk, tv)
+    # merged vs single pass, every element
+    ma = (Om.float() - Os.float()).abs().max().item()
+    assert ma <= 2e-2, ma
+    assert (Lm - Ls).abs().max().item() <= 1e-3
+    # merged and per-block partials vs the oracle on sampled rows of every head
+    rows = datagen.sample_rows(32768, 32, 1003)
+    ri = torch.from_numpy(rows).cuda()
+    q64, k64, v64 = f64(qb[:, :, rows]), f64(kb), f64(vb)
+    Oref, Lref = oracle.attention(q64, k64, v64)
+    assert_bf16_close(to_f64(Om[:, :, ri]), to_f64(Lm[:, :, ri]), Oref, Lref, "ring merged")
+    for i in (0, 3):
+        Opr, Lpr = oracle.attention(q64, k64[:, :, i * s:(i + 1) * s], v64[:, :, i * s:(i + 1) * s])
+        assert_bf16_close(to_f64(o_parts[i][:, :, ri]), to_f64(l_parts[i][:, :, ri]), Opr, Lpr,
+                          f"ring partial {i}")
+
+
+def test_long_video_tail():
+    say("long video B1 H10 N75600 D128 (tail), 64 sampled rows per head, guard bands")
+    qb, kb, vb = datagen.workload_inputs("long_video")
+    tq, tk, tv = (bits_to_torch_bf16(x) for x in (qb, kb, vb))
+    obuf, O = guarded((1, 10, 75600, 128), torch.bfloat16)
+    lbuf, L = guarded((1, 10, 75600), torch.float32)
+    dta.dit_attn_fwd(tq, tk, tv, out=O, lse=L)
+    torch.cuda.synchronize()
+    assert margins_intact(obuf) and margins_intact(lbuf)
+    rows = datagen.sample_rows(75600, 64, 1004)
+    Oref, Lref = oracle.attention_rows(f64(qb), f64(kb), f64(vb), rows)
+    ri = torch.from_numpy(rows).cuda()
+    assert_bf16_close(to_f64(O[:, :, ri]), to_f64(L[:, :, ri]), Oref, Lref, "long video")
