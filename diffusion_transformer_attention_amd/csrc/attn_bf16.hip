@@ -27,9 +27,11 @@
 //    so each lane holds one query column of S^T and O^T: softmax statistics
 //    are per-lane scalars and the S^T accumulator becomes the P^T operand in
 //    registers;
-//  * the key loop runs in 32-key steps, software-pipelined: step s issues
-//    the QK^T MFMAs of step s+1 while the vector ALUs do the softmax of
-//    step s, then the PV MFMAs of step s;
+//  * the key loop runs in 32-key slots, software-pipelined: slot s issues
+//    the QK^T MFMAs of step s+1 and the PV MFMAs of step s-1 while the
+//    vector ALUs do the softmax of step s; the three are independent and
+//    share one basic block, and scheduling hints interleave the MFMAs with
+//    the softmax instructions and the LDS reads;
 //  * softmax in base 2: p = 2^(s*c - m*c) with c = scale*log2(e).  Two row
 //    sums: lb of the bf16-rounded p that the PV product multiplies (via
 //    v_dot2_f32_bf16), which normalises O, so O stays an exact convex
@@ -62,9 +64,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;              // two waves per SIMD
 constexpr int kThreads = 64 * kWaves;
-constexpr int kQB = 2;                 // 32-row query blocks per wave
+constexpr int kQB = 1;                 // 32-row query blocks per wave
 constexpr int kBM = 32 * kQB * kWaves; // query rows per workgroup
 constexpr int kBN = 64;                // keys per LDS tile (two 32-key steps)
 constexpr int kStages = 3;             // LDS stages for K and for V (tile t uses stage t % 3)
@@ -77,7 +79,7 @@ struct Geo {
   static constexpr int CPR = D / 8;            // 16-byte chunks per row
   static constexpr int ROWB = D * 2;           // bytes per row
   static constexpr int TILE = kBN * ROWB;      // bytes per K or V tile
-  static constexpr int LOADS = TILE / (kThreads * 16);  // 1 KB loads per wave per tile
+  static constexpr int PIECES = TILE / 1024;  // 1 KB pieces per tile (one load instruction each)
 };
 
 // Chunk swizzles (chunk index XOR f(row)).  K: the 16 rows read together
@@ -116,6 +118,8 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// LDS pointers are 32-bit address-space-3 pointers throughout.
+typedef __attribute__((address_space(3))) char lds_t;
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 // global_load_lds writes LDS asynchronously and is counted by vmcnt: each
@@ -132,11 +136,12 @@ __device__ __forceinline__ void tile_barrier() {
 // source of each lane is the chunk whose swizzled position that is.
 template <int D, bool IS_V>
 __device__ __forceinline__ void stage_tile(const __bf16* __restrict__ G, int k0, int Nkv,
-                                           char* buf, int wave, int lane) {
+                                           lds_t* buf, int wave, int lane) {
   using Gm = Geo<D>;
 #pragma unroll
-  for (int n = 0; n < Gm::LOADS; ++n) {
-    const int inst = wave * Gm::LOADS + n;
+  for (int n = 0; n < (Gm::PIECES + kWaves - 1) / kWaves; ++n) {
+    const int inst = n * kWaves + wave;
+    if (Gm::PIECES % kWaves != 0 && inst >= Gm::PIECES) break;
     const int p = inst * 64 + lane;
     const int row = p / Gm::CPR, pc = p % Gm::CPR;
     const int lc = pc ^ (IS_V ? swz_v<D>(row) : swz_k<D>(row));
@@ -155,13 +160,13 @@ struct Frags {
 
 // S^T for one 32-key step: keys rows [sub*32, sub*32+32) of the K stage.
 template <int D>
-__device__ __forceinline__ void qk_step(f32x16 (&S)[kQB], const char* kst, const int (&koff)[Geo<D>::KS],
+__device__ __forceinline__ void qk_step(f32x16 (&S)[kQB], const lds_t* kst, const int (&koff)[Geo<D>::KS],
                                         const bf16x8 (&q)[kQB][Geo<D>::KS]) {
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) S[qb] = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < Geo<D>::KS; ++ks) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(kst + koff[ks]);
+    const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kst + koff[ks]);
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) S[qb] = mfma32(a, q[qb][ks], S[qb]);
   }
@@ -238,14 +243,14 @@ __device__ __forceinline__ void rowmax_step(const f32x16 (&S)[kQB], float (&m)[k
 // O^T += V^T P^T for one 32-key step: value rows [sub*32, sub*32+32) of the V stage.
 // MFMA k index 8*half + j <-> key 16*hc + 8*(j/4) + 4*half + (j%4) of the step.
 template <int D>
-__device__ __forceinline__ void pv_step(Frags<D>& f, const bf16x8 (&P)[kQB][2], const char* vst,
+__device__ __forceinline__ void pv_step(Frags<D>& f, const bf16x8 (&P)[kQB][2], const lds_t* vst,
                                         const int (&voff)[Geo<D>::DB]) {
   typedef short i16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int hc = 0; hc < 2; ++hc)
 #pragma unroll
     for (int db = 0; db < Geo<D>::DB; ++db) {
-      const char* base = vst + voff[db] + 16 * hc * Geo<D>::ROWB;
+      const lds_t* base = vst + voff[db] + 16 * hc * Geo<D>::ROWB;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) i16x4*)(base));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -262,73 +267,103 @@ template <int D>
 struct PassCtx {
   const __bf16* Kb;
   const __bf16* Vb;
-  char* ks[kStages];
-  char* vs[kStages];
+  lds_t *k0, *k1, *k2;  // K stages (separate scalars: never an indexed array)
+  lds_t *v0, *v1, *v2;  // V stages
   int Nkv, ntiles, wave, lane, half;
   float c;
   int koff[Geo<D>::KS];
   int voff[Geo<D>::DB];
 };
 
-template <int D>
-__device__ __forceinline__ char* stage_of(char* const (&st)[kStages], int PH, int t) {
-  if (PH >= 0) return st[PH % kStages];
-  const int i = t % kStages;
-  return i == 0 ? st[0] : (i == 1 ? st[1] : st[2]);
+// Stage of tile t: PH = t % 3 when known at compile time, else -1.
+__device__ __forceinline__ lds_t* stage_of(lds_t* s0, lds_t* s1, lds_t* s2, int PH, int t) {
+  const int i = PH >= 0 ? PH % kStages : t % kStages;
+  return i == 0 ? s0 : (i == 1 ? s1 : s2);
+}
+#define KSTAGE(x, PH, t) stage_of((x).k0, (x).k1, (x).k2, (PH), (t))
+#define VSTAGE(x, PH, t) stage_of((x).v0, (x).v1, (x).v2, (PH), (t))
+
+// Ask the scheduler to interleave one slot's 32 MFMAs with its LDS reads and
+// its softmax VALU work (groups are filled in order; empty ones are skipped).
+__device__ __forceinline__ void interleave_slot() {
+#pragma unroll
+  for (int i = 0; i < 16 * kQB; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // five VALU
+  }
 }
 
-// One 64-key tile t = two 32-key steps.  PH = t % 3 when known at compile
+// One 32-key slot: QK^T of the next step into Sn, PV of the previous step
+// from Pp, softmax of this step from Sc into Pc.
+template <int D, bool MASK>
+__device__ __forceinline__ void slot(Frags<D>& f, const f32x16 (&Sc)[kQB], f32x16 (&Sn)[kQB],
+                                     const bf16x8 (&Pp)[kQB][2], bf16x8 (&Pc)[kQB][2],
+                                     const lds_t* k_next, const lds_t* v_prev,
+                                     const PassCtx<D>& x, int key0, bool& flag) {
+  qk_step<D>(Sn, k_next, x.koff, f.q);
+  pv_step<D>(f, Pp, v_prev, x.voff);
+  softmax_step<D, MASK>(Sc, Pc, f, x.c, key0, x.Nkv, x.half, flag);
+  interleave_slot();
+}
+
+// One 64-key tile t = slots 2t and 2t+1.  PH = t % 3 when known at compile
 // time (the unrolled main loop: every LDS stage is then a distinct array and
-// the loads into stage t+2 overlap the reads of stages t, t+1), or -1.
-// On entry S0 holds S^T of the tile's first step; on exit S0 holds S^T of
-// the next tile's first step (garbage past the last tile: computed from
-// stale LDS, never used).
+// the loads into stage t+2 overlap the reads of the others), or -1.
+// On entry S0 holds S^T of step 2t and Pa holds P of step 2t-1; on exit S0
+// holds S^T of step 2t+2 (garbage past the last tile, never used) and Pa
+// holds P of step 2t+1.
 template <int D, int PH, bool MASK>
 __device__ __forceinline__ void tile_trip(int t, Frags<D>& f, f32x16 (&S0)[kQB], f32x16 (&S1)[kQB],
+                                          bf16x8 (&Pa)[kQB][2], bf16x8 (&Pb)[kQB][2],
                                           const PassCtx<D>& x, bool& flag) {
   using Gm = Geo<D>;
   tile_barrier();  // K_{t+1}, V_t landed; every wave is done with tile t-1
   const int p2 = PH >= 0 ? PH + 2 : -1, p1 = PH >= 0 ? PH + 1 : -1;
   if (t + 2 < x.ntiles)
-    stage_tile<D, false>(x.Kb, (t + 2) * kBN, x.Nkv, stage_of<D>(x.ks, p2, t + 2), x.wave, x.lane);
+    stage_tile<D, false>(x.Kb, (t + 2) * kBN, x.Nkv, KSTAGE(x, p2, t + 2), x.wave, x.lane);
   if (t + 1 < x.ntiles)
-    stage_tile<D, true>(x.Vb, (t + 1) * kBN, x.Nkv, stage_of<D>(x.vs, p1, t + 1), x.wave, x.lane);
-  const char* kcur = stage_of<D>(x.ks, PH, t);
-  const char* knext = stage_of<D>(x.ks, p1, t + 1);
-  const char* vcur = stage_of<D>(x.vs, PH, t);
+    stage_tile<D, true>(x.Vb, (t + 1) * kBN, x.Nkv, VSTAGE(x, p1, t + 1), x.wave, x.lane);
+  const lds_t* kcur = KSTAGE(x, PH, t);
+  const lds_t* knext = KSTAGE(x, p1, t + 1);
+  const lds_t* vcur = VSTAGE(x, PH, t);
+  const lds_t* vprev = VSTAGE(x, p2, t + 2);  // stage of tile t-1
   const int key0 = t * kBN;
-  bf16x8 P[kQB][2];
-
-  // step 2t: QK^T of step 2t+1 || softmax of step 2t; then PV of step 2t
-  qk_step<D>(S1, kcur + 32 * Gm::ROWB, x.koff, f.q);
-  softmax_step<D, MASK>(S0, P, f, x.c, key0, x.Nkv, x.half, flag);
-  pv_step<D>(f, P, vcur, x.voff);
-  // step 2t+1: QK^T of step 2t+2 (next tile) || softmax of step 2t+1; PV
-  qk_step<D>(S0, knext, x.koff, f.q);
-  softmax_step<D, MASK>(S1, P, f, x.c, key0 + 32, x.Nkv, x.half, flag);
-  pv_step<D>(f, P, vcur + 32 * Gm::ROWB, x.voff);
+  slot<D, MASK>(f, S0, S1, Pa, Pb, kcur + 32 * Gm::ROWB, vprev + 32 * Gm::ROWB, x, key0, flag);
+  slot<D, MASK>(f, S1, S0, Pb, Pa, knext, vcur, x, key0 + 32, flag);
 }
 
 // One full pass over the keys: stage, the unmasked tiles (unrolled by the
-// stage count), then the partial last tile (if any) with masking.
+// stage count), the partial last tile (if any) with masking, then the PV of
+// the last step.
 template <int D>
 __device__ __forceinline__ void run_pass(Frags<D>& f, const PassCtx<D>& x, bool& flag) {
-  stage_tile<D, false>(x.Kb, 0, x.Nkv, x.ks[0], x.wave, x.lane);
-  if (x.ntiles > 1) stage_tile<D, false>(x.Kb, kBN, x.Nkv, x.ks[1], x.wave, x.lane);
-  stage_tile<D, true>(x.Vb, 0, x.Nkv, x.vs[0], x.wave, x.lane);
+  using Gm = Geo<D>;
+  // The first slot multiplies P = 0 by the V stage of tile -1 (stage 2): zero
+  // it so no stale Inf/NaN bit pattern can turn 0 * V into NaN.
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  for (int i = threadIdx.x; i < Gm::TILE / 16; i += kThreads)
+    reinterpret_cast<__attribute__((address_space(3))) u32x4*>(x.v2)[i] = u32x4{0u, 0u, 0u, 0u};
+  stage_tile<D, false>(x.Kb, 0, x.Nkv, x.k0, x.wave, x.lane);
+  if (x.ntiles > 1) stage_tile<D, false>(x.Kb, kBN, x.Nkv, x.k1, x.wave, x.lane);
+  stage_tile<D, true>(x.Vb, 0, x.Nkv, x.v0, x.wave, x.lane);
   f32x16 S0[kQB], S1[kQB];
+  bf16x8 Pa[kQB][2], Pb[kQB][2];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) Pa[qb][0] = Pa[qb][1] = bf16x8{};
   tile_barrier();  // K tile 0 (and K 1, V 0) landed
-  qk_step<D>(S0, x.ks[0], x.koff, f.q);
+  qk_step<D>(S0, x.k0, x.koff, f.q);
   const bool partial = (x.Nkv % kBN) != 0;
   const int nfull = partial ? x.ntiles - 1 : x.ntiles;
   int t = 0;
   for (; t + kStages <= nfull; t += kStages) {
-    tile_trip<D, 0, false>(t, f, S0, S1, x, flag);
-    tile_trip<D, 1, false>(t + 1, f, S0, S1, x, flag);
-    tile_trip<D, 2, false>(t + 2, f, S0, S1, x, flag);
+    tile_trip<D, 0, false>(t, f, S0, S1, Pa, Pb, x, flag);
+    tile_trip<D, 1, false>(t + 1, f, S0, S1, Pa, Pb, x, flag);
+    tile_trip<D, 2, false>(t + 2, f, S0, S1, Pa, Pb, x, flag);
   }
-  for (; t < nfull; ++t) tile_trip<D, -1, false>(t, f, S0, S1, x, flag);
-  if (partial) tile_trip<D, -1, true>(t, f, S0, S1, x, flag);
+  for (; t < nfull; ++t) tile_trip<D, -1, false>(t, f, S0, S1, Pa, Pb, x, flag);
+  if (partial) tile_trip<D, -1, true>(t, f, S0, S1, Pa, Pb, x, flag);
+  pv_step<D>(f, Pa, VSTAGE(x, -1, x.ntiles - 1) + 32 * Gm::ROWB, x.voff);
 }
 
 // Exact row max over all keys (only when the fixed-reference loop flagged).
@@ -340,12 +375,12 @@ __device__ __forceinline__ void exact_max_pass(Frags<D>& f, const PassCtx<D>& x)
   for (int qb = 0; qb < kQB; ++qb) m[qb] = -INFINITY;
   for (int t = 0; t < x.ntiles; ++t) {
     __syncthreads();  // every wave is done reading the stage
-    stage_tile<D, false>(x.Kb, t * kBN, x.Nkv, x.ks[0], x.wave, x.lane);
+    stage_tile<D, false>(x.Kb, t * kBN, x.Nkv, x.k0, x.wave, x.lane);
     tile_barrier();  // landed
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       f32x16 S[kQB];
-      qk_step<D>(S, x.ks[0] + sub * 32 * Gm::ROWB, x.koff, f.q);
+      qk_step<D>(S, x.k0 + sub * 32 * Gm::ROWB, x.koff, f.q);
       if (t * kBN + kBN > x.Nkv)
         rowmax_step<true>(S, m, t * kBN + sub * 32, x.Nkv, x.half);
       else
@@ -358,7 +393,7 @@ __device__ __forceinline__ void exact_max_pass(Frags<D>& f, const PassCtx<D>& x)
 }
 
 template <int D, bool OUT_F32>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                           const __bf16* __restrict__ V, void* __restrict__ Oout,
                           float* __restrict__ LSE, int Nq, int Nkv, int n_qtiles, int total_tiles,
@@ -382,8 +417,8 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   PassCtx<D> x;
   x.Kb = K + (int64_t)bh * Nkv * D;
   x.Vb = V + (int64_t)bh * Nkv * D;
-  x.ks[0] = k0s; x.ks[1] = k1s; x.ks[2] = k2s;
-  x.vs[0] = v0s; x.vs[1] = v1s; x.vs[2] = v2s;
+  x.k0 = (lds_t*)k0s; x.k1 = (lds_t*)k1s; x.k2 = (lds_t*)k2s;
+  x.v0 = (lds_t*)v0s; x.v1 = (lds_t*)v1s; x.v2 = (lds_t*)v2s;
   x.Nkv = Nkv;
   x.ntiles = (Nkv + kBN - 1) / kBN;
   x.wave = wave;
