@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--no-ring", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run three 1 GiB device-to-device copies (counter calibration)")
     return ap.parse_args()
 
 
@@ -194,6 +196,16 @@ def main():
                      "ring_block_fwd_TFLOPs": attn_flops(B, H_FULL, N, s, D) / (blk_ms * 1e-3) / 1e12,
                      "merge_ms": mrg_ms, "merge_GBps": merge_bytes / (mrg_ms * 1e-3) / 1e9})
         del o_parts, l_parts
+
+    if args.copy_probe:
+        # A plain copy of known size: what FETCH_SIZE / WRITE_SIZE read for
+        # 1 GiB in and 1 GiB out calibrates the attention kernel's counters.
+        src = torch.empty(1 << 30, device=dev, dtype=torch.uint8).fill_(7)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
