@@ -45,6 +45,27 @@ def attn_flops(b, h, nq, nkv, d):
     return 4.0 * b * h * nq * nkv * d
 
 
+KERNEL_SRC = os.path.join(ROOT, "diffusion_transformer_attention_amd", "csrc", "attn_bf16.hip")
+COUNTERS_MD = os.path.join(ROOT, "profiles", "attn_fwd_bf16_ulysses_share.md")
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed FETCH_SIZE / WRITE_SIZE
+    counters (already scaled by the copy-kernel calibration), or None when the
+    kernel source has changed since they were taken."""
+    import hashlib
+    try:
+        text = open(COUNTERS_MD).read()
+        fields = dict(l.split(": ", 1) for l in text.splitlines()
+                      if l.startswith(("counters-for-source-sha256:", "traffic_bytes_per_launch:")))
+        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if fields.get("counters-for-source-sha256", "").strip() != src:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,7 +244,7 @@ def main():
         "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16_kernel<128,false>",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
                      "flops_per_launch": flops_launch, "launches_timed": len(attn_ms)},
         "cpu_baseline": cpu,
         "legs": legs,
