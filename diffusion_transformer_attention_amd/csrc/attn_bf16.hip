@@ -239,10 +239,12 @@ __device__ __forceinline__ void rowmax_step(const f32x4 (&S)[2][kQB], float (&m)
 
 // One 32-key slot: QK^T of the next step into Sn (K rows at k_next), PV of
 // the previous step from Pp (V rows at v_prev), softmax of this step from Sc
-// into Pc.  Laid out as 16 groups fenced by sched_barrier(0); group i issues
-// the LDS reads for fragment i/2 + LA (even i), the QK^T MFMA i (ks = i/4,
-// kb = (i/2)%2, qb = i%2), the PV MFMA i (db = i/2, qb = i%2) and softmax
-// score i (qb = i/8, kb = (i/4)%2, r = i%4).
+// into Pc.  Laid out as 16 groups fenced by sched_barrier(0): group g runs
+// the QK^T MFMAs [g NQK/16, (g+1) NQK/16) (index i: ks = i / 2kQB, kb =
+// (i / kQB) % 2, qb = i % kQB), the PV MFMAs [g NPV/16, (g+1) NPV/16)
+// (index j: db = j / kQB, qb = j % kQB) and the softmax scores
+// [g NS/16, (g+1) NS/16) (index e: qb = e / 8, kb = (e / 4) % 2, r = e % 4),
+// and issues the LDS reads of the fragments first needed LA groups later.
 // The P^T operand of block qb packs the keys 4g + r (kb 0) and 16 + 4g + r
 // (kb 1): MFMA k index 8g + j <-> key 4g + j (j < 4), 16 + 4g + j - 4 (j >= 4).
 template <int D, bool MASK>
@@ -251,14 +253,17 @@ __device__ __forceinline__ void slot(Frags<D>& f, const f32x4 (&Sc)[2][kQB], f32
                                      const lds_t* k_next, const lds_t* v_prev,
                                      const PassCtx<D>& x, int key0) {
   using Gm = Geo<D>;
-  static_assert(kQB == 2, "group layout assumes two query blocks per wave");
-  constexpr int NKF = 2 * Gm::KS;  // K fragments (ks, kb), ks-major
-  constexpr int NVF = Gm::DB;      // V^T fragments (db)
-  constexpr int LA = 2;            // fragment lookahead
+  constexpr int NG = 16;                       // groups
+  constexpr int NQK = 2 * kQB * Gm::KS;        // QK^T MFMAs
+  constexpr int NPV = kQB * Gm::DB;            // PV MFMAs
+  constexpr int NS = 8 * kQB;                  // softmax scores per lane
+  constexpr int NKF = 2 * Gm::KS;              // K fragments (ks, kb), ks-major
+  constexpr int NVF = Gm::DB;                  // V^T fragments (db)
+  constexpr int LA = 2;                        // read lookahead, in groups
   bf16x8 kf[NKF], vf[NVF];
   // Keep one register for the V^T offsets: hide vxb from loop-invariant code
-  // motion so the eight per-fragment XORs are not hoisted into eight
-  // registers for the whole loop.
+  // motion so the per-fragment XORs are not hoisted into one register each
+  // for the whole loop.
   int vxb = x.vxb;
   asm volatile("" : "+v"(vxb));
   auto load_k = [&](int i) {
@@ -271,11 +276,15 @@ __device__ __forceinline__ void slot(Frags<D>& f, const f32x4 (&Sc)[2][kQB], f32
         bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 16 * Gm::ROWB)));
     vf[i] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
+  // first group that uses K fragment f / V^T fragment f
+  auto kfirst = [](int fi) { return fi * kQB * NG / NQK; };
+  auto vfirst = [](int fi) { return fi * kQB * NG / NPV; };
 #pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    if (i < NKF) load_k(i);
-    if (i < NVF) load_v(i);
-  }
+  for (int fi = 0; fi < NKF; ++fi)
+    if (kfirst(fi) < LA) load_k(fi);
+#pragma unroll
+  for (int fi = 0; fi < NVF; ++fi)
+    if (vfirst(fi) < LA) load_v(fi);
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   float l[kQB], lb[kQB], mc[kQB], p[kQB][8];
 #pragma unroll
@@ -288,35 +297,42 @@ __device__ __forceinline__ void slot(Frags<D>& f, const f32x4 (&Sc)[2][kQB], f32
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) Sn[kb][qb] = f32x4{};
-  constexpr int NG = 16;  // groups: one softmax score each
-  constexpr int NQK = 2 * kQB * Gm::KS, NPV = kQB * Gm::DB;
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int i = 0; i < NG; ++i) {
-    if ((i & 1) == 0) {
-      const int fi = i / 2 + LA;
-      if (fi < NKF) load_k(fi);
-      if (fi < NVF) load_v(fi);
-    }
-    if (i < NQK) {
-      const int ks = i / 4, kb = (i / 2) % 2, qb = i % 2;
+  for (int g = 0; g < NG; ++g) {
+#pragma unroll
+    for (int fi = 0; fi < NKF; ++fi)
+      if (kfirst(fi) >= LA && kfirst(fi) == g + LA) load_k(fi);
+#pragma unroll
+    for (int fi = 0; fi < NVF; ++fi)
+      if (vfirst(fi) >= LA && vfirst(fi) == g + LA) load_v(fi);
+#pragma unroll
+    for (int i = g * NQK / NG; i < (g + 1) * NQK / NG; ++i) {
+      const int ks = i / (2 * kQB), kb = (i / kQB) % 2, qb = i % kQB;
       Sn[kb][qb] = mfma16(kf[ks * 2 + kb], f.q[qb][ks], Sn[kb][qb]);
     }
-    if (i < NPV) {
-      const int db = i / 2, qb = i % 2;
+#pragma unroll
+    for (int j = g * NPV / NG; j < (g + 1) * NPV / NG; ++j) {
+      const int db = j / kQB, qb = j % kQB;
       f.o[qb][db] = mfma16(vf[db], Pp[qb], f.o[qb][db]);
     }
-    {
-      const int qb = i / 8, kb = (i / 4) % 2, r = i % 4;
+#pragma unroll
+    for (int e = g * NS / NG; e < (g + 1) * NS / NG; ++e) {
+      const int qb = e / 8, kb = (e / 4) % 2, r = e % 4;
       float sv = Sc[kb][qb][r];
+      // Pin the softmax work to its group: without the opaque copies the
+      // optimizer sinks it (and the row sums) towards its uses in later
+      // slots, which leaves those slots' MFMAs with no VALU work to hide.
+      asm volatile("" : "+v"(sv));
       if (MASK) sv = (key0 + 16 * kb + 4 * x.g + r < x.Nkv) ? sv : -INFINITY;
       p[qb][4 * kb + r] = __builtin_amdgcn_exp2f(fmaf(sv, x.c, -mc[qb]));
-      if (i & 1) {
+      if (e & 1) {
         const int j = 4 * kb + r - 1;
         const float p0 = p[qb][j], p1 = p[qb][j + 1];
-        const bf16x2 pk = {(__bf16)p0, (__bf16)p1};
+        bf16x2 pk = {(__bf16)p0, (__bf16)p1};
         l[qb] += p0 + p1;
         lb[qb] = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, lb[qb], false);
+        asm volatile("" : "+v"(pk), "+v"(l[qb]), "+v"(lb[qb]));
         Pc[qb][j] = pk[0];
         Pc[qb][j + 1] = pk[1];
       }
