@@ -10,6 +10,10 @@ layer of a Wan-shaped tensor [1,40,32768,128] bf16, run on one GPU:
 Inputs are resident in HBM before the timed region.  `value` is the
 attention FLOPs of the step (4 * 4*B*H*N^2*D) over the step's wall time.
 
+The fused leg runs the same step as four dit_attn_fwd_ulysses calls that
+read the token shards and write the token-shard output directly, with no
+exchange buffers; it is reported under "legs" beside the unfused step time.
+
 The ring leg (K/V in 4 blocks of 8192: four dit_attn_fwd_block calls with
 float32 partials, then dit_attn_merge, B1 H40 N32768 D128) is timed after the
 steps and reported under "legs"; it is not part of `value`.
@@ -195,6 +199,20 @@ def main():
     legs = {"attn_fwd_ms_avg": attn_avg_ms, "attn_fwd_ms_min": float(np.min(attn_ms)),
             "seq2head_ms": s2h_ms, "seq2head_GBps": perm_bytes / (s2h_ms * 1e-3) / 1e9,
             "head2seq_ms": h2s_ms, "head2seq_GBps": perm_bytes / (h2s_ms * 1e-3) / 1e9}
+
+    # fused leg: the same step with dit_attn_fwd_ulysses reading the shards
+    # and writing the token-shard output directly (no exchange buffers)
+    print("[bench] fused Ulysses leg", file=sys.stderr, flush=True)
+    fused_out = torch.empty_like(back)
+
+    def fused_step():
+        for r in range(P):
+            dta.dit_attn_fwd_ulysses(*shards, r, out=fused_out, lse=lses[r])
+
+    fused_ms = time_it(fused_step, reps=3)
+    legs.update({"fused_step_ms": fused_ms,
+                 "fused_step_TFLOPs": P * flops_launch / (fused_ms * 1e-3) / 1e12,
+                 "unfused_step_ms": ms_per_step})
 
     if not args.no_ring:
         print("[bench] ring leg", file=sys.stderr, flush=True)

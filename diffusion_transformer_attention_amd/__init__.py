@@ -21,8 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libditattn.so")
 
 DIT_BF16, DIT_F32 = 0, 1
 DIT_OK, DIT_EINVAL, DIT_EUNSUPPORTED, DIT_EALIGN, DIT_ELAUNCH, DIT_ERANGE = 0, -1, -2, -3, -4, -5
-EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_merge", "ulysses_seq2head",
-            "ulysses_head2seq", "dit_strerror", "dit_abi_version")
+EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_ulysses", "dit_attn_merge",
+            "ulysses_seq2head", "ulysses_head2seq", "dit_strerror", "dit_abi_version")
 
 _lib = None
 
@@ -39,11 +39,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.dit_attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P]
     lib.dit_attn_fwd_block.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, P]
+    lib.dit_attn_fwd_ulysses.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, P]
     lib.dit_attn_merge.argtypes = [P, P, I, P, P, I, I, I, I, I, P]
     lib.ulysses_seq2head.argtypes = [P, P, I, I, I, I, I, I, P]
     lib.ulysses_head2seq.argtypes = [P, P, I, I, I, I, I, I, P]
-    for name in ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_merge", "ulysses_seq2head",
-                 "ulysses_head2seq", "dit_abi_version"):
+    for name in ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_ulysses", "dit_attn_merge",
+                 "ulysses_seq2head", "ulysses_head2seq", "dit_abi_version"):
         getattr(lib, name).restype = ctypes.c_int
     lib.dit_strerror.argtypes = [ctypes.c_int]
     lib.dit_strerror.restype = ctypes.c_char_p
@@ -153,6 +154,39 @@ def dit_attn_fwd_block(q, k, v, scale=None, out_dtype=torch.float32, out=None, l
     return o, lse
 
 
+def dit_attn_fwd_ulysses(q, k, v, r, scale=None, out=None, lse=None, return_lse=True):
+    """Attention of Ulysses head group r read from / written to token shards.
+
+    q, k, v: bf16 [P,B,H,N/P,D] token shards.  Writes heads [r*H/P, (r+1)*H/P)
+    of every shard of `out` (allocated as zeros when None) and returns
+    (out [P,B,H,N/P,D], LSE float32 [B,H/P,N] or None).
+    """
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, 5)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share shape and dtype")
+    P, B, H, Ns, D = q.shape
+    if P == 0 or H % P:
+        raise ValueError("H must be divisible by P")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o = torch.zeros_like(q) if out is None else out
+    _need(o, "out", 5)
+    if o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H // P, Ns * P), device=q.device, dtype=torch.float32)
+    if lse is not None:
+        _need(lse, "lse", 3)
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H // P, Ns * P):
+            raise ValueError("lse must be float32 [B,H/P,N]")
+    rc = lib.dit_attn_fwd_ulysses(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), P, int(r), B, H,
+                                  Ns * P, D, ctypes.c_float(scale), _dtype_code(q.dtype),
+                                  _stream())
+    _check(rc, "dit_attn_fwd_ulysses")
+    return o, lse
+
+
 def dit_attn_merge(o_parts, lse_parts, out_dtype=torch.bfloat16, out=None, lse=None,
                    return_lse=True):
     """Exact LSE merge: o_parts float32 [nblk,B,H,N,D], lse_parts float32 [nblk,B,H,N].
@@ -209,6 +243,6 @@ def ulysses_head2seq(groups, out=None):
     return o
 
 
-__all__ = ["dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_merge", "ulysses_seq2head",
+__all__ = ["dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_ulysses", "dit_attn_merge", "ulysses_seq2head",
            "ulysses_head2seq", "dit_strerror", "dit_abi_version", "load_library", "DitError",
            "LIB_PATH", "EXPORTED", "DIT_BF16", "DIT_F32"]

@@ -97,6 +97,23 @@ int dit_attn_merge(const float* o_parts, const float* lse_parts, int nblk, void*
                                           static_cast<hipStream_t>(stream)));
 }
 
+int dit_attn_fwd_ulysses(const void* q, const void* k, const void* v, void* o, float* lse, int P,
+                         int r, int B, int H, int N, int D, float scale, int dtype, void* stream) {
+  if (P < 1 || r < 0 || r >= P || B < 0 || H < 0 || N < 0 || D <= 0) return DIT_EINVAL;
+  if (!(isfinite(scale) && scale > 0.0f)) return DIT_EINVAL;
+  if (H % P != 0 || N % P != 0) return DIT_EINVAL;
+  if (dtype != DIT_BF16) return DIT_EUNSUPPORTED;
+  if (!supported_head_dim(D)) return DIT_EUNSUPPORTED;
+  if ((N / P) % 64 != 0) return DIT_EUNSUPPORTED;  // a key tile must not straddle two shards
+  if (!size_ok(B, H, N, D)) return DIT_ERANGE;
+  if (B == 0 || H == 0 || N == 0) return DIT_OK;
+  if (!q || !k || !v || !o) return DIT_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return DIT_EALIGN;
+  if (lse && !aligned(lse, 4)) return DIT_EALIGN;
+  return map_launch(ditattn::launch_attn_bf16_ulysses(q, k, v, o, lse, P, r, B, H, N, D, scale,
+                                                      static_cast<hipStream_t>(stream)));
+}
+
 int ulysses_seq2head(const void* in, void* out, int P, int B, int H, int N, int D, int elem_bytes,
                      void* stream) {
   return permute_common(in, out, P, B, H, N, D, elem_bytes, false, stream);

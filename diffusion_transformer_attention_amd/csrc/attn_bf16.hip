@@ -139,14 +139,23 @@ __device__ __forceinline__ void tile_barrier() {
 // Stage one 64-key tile of K (or V) into LDS.  Each load instruction writes
 // 1 KB contiguously (lane i -> bytes [16i, 16i+16)); voff[n] is the byte
 // offset, within a tile, of the global chunk whose swizzled position that
-// is (see piece_offsets).  The descriptor covers rows [k0, Nkv) only, so
-// rows past the end read as zero.
+// is (see piece_offsets).  The keys of one (b, h) lie in segments of kseg
+// rows, sstride elements apart (a single segment unless the keys come from
+// Ulysses token shards, whose length is then a multiple of the tile).  The
+// descriptor covers the tile's rows up to the end of its segment, so rows
+// past the end read as zero.
 template <int D>
-__device__ __forceinline__ void stage_tile(const __bf16* __restrict__ G, int k0, int Nkv,
-                                           lds_t* buf, int wave, const int* voff) {
+__device__ __forceinline__ void stage_tile(const __bf16* __restrict__ G, int k0, int kseg,
+                                           int64_t sstride, lds_t* buf, int wave, const int* voff) {
   using Gm = Geo<D>;
+  int local = k0;
+  if (k0 >= kseg) {
+    const int sg = k0 / kseg;
+    local = k0 - sg * kseg;
+    G += sg * sstride;
+  }
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(G + (int64_t)k0 * D), (short)0, (Nkv - k0) * Gm::ROWB, 0x00020000);
+      (void*)(G + (int64_t)local * D), (short)0, (kseg - local) * Gm::ROWB, 0x00020000);
 #pragma unroll
   for (int n = 0; n < (Gm::PIECES + kWaves - 1) / kWaves; ++n) {
     const int inst = n * kWaves + wave;
@@ -179,8 +188,10 @@ struct Frags {
 // Everything one pass over the keys needs.
 template <int D>
 struct PassCtx {
-  const __bf16* Kb;
+  const __bf16* Kb;  // keys / values of this (b, h): segment 0
   const __bf16* Vb;
+  int kseg;          // keys per segment (Nkv for contiguous keys)
+  int64_t sstride;   // elements from one segment to the next
   lds_t *k0, *k1, *k2;  // K stages (separate scalars: never an indexed array)
   lds_t *v0, *v1, *v2;  // V stages
   int Nkv, ntiles, wave, lane, g;
@@ -360,9 +371,9 @@ __device__ __forceinline__ void tile_trip(int t, Frags<D>& f, f32x4 (&S0)[2][kQB
   tile_barrier();  // K_{t+1}, V_t landed; every wave is done with tile t-1
   const int p2 = PH >= 0 ? PH + 2 : -1, p1 = PH >= 0 ? PH + 1 : -1;
   if (t + 2 < x.ntiles)
-    stage_tile<D>(x.Kb, (t + 2) * kBN, x.Nkv, KSTAGE(x, p2, t + 2), x.wave, x.kld);
+    stage_tile<D>(x.Kb, (t + 2) * kBN, x.kseg, x.sstride, KSTAGE(x, p2, t + 2), x.wave, x.kld);
   if (t + 1 < x.ntiles)
-    stage_tile<D>(x.Vb, (t + 1) * kBN, x.Nkv, VSTAGE(x, p1, t + 1), x.wave, x.vld);
+    stage_tile<D>(x.Vb, (t + 1) * kBN, x.kseg, x.sstride, VSTAGE(x, p1, t + 1), x.wave, x.vld);
   const lds_t* kcur = KSTAGE(x, PH, t);
   const lds_t* knext = KSTAGE(x, p1, t + 1);
   const lds_t* vcur = VSTAGE(x, PH, t);
@@ -399,9 +410,9 @@ __device__ __forceinline__ bool run_pass(Frags<D>& f, const PassCtx<D>& x) {
   // it so no stale Inf/NaN bit pattern can turn 0 * V into NaN.
   for (int i = threadIdx.x; i < Gm::TILE / 16; i += kThreads)
     reinterpret_cast<lds_u32x4*>(x.v2)[i] = u32x4{0u, 0u, 0u, 0u};
-  stage_tile<D>(x.Kb, 0, x.Nkv, x.k0, x.wave, x.kld);
-  if (x.ntiles > 1) stage_tile<D>(x.Kb, kBN, x.Nkv, x.k1, x.wave, x.kld);
-  stage_tile<D>(x.Vb, 0, x.Nkv, x.v0, x.wave, x.vld);
+  stage_tile<D>(x.Kb, 0, x.kseg, x.sstride, x.k0, x.wave, x.kld);
+  if (x.ntiles > 1) stage_tile<D>(x.Kb, kBN, x.kseg, x.sstride, x.k1, x.wave, x.kld);
+  stage_tile<D>(x.Vb, 0, x.kseg, x.sstride, x.v0, x.wave, x.vld);
   f32x4 S0[2][kQB], S1[2][kQB];
   bf16x8 Pa[kQB], Pb[kQB];
 #pragma unroll
@@ -445,7 +456,7 @@ __device__ __forceinline__ void exact_max_pass(Frags<D>& f, const PassCtx<D>& x)
   for (int qb = 0; qb < kQB; ++qb) m[qb] = -INFINITY;
   for (int t = 0; t < x.ntiles; ++t) {
     __syncthreads();  // every wave is done reading the stage
-    stage_tile<D>(x.Kb, t * kBN, x.Nkv, x.k0, x.wave, x.kld);
+    stage_tile<D>(x.Kb, t * kBN, x.kseg, x.sstride, x.k0, x.wave, x.kld);
     tile_barrier();  // landed
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -462,12 +473,33 @@ __device__ __forceinline__ void exact_max_pass(Frags<D>& f, const PassCtx<D>& x)
   for (int qb = 0; qb < kQB; ++qb) f.m[qb] = m[qb];
 }
 
+// Where the tokens of one (b, h) live.  Contiguous [B,H,N,D] tensors are one
+// segment per (b, h) (qseg = Nq, kseg = Nkv, hg = htot = H, hoff = 0).  Ulysses
+// token shards [P][B,H,N/P,D] hold the N tokens of head h in P segments of
+// N/P rows, one per shard; the launch then covers the hg = H/P heads of one
+// head group, starting at head hoff.
+struct Layout {
+  int qseg, kseg;  // query / key rows per segment
+  int hg;          // heads covered by the launch
+  int htot;        // heads in the buffers
+  int hoff;        // first head of the launch
+  int B;
+};
+
+// Element offset of token n of the (b, hh) head: segment n / seg.
+__device__ __forceinline__ int64_t token_offset(int n, int seg, int64_t head_elems,
+                                                int64_t sstride, int D) {
+  if (n < seg) return head_elems + (int64_t)n * D;
+  const int sg = n / seg;
+  return head_elems + sg * sstride + (int64_t)(n - sg * seg) * D;
+}
+
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                           const __bf16* __restrict__ V, void* __restrict__ Oout,
                           float* __restrict__ LSE, int Nq, int Nkv, int n_qtiles, int total_tiles,
-                          float c) {
+                          float c, Layout lay) {
   using Gm = Geo<D>;
   __shared__ __attribute__((aligned(1024))) char k0s[Gm::TILE];
   __shared__ __attribute__((aligned(1024))) char k1s[Gm::TILE];
@@ -483,10 +515,16 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15, g = lane >> 4;
 
-  const __bf16* Qb = Q + (int64_t)bh * Nq * D;
+  // bh = b * hg + h'; the buffers hold head hoff + h' of batch b.
+  const int bb = bh / lay.hg;
+  const int hh = lay.hoff + (bh - bb * lay.hg);
+  const int64_t qhead = ((int64_t)bb * lay.htot + hh) * lay.qseg * D;
+  const int64_t qsstride = (int64_t)lay.B * lay.htot * lay.qseg * D;
   PassCtx<D> x;
-  x.Kb = K + (int64_t)bh * Nkv * D;
-  x.Vb = V + (int64_t)bh * Nkv * D;
+  x.Kb = K + ((int64_t)bb * lay.htot + hh) * lay.kseg * D;
+  x.Vb = V + ((int64_t)bb * lay.htot + hh) * lay.kseg * D;
+  x.kseg = lay.kseg;
+  x.sstride = (int64_t)lay.B * lay.htot * lay.kseg * D;
   x.k0 = (lds_t*)k0s; x.k1 = (lds_t*)k1s; x.k2 = (lds_t*)k2s;
   x.v0 = (lds_t*)v0s; x.v1 = (lds_t*)v1s; x.v2 = (lds_t*)v2s;
   x.Nkv = Nkv;
@@ -521,7 +559,8 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     const int row = min(qrow0 + 16 * qb, Nq - 1);
 #pragma unroll
     for (int ks = 0; ks < Gm::KS; ++ks)
-      f.q[qb][ks] = *reinterpret_cast<const bf16x8*>(Qb + (int64_t)row * D + ks * 32 + g * 8);
+      f.q[qb][ks] = *reinterpret_cast<const bf16x8*>(
+          Q + token_offset(row, lay.qseg, qhead, qsstride, D) + ks * 32 + g * 8);
     f.m[qb] = -INFINITY;
     f.l[qb] = 0.f;
     f.lb[qb] = 0.f;
@@ -551,7 +590,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     const float inv = 1.0f / quad_sum(f.lb[qb]);
     const int qrow = qrow0 + 16 * qb;
     if (qrow < Nq) {
-      const int64_t obase = ((int64_t)bh * Nq + qrow) * D;
+      const int64_t obase = token_offset(qrow, lay.qseg, qhead, qsstride, D);
 #pragma unroll
       for (int db = 0; db < Gm::DB; ++db) {
         const int d0 = db * 16 + 4 * g;
@@ -571,15 +610,26 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
 }
 
 template <int D, bool OUT_F32>
-hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                    int H, int Nq, int Nkv, float c, hipStream_t stream) {
+hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float* lse, int Nq,
+                    int Nkv, float c, const Layout& lay, hipStream_t stream) {
   const int n_qtiles = (Nq + kBM - 1) / kBM;
-  const int64_t total = (int64_t)B * H * n_qtiles;
+  const int64_t total = (int64_t)lay.B * lay.hg * n_qtiles;
   if (total > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OUT_F32>), dim3((unsigned)total), dim3(kThreads), 0,
                      stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                     static_cast<const __bf16*>(v), o, lse, Nq, Nkv, n_qtiles, (int)total, c);
+                     static_cast<const __bf16*>(v), o, lse, Nq, Nkv, n_qtiles, (int)total, c, lay);
   return hipGetLastError();
+}
+
+template <bool OUT_F32>
+hipError_t launch_layout(const void* q, const void* k, const void* v, void* o, float* lse, int Nq,
+                         int Nkv, int D, float scale, const Layout& lay, hipStream_t stream) {
+  const float c = scale * 1.4426950408889634f;
+  switch (D) {
+    case 32: return launch_d<32, OUT_F32>(q, k, v, o, lse, Nq, Nkv, c, lay, stream);
+    case 64: return launch_d<64, OUT_F32>(q, k, v, o, lse, Nq, Nkv, c, lay, stream);
+    default: return launch_d<128, OUT_F32>(q, k, v, o, lse, Nq, Nkv, c, lay, stream);
+  }
 }
 
 }  // namespace
@@ -587,19 +637,17 @@ hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float*
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                             int B, int H, int Nq, int Nkv, int D, float scale, bool o_f32,
                             hipStream_t stream) {
-  const float c = scale * 1.4426950408889634f;
-  if (o_f32) {
-    switch (D) {
-      case 32: return launch_d<32, true>(q, k, v, o, lse, B, H, Nq, Nkv, c, stream);
-      case 64: return launch_d<64, true>(q, k, v, o, lse, B, H, Nq, Nkv, c, stream);
-      default: return launch_d<128, true>(q, k, v, o, lse, B, H, Nq, Nkv, c, stream);
-    }
-  }
-  switch (D) {
-    case 32: return launch_d<32, false>(q, k, v, o, lse, B, H, Nq, Nkv, c, stream);
-    case 64: return launch_d<64, false>(q, k, v, o, lse, B, H, Nq, Nkv, c, stream);
-    default: return launch_d<128, false>(q, k, v, o, lse, B, H, Nq, Nkv, c, stream);
-  }
+  const Layout lay{Nq, Nkv, H, H, 0, B};
+  return o_f32 ? launch_layout<true>(q, k, v, o, lse, Nq, Nkv, D, scale, lay, stream)
+               : launch_layout<false>(q, k, v, o, lse, Nq, Nkv, D, scale, lay, stream);
+}
+
+hipError_t launch_attn_bf16_ulysses(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, int P, int r, int B, int H, int N, int D,
+                                    float scale, hipStream_t stream) {
+  const int ns = N / P, hg = H / P;
+  const Layout lay{ns, ns, hg, H, r * hg, B};
+  return launch_layout<false>(q, k, v, o, lse, N, N, D, scale, lay, stream);
 }
 
 }  // namespace ditattn

@@ -11,6 +11,13 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
                             int B, int H, int Nq, int Nkv, int D, float scale, bool o_f32,
                             hipStream_t stream);
 
+// bf16 q/k/v/o in Ulysses token-shard layout [P][B,H,N/P,D]: attention of
+// head group r (heads [r*H/P, (r+1)*H/P)) over all N tokens.  lse is
+// [B,H/P,N] or null.  Requires (N/P) % 64 == 0.
+hipError_t launch_attn_bf16_ulysses(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, int P, int r, int B, int H, int N, int D,
+                                    float scale, hipStream_t stream);
+
 // float32 q/k/v/o.  lse may be null.
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                            int B, int H, int Nq, int Nkv, int D, float scale, hipStream_t stream);

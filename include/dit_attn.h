@@ -47,9 +47,10 @@ typedef enum { DIT_BF16 = 0, DIT_F32 = 1 } dit_dtype;
 enum {
   DIT_OK = 0,
   DIT_EINVAL = -1,       /* null pointer, negative size, Nkv == 0, scale not finite or <= 0,
-                            H % P != 0, N % P != 0, nblk < 1, P < 1 */
+                            H % P != 0, N % P != 0, nblk < 1, P < 1, r outside [0, P) */
   DIT_EUNSUPPORTED = -2, /* D not in {32, 64, 128}, a dtype combination not built, elem_bytes
-                            not in {1, 2, 4, 8} */
+                            not in {1, 2, 4, 8}, fused Ulysses shard length not a multiple
+                            of 64 */
   DIT_EALIGN = -3,       /* q/k/v/o/o_parts not 16-byte aligned, lse not 4-byte aligned,
                             permute buffers not aligned to elem_bytes */
   DIT_ELAUNCH = -4,      /* the HIP runtime reported an error at launch */
@@ -108,6 +109,33 @@ int dit_attn_fwd_block(const void* q, const void* k, const void* v, void* o, flo
  */
 int dit_attn_merge(const float* o_parts, const float* lse_parts, int nblk,
                    void* o, float* lse, int B, int H, int N, int D, int o_dtype, void* stream);
+
+/*
+ * Attention of one Ulysses head group read straight from the token shards
+ * and written straight back into them: ulysses_seq2head of q, k, v, then
+ * dit_attn_fwd on head group r, then ulysses_head2seq of that group's
+ * output, without the exchange buffers ([HB] Ulysses simulation: the
+ * all_to_all_heads / per-card attention / all_to_all_tokens sequence of one
+ * card, r being its rank).
+ *
+ *   q, k, v : bf16 [P][B,H,N/P,D]   rank s holds every head of tokens
+ *                                   [s*N/P, (s+1)*N/P)
+ *   o       : bf16 [P][B,H,N/P,D]   only heads [r*H/P, (r+1)*H/P) of every
+ *                                   shard are written; the other heads are
+ *                                   left untouched, so the P calls r = 0..P-1
+ *                                   fill the whole output
+ *   lse     : float32 [B,H/P,N] for head group r (natural log, scale
+ *             included), or NULL to skip
+ *   0 <= r < P;  N is the full sequence length; dtype must be DIT_BF16.
+ * The O and LSE values are bit-identical to the unfused sequence above (the
+ * same kernel, with different addressing).  Requires H % P == 0 and
+ * N % P == 0 (DIT_EINVAL otherwise, [PR] "Limitations") and, as a limit of
+ * this implementation, (N/P) % 64 == 0 (DIT_EUNSUPPORTED otherwise; use the
+ * unfused sequence).
+ */
+int dit_attn_fwd_ulysses(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int P, int r, int B, int H, int N, int D, float scale, int dtype,
+                         void* stream);
 
 /*
  * Ulysses sequence -> head exchange as it lands on one device ([HB] Ulysses

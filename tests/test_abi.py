@@ -89,6 +89,24 @@ def test_merge_validation(lib):
     assert m(N=0) == dta.DIT_OK
 
 
+def test_fused_ulysses_validation(lib):
+    u = lambda P=4, r=0, H=8, N=512, D=128, dt=0, q=A, o=A, lse=A, scale=0.125: \
+        lib.dit_attn_fwd_ulysses(q, A, A, o, lse, P, r, 1, H, N, D, ctypes.c_float(scale), dt, S)
+    assert u(r=4) == dta.DIT_EINVAL          # rank outside [0, P)
+    assert u(r=-1) == dta.DIT_EINVAL
+    assert u(P=0) == dta.DIT_EINVAL
+    assert u(H=6) == dta.DIT_EINVAL          # heads not divisible by P
+    assert u(N=514) == dta.DIT_EINVAL        # tokens not divisible by P
+    assert u(N=4 * 96) == dta.DIT_EUNSUPPORTED  # shard length 96 not a multiple of 64
+    assert u(dt=1) == dta.DIT_EUNSUPPORTED   # bf16 only
+    assert u(D=80) == dta.DIT_EUNSUPPORTED
+    assert u(scale=0.0) == dta.DIT_EINVAL
+    assert u(q=NULL) == dta.DIT_EINVAL
+    assert u(o=MIS) == dta.DIT_EALIGN
+    assert u(lse=V(0x10002)) == dta.DIT_EALIGN
+    assert u(N=0) == dta.DIT_OK              # nothing to compute
+
+
 @pytest.mark.parametrize("fn", ["ulysses_seq2head", "ulysses_head2seq"])
 def test_permute_validation(lib, fn):
     f = getattr(lib, fn)

@@ -201,6 +201,46 @@ def test_merge_against_oracle(nblk, out):
         assert (Og[0, 0, 10] == 0).all()
 
 
+# ------------------------------------------------------------ fused Ulysses attention
+def _shard(t, P):
+    """[B,H,N,D] -> [P,B,H,N/P,D]: rank s's token slice."""
+    return torch.stack(t.chunk(P, dim=2)).contiguous()
+
+
+@pytest.mark.parametrize("P,B,H,N,D", [
+    (4, 1, 8, 512, 128),     # shards of 128 tokens: a query tile spans two shards
+    (4, 2, 8, 256, 64),      # shards of one 64-key tile: every tile starts a new shard
+    (2, 1, 6, 384, 32),      # three heads per group, shards of 192 tokens (ragged query tiles)
+    (1, 1, 3, 320, 128),     # P = 1: the shard is the whole sequence
+])
+def test_fused_ulysses_small(P, B, H, N, D):
+    """dit_attn_fwd_ulysses == seq2head -> dit_attn_fwd -> head2seq bit for bit,
+    leaves the other groups' heads alone, and matches the oracle."""
+    say("fused ulysses", P, B, H, N, D)
+    qb, kb, vb = datagen.small_bf16(B, H, N, D, seed=7 * N + D + P)
+    full = [bits_to_torch_bf16(x) for x in (qb, kb, vb)]
+    sh = [_shard(t, P) for t in full]
+    groups = [dta.ulysses_seq2head(t) for t in sh]
+    hg = H // P
+    out = torch.full_like(sh[0], -7.0)
+    outs = []
+    for r in range(P):
+        O_ref, L_ref = dta.dit_attn_fwd(groups[0][r], groups[1][r], groups[2][r])
+        before = out.clone()
+        _, L = dta.dit_attn_fwd_ulysses(*sh, r, out=out)
+        assert torch.equal(L, L_ref), f"LSE of group {r}"
+        heads = slice(r * hg, (r + 1) * hg)
+        others = torch.ones(H, dtype=torch.bool)
+        others[heads] = False
+        assert torch.equal(out[:, :, others], before[:, :, others]), "other groups' heads written"
+        outs.append(O_ref)
+    unfused = dta.ulysses_head2seq(torch.stack(outs))
+    assert torch.equal(out, unfused)
+    Oref, Lref = oracle.attention(f64(qb), f64(kb), f64(vb))
+    O_full = torch.cat(list(out), dim=2)
+    assert_bf16_close(to_f64(O_full), None, Oref, Lref, f"fused P{P} B{B} H{H} N{N} D{D}")
+
+
 # ------------------------------------------------------------ full-size workloads
 @pytest.fixture(scope="module")
 def wan_draw():
@@ -242,6 +282,14 @@ def test_ulysses_share(wan_draw):
     O_ul = torch.cat(list(back), dim=2)
     O_single, _ = dta.dit_attn_fwd(*full, return_lse=False)
     assert torch.equal(O_ul, O_single)
+    # the fused entry point reads the shards directly: same bits, no exchange buffers
+    sh = [shard(t) for t in full]
+    out = torch.zeros_like(sh[0])
+    for r in range(P):
+        _, Lr = dta.dit_attn_fwd_ulysses(*sh, r, out=out)
+        if r == 0:
+            assert torch.equal(Lr, L0)
+    assert torch.equal(out, back)
 
 
 def test_ring_merge(wan_draw):
