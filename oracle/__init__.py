@@ -4,11 +4,13 @@ Only tests/, ``__graft_entry__.smoke()`` and bench.py's ``cpu_baseline`` leg
 may import this package.  The HIP library and its Python binding never do.
 """
 from .ref import (attention, attention_rows, probabilities, split_kv, merge,
+                  attention_backward, attention_backward_rows, attention_backward_keys,
                   ring_attention, shard_tokens, seq2head, head2seq,
                   unshard_tokens, ulysses_attention, ulysses_send_bytes_per_rank,
                   default_scale)
 
 __all__ = ["attention", "attention_rows", "probabilities", "split_kv", "merge",
+           "attention_backward", "attention_backward_rows", "attention_backward_keys",
            "ring_attention", "shard_tokens", "seq2head", "head2seq",
            "unshard_tokens", "ulysses_attention", "ulysses_send_bytes_per_rank",
            "default_scale"]

@@ -93,6 +93,87 @@ def probabilities(q, k, scale=None):
 
 
 # --------------------------------------------------------------------------
+# Backward (pull request, "Ring kernel selection": the ring kernels pair with
+# a real backward kernel, timed forward + backward; Validation: dQ/dK/dV are
+# compared against a full-sequence reference).  The pages give no formulas;
+# these are the chain rule applied to the definition above, for the scalar
+# sum(dO * O):
+#   P = softmax_row(scale Q K^T),  O = P V
+#   dV = P^T dO,  dP = dO V^T,  delta_i = sum_d dO_id O_id (= sum_j P_ij dP_ij)
+#   dS = P * (dP - delta),  dQ = scale dS K,  dK = scale dS^T Q
+# --------------------------------------------------------------------------
+def attention_backward(q, k, v, dout, scale=None, row_block=256):
+    """Gradients of sum(dout * attention(q, k, v)[0]) with respect to q, k, v.
+
+    q, dout: [B,H,Nq,D]; k, v: [B,H,Nkv,D].  Returns (dq, dk, dv, delta), all
+    float64, delta [B,H,Nq] = rowsum(dout * O).  Query rows are independent
+    in P, dP and dq; dk and dv sum over them, ``row_block`` rows at a time.
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, Nq, D = q.shape
+    scale = default_scale(D) if scale is None else float(scale)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    delta = np.empty((B, H, Nq), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, Nq, row_block):
+                r1 = min(Nq, r0 + row_block)
+                S = scale * (q[b, h, r0:r1] @ k[b, h].T)
+                E = np.exp(S - S.max(axis=1, keepdims=True))
+                P = E / E.sum(axis=1, keepdims=True)
+                O = P @ v[b, h]
+                dO = dout[b, h, r0:r1]
+                dl = (dO * O).sum(axis=1)
+                dP = dO @ v[b, h].T
+                dS = P * (dP - dl[:, None])
+                dq[b, h, r0:r1] = scale * (dS @ k[b, h])
+                dk[b, h] += scale * (dS.T @ q[b, h, r0:r1])
+                dv[b, h] += P.T @ dO
+                delta[b, h, r0:r1] = dl
+    return dq, dk, dv, delta
+
+
+def attention_backward_rows(q, k, v, dout, rows, scale=None):
+    """``attention_backward``'s dq and delta for the query rows ``rows`` only
+    (a query row's gradient depends on that row alone)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    q = np.asarray(q)
+    kz = np.asarray(k)
+    dq, _, _, delta = attention_backward(q[:, :, rows], kz, v, np.asarray(dout)[:, :, rows], scale)
+    return dq, delta
+
+
+def attention_backward_keys(q, k, v, dout, keys, scale=None):
+    """``attention_backward``'s dk and dv for the key rows ``keys`` only.
+
+    A key's gradients sum over every query row, each needing that row's LSE
+    and delta, so those are computed for all rows first (with ``attention``);
+    then for the chosen keys: P_ij = exp(scale q_i.k_j - LSE_i), dP_ij =
+    dO_i.v_j, dS_ij = P_ij (dP_ij - delta_i), dk_j = scale sum_i dS_ij q_i,
+    dv_j = sum_i P_ij dO_i.
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    keys = np.asarray(keys, dtype=np.int64)
+    scale = default_scale(q.shape[-1]) if scale is None else float(scale)
+    O, L = attention(q, k, v, scale)
+    delta = (dout * O).sum(axis=-1)
+    B, H = q.shape[:2]
+    dk = np.empty((B, H, len(keys), k.shape[-1]))
+    dv = np.empty((B, H, len(keys), v.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            S = scale * (q[b, h] @ k[b, h, keys].T)           # [Nq, nkeys]
+            P = np.exp(S - L[b, h][:, None])
+            dP = dout[b, h] @ v[b, h, keys].T
+            dS = P * (dP - delta[b, h][:, None])
+            dk[b, h] = scale * (dS.T @ q[b, h])
+            dv[b, h] = P.T @ dout[b, h]
+    return dk, dv
+
+
+# --------------------------------------------------------------------------
 # Ring share (handbook, Ring paragraph: attention over each arriving K/V block,
 # merged by log-sum-exp; pull request, "Ring kernel selection": the block
 # kernel returns its LSE so the merge is exact).
