@@ -14,6 +14,10 @@ The fused leg runs the same step as four dit_attn_fwd_ulysses calls that
 read the token shards and write the token-shard output directly, with no
 exchange buffers; it is reported under "legs" beside the unfused step time.
 
+The backward leg times dit_attn_bwd (dQ, dK, dV from the forward's O and
+LSE) on one head group; its TFLOP/s counts the five products of the
+backward, 10*B*H*N^2*D.
+
 The ring leg (K/V in 4 blocks of 8192: four dit_attn_fwd_block calls with
 float32 partials, then dit_attn_merge, B1 H40 N32768 D128) is timed after the
 steps and reported under "legs"; it is not part of `value`.
@@ -213,6 +217,21 @@ def main():
     legs.update({"fused_step_ms": fused_ms,
                  "fused_step_TFLOPs": P * flops_launch / (fused_ms * 1e-3) / 1e12,
                  "unfused_step_ms": ms_per_step})
+
+    # backward leg: dit_attn_bwd on the same head group (the forward's O and
+    # LSE, a seeded dO); algorithmic FLOPs of the five products 10*B*H*N^2*D.
+    print("[bench] backward leg", file=sys.stderr, flush=True)
+    dout = torch.empty_like(outs[0]).normal_(generator=torch.Generator(device=dev).manual_seed(5))
+    g_dq = torch.empty((B, H, N, D), device=dev, dtype=torch.float32)
+    g_dk, g_dv = torch.empty_like(g_dq), torch.empty_like(g_dq)
+    g_delta = torch.empty((B, H, N), device=dev, dtype=torch.float32)
+    bwd_ms = time_it(lambda: dta.dit_attn_bwd(groups[0][0], groups[1][0], groups[2][0], outs[0], dout,
+                                              lses[0], dq=g_dq, dk=g_dk, dv=g_dv, delta=g_delta),
+                     reps=3)
+    legs.update({"bwd_ms": bwd_ms,
+                 "bwd_TFLOPs": 2.5 * flops_launch / (bwd_ms * 1e-3) / 1e12,
+                 "fwd_plus_bwd_ms": attn_avg_ms + bwd_ms})
+    del g_dq, g_dk, g_dv, dout
 
     if not args.no_ring:
         print("[bench] ring leg", file=sys.stderr, flush=True)

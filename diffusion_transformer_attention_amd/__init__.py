@@ -21,8 +21,9 @@ LIB_PATH = os.path.join(_HERE, "libditattn.so")
 
 DIT_BF16, DIT_F32 = 0, 1
 DIT_OK, DIT_EINVAL, DIT_EUNSUPPORTED, DIT_EALIGN, DIT_ELAUNCH, DIT_ERANGE = 0, -1, -2, -3, -4, -5
-EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_ulysses", "dit_attn_merge",
-            "ulysses_seq2head", "ulysses_head2seq", "dit_strerror", "dit_abi_version")
+EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_ulysses", "dit_attn_bwd",
+            "dit_attn_merge", "ulysses_seq2head", "ulysses_head2seq", "dit_strerror",
+            "dit_abi_version")
 
 _lib = None
 
@@ -40,11 +41,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dit_attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P]
     lib.dit_attn_fwd_block.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, P]
     lib.dit_attn_fwd_ulysses.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, P]
+    lib.dit_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P]
     lib.dit_attn_merge.argtypes = [P, P, I, P, P, I, I, I, I, I, P]
     lib.ulysses_seq2head.argtypes = [P, P, I, I, I, I, I, I, P]
     lib.ulysses_head2seq.argtypes = [P, P, I, I, I, I, I, I, P]
-    for name in ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_ulysses", "dit_attn_merge",
-                 "ulysses_seq2head", "ulysses_head2seq", "dit_abi_version"):
+    for name in ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_ulysses", "dit_attn_bwd",
+                 "dit_attn_merge", "ulysses_seq2head", "ulysses_head2seq", "dit_abi_version"):
         getattr(lib, name).restype = ctypes.c_int
     lib.dit_strerror.argtypes = [ctypes.c_int]
     lib.dit_strerror.restype = ctypes.c_char_p
@@ -187,6 +189,42 @@ def dit_attn_fwd_ulysses(q, k, v, r, scale=None, out=None, lse=None, return_lse=
     return o, lse
 
 
+def dit_attn_bwd(q, k, v, o, dout, lse, scale=None, dq=None, dk=None, dv=None, delta=None):
+    """Attention backward: q, o, dout bf16 [B,H,Nq,128]; k, v bf16 [B,H,Nkv,128];
+    lse float32 [B,H,Nq] from the forward.
+
+    Returns (dq [B,H,Nq,D], dk, dv [B,H,Nkv,D], delta [B,H,Nq]), all float32.
+    """
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, n, 4)
+    _need(lse, "lse", 3)
+    B, H, Nq, D = q.shape
+    Nkv = k.shape[2]
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must match q")
+    if k.shape != v.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != D:
+        raise ValueError("k, v must be [B,H,Nkv,D] matching q")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype):
+        raise ValueError("q, k, v, o, dout must share dtype")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("lse must be float32 [B,H,Nq]")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    f32 = dict(device=q.device, dtype=torch.float32)
+    dq = torch.empty((B, H, Nq, D), **f32) if dq is None else dq
+    dk = torch.empty((B, H, Nkv, D), **f32) if dk is None else dk
+    dv = torch.empty((B, H, Nkv, D), **f32) if dv is None else dv
+    delta = torch.empty((B, H, Nq), **f32) if delta is None else delta
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, n, 4)
+    _need(delta, "delta", 3)
+    rc = lib.dit_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta),
+                          _ptr(dq), _ptr(dk), _ptr(dv), B, H, Nq, Nkv, D, ctypes.c_float(scale),
+                          _dtype_code(q.dtype), _dtype_code(dq.dtype), _stream())
+    _check(rc, "dit_attn_bwd")
+    return dq, dk, dv, delta
+
+
 def dit_attn_merge(o_parts, lse_parts, out_dtype=torch.bfloat16, out=None, lse=None,
                    return_lse=True):
     """Exact LSE merge: o_parts float32 [nblk,B,H,N,D], lse_parts float32 [nblk,B,H,N].
@@ -243,6 +281,7 @@ def ulysses_head2seq(groups, out=None):
     return o
 
 
-__all__ = ["dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_ulysses", "dit_attn_merge", "ulysses_seq2head",
+__all__ = ["dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_ulysses", "dit_attn_bwd",
+           "dit_attn_merge", "ulysses_seq2head",
            "ulysses_head2seq", "dit_strerror", "dit_abi_version", "load_library", "DitError",
            "LIB_PATH", "EXPORTED", "DIT_BF16", "DIT_F32"]

@@ -114,6 +114,25 @@ int dit_attn_fwd_ulysses(const void* q, const void* k, const void* v, void* o, f
                                                       static_cast<hipStream_t>(stream)));
 }
 
+int dit_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H, int Nq,
+                 int Nkv, int D, float scale, int dtype, int grad_dtype, void* stream) {
+  if (B < 0 || H < 0 || Nq < 0 || Nkv < 0 || D <= 0) return DIT_EINVAL;
+  if (!(isfinite(scale) && scale > 0.0f)) return DIT_EINVAL;
+  if (dtype != DIT_BF16 || grad_dtype != DIT_F32) return DIT_EUNSUPPORTED;
+  if (D != 128) return DIT_EUNSUPPORTED;
+  if (!size_ok(B, H, Nq, D) || !size_ok(B, H, Nkv, D)) return DIT_ERANGE;
+  if (B == 0 || H == 0) return DIT_OK;
+  if (Nq == 0 || Nkv == 0) return DIT_EINVAL;
+  if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return DIT_EINVAL;
+  for (const void* p : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned(p, 16)) return DIT_EALIGN;
+  if (!aligned(lse, 4) || !aligned(delta, 4)) return DIT_EALIGN;
+  return map_launch(ditattn::launch_attn_bwd_bf16(
+      q, k, v, o, dout, lse, delta, static_cast<float*>(dq), static_cast<float*>(dk),
+      static_cast<float*>(dv), B, H, Nq, Nkv, scale, static_cast<hipStream_t>(stream)));
+}
+
 int ulysses_seq2head(const void* in, void* out, int P, int B, int H, int N, int D, int elem_bytes,
                      void* stream) {
   return permute_common(in, out, P, B, H, N, D, elem_bytes, false, stream);

@@ -1,0 +1,516 @@
+// bf16 attention backward on the CDNA4 matrix cores: dQ, dK, dV from q, k, v,
+// the forward's O and LSE, and the output gradient dO.
+//
+// What is computed (the chain rule of the forward definition; the pages'
+// "Feat: USP sequence parallelism (Ulysses x Ring)" pull request, "Ring kernel
+// selection": ring kernels pair with a real backward kernel; Validation:
+// dQ/dK/dV against a full-sequence reference, deterministic double runs):
+//   P_ij    = exp(scale q_i.k_j - LSE_i)
+//   delta_i = sum_d dO_id O_id
+//   dS_ij   = P_ij (dO_i.v_j - delta_i)
+//   dV_j    = sum_i P_ij dO_i
+//   dK_j    = scale sum_i dS_ij q_i
+//   dQ_i    = scale sum_j dS_ij k_j
+// With the merged LSE and the final O of a ring, a call on one K/V block gives
+// that block's dK, dV and its share of dQ.
+//
+// Three kernels, each writing every output element once (no atomics, so the
+// results are bitwise repeatable):
+//  * delta_kernel: delta = rowsum(dO * O) in float32;
+//  * dkdv_kernel: a workgroup of 8 waves owns 128 keys of one (b, h), 16 per
+//    wave, with its K and V rows in registers; it streams the query rows in
+//    64-row LDS tiles (Q, dO, LSE, delta; two stages, loaded with
+//    buffer_load ... lds) and per 32-query step computes, with
+//    v_mfma_f32_16x16x32_bf16,
+//      S  = Q K^T and dP = dO V^T  (A = Q / dO rows from LDS, B = K / V),
+//      P, dS per element in float32,
+//      dV^T += dO^T P and dK^T += Q^T dS  (A = transposing LDS reads of the
+//      same tiles, B = P / dS packed to bf16 from the lane's own S layout);
+//  * dq_kernel: the forward's arrangement: 8 waves x 32 query rows with Q and
+//    dO in registers, K and V streamed in 64-key LDS tiles; per 32-key step
+//      S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T.
+// The tiles' 16-byte chunks are XOR-swizzled with 2(row & 7) + ((row >> 3) & 1)
+// so both read patterns are bank-conflict-free: ds_read_b128 of 16 rows at
+// one column, and ds_read_b64_tr_b16 of 8 rows x 2 chunks per 32 lanes.
+// Head dimension 128 only.
+#include <math.h>
+
+#include "launch.h"
+
+namespace ditattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_t;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) float lds_f32;
+
+constexpr int D = 128;
+constexpr int ROWB = 2 * D;        // bytes per row
+constexpr int CPR = D / 8;         // 16-byte chunks per row
+constexpr int KS = D / 32;         // 32-wide k-steps over channels
+constexpr int DB = D / 16;         // 16-channel blocks
+constexpr int TR = 64;             // rows per LDS tile
+constexpr int TILE = TR * ROWB;    // 16 KB
+constexpr int PIECES = TILE / 1024;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int KEYS_PER_WG = 16 * kWaves;     // dkdv_kernel
+constexpr int QUERIES_PER_WG = 32 * kWaves;  // dq_kernel
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int swz(int row) { return 2 * (row & 7) + ((row >> 3) & 1); }
+
+__device__ __forceinline__ int remap_xcd(int i, int total) {
+  const int x = i & 7, j = i >> 3;
+  const int q = total >> 3, r = total & 7;
+  return x * q + (x < r ? x : r) + j;
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Loads into LDS are counted by vmcnt: wait for them (gfx9 s_waitcnt
+// encoding: vmcnt 0, expcnt 7, lgkmcnt 15) before the barrier that publishes
+// the tile.
+__device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+}
+
+// Stage rows [r0, r0 + 64) of a [rows, D] bf16 matrix into a swizzled LDS
+// tile: LDS slot pc of row r holds chunk pc ^ swz(r).  The descriptor ends at
+// row nrows, so rows past the end arrive as zeros.
+__device__ __forceinline__ void stage_rows(const __bf16* G, int r0, int nrows, lds_t* buf,
+                                           int wave, const int* voff) {
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(G + (int64_t)r0 * D), (short)0, (nrows - r0) * ROWB, 0x00020000);
+#pragma unroll
+  for (int n = 0; n < PIECES / kWaves; ++n)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(buf + (n * kWaves + wave) * 1024), 16, voff[n],
+        0, 0, 0);
+}
+
+// Stage 64 floats (rows [r0, r0 + 64) of a row vector) into LDS, lane l -> row r0 + l.
+__device__ __forceinline__ void stage_vec(const float* G, int r0, int nrows, lds_f32* buf, int lane) {
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(G + r0), (short)0, (nrows - r0) * 4, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)buf, 4,
+                                           4 * lane, 0, 0, 0);
+}
+
+__device__ __forceinline__ void piece_offsets(int* voff, int wave, int lane) {
+#pragma unroll
+  for (int n = 0; n < PIECES / kWaves; ++n) {
+    const int p = (n * kWaves + wave) * 64 + lane;
+    const int row = p / CPR, pc = p % CPR;
+    voff[n] = row * ROWB + ((pc ^ swz(row)) << 4);
+  }
+}
+
+// Byte offset, within a 16-row block, of the A-operand fragment of k-step ks
+// for a row-major tile: lane (c16, g) reads row c16, chunk 4ks + g.
+__device__ __forceinline__ int a_off(int c16, int g, int ks) {
+  return c16 * ROWB + (((4 * ks + g) ^ swz(c16)) << 4);
+}
+
+// Transposing read base: lane t of 16-lane group g reads row 4g + t/4,
+// channels 16db + 4(t%4) .. +3 (the second read is 16 rows further, same
+// swizzle).  The channel block only flips bits 5-7 of the in-row offset:
+// block db is at trb ^ (32 db).
+__device__ __forceinline__ int tr_base(int lane) {
+  const int t = lane & 15, g = lane >> 4;
+  const int r = 4 * g + (t >> 2);
+  const int a = (t & 3) >> 1;
+  const int b = (r >> 3) & 1;
+  return r * ROWB + 32 * (r & 7) + 16 * (a ^ b) + 8 * (t & 1);
+}
+
+__device__ __forceinline__ bf16x8 tr_frag(const lds_t* base) {
+  const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)base));
+  const bf16x4 hi = __builtin_bit_cast(
+      bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 16 * ROWB)));
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// ---------------------------------------------------------------- delta
+// One 16-lane group per row: lane i holds channels 8i .. 8i+7.
+__global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ O,
+                                                    const __bf16* __restrict__ dO,
+                                                    float* __restrict__ delta, int64_t rows) {
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int i = threadIdx.x & 15;
+  float s = 0.f;
+  if (row < rows) {
+    const bf16x8 o = *reinterpret_cast<const bf16x8*>(O + row * D + 8 * i);
+    const bf16x8 d = *reinterpret_cast<const bf16x8*>(dO + row * D + 8 * i);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s = fmaf((float)o[j], (float)d[j], s);
+  }
+  s += __shfl_xor(s, 8, 16);
+  s += __shfl_xor(s, 4, 16);
+  s += __shfl_xor(s, 2, 16);
+  s += __shfl_xor(s, 1, 16);
+  if (row < rows && i == 0) delta[row] = s;
+}
+
+// ---------------------------------------------------------------- dK, dV
+struct KVCtx {
+  bf16x8 k[KS], v[KS];  // B operands: lane holds key c16, channels 32ks + 8g .. +7
+  f32x4 dk[DB], dv[DB]; // dK^T, dV^T blocks: lane holds channels 16db + 4g + r of key c16
+  int aoff[KS];
+  int trb;
+  int g, lane;
+};
+
+// One 32-query step of the dK/dV accumulation from the stage (q, o, l, d);
+// queries q0 .. q0+31 of the tile at rows [32 st, 32 st + 32).
+template <bool MASK>
+__device__ __forceinline__ void dkdv_step(KVCtx& x, const lds_t* qt, const lds_t* ot,
+                                          const lds_f32* lt, const lds_f32* dt, int st, int q0,
+                                          int Nq, float c) {
+  const lds_t* qs = qt + 32 * st * ROWB;
+  const lds_t* os = ot + 32 * st * ROWB;
+  f32x4 S[2], dP[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    S[qb] = f32x4{};
+    dP[qb] = f32x4{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 aq = *reinterpret_cast<const lds_bf16x8*>(qs + 16 * qb * ROWB + x.aoff[ks]);
+      const bf16x8 ao = *reinterpret_cast<const lds_bf16x8*>(os + 16 * qb * ROWB + x.aoff[ks]);
+      S[qb] = mfma16(aq, x.k[ks], S[qb]);
+      dP[qb] = mfma16(ao, x.v[ks], dP[qb]);
+    }
+  }
+  // S[qb] holds queries 32st + 16qb + 4g + r (rows) of key c16 (column).
+  bf16x8 pp, dsp;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qi = 32 * st + 16 * qb + 4 * x.g;
+    const f32x4 lse = *reinterpret_cast<const lds_f32x4*>(lt + qi);
+    const f32x4 del = *reinterpret_cast<const lds_f32x4*>(dt + qi);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float p = __builtin_amdgcn_exp2f(fmaf(S[qb][r], c, -lse[r] * kLog2e));
+      if (MASK && q0 + qi + r >= Nq) p = 0.f;
+      const float ds = p * (dP[qb][r] - del[r]);
+      pp[4 * qb + r] = (__bf16)p;
+      dsp[4 * qb + r] = (__bf16)ds;
+    }
+  }
+  // B operands: k index 8g + j <-> query 4g + j (j < 4), 16 + 4g + j - 4 (j >= 4).
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const bf16x8 aot = tr_frag(os + (x.trb ^ (32 * db)));
+    const bf16x8 aqt = tr_frag(qs + (x.trb ^ (32 * db)));
+    x.dv[db] = mfma16(aot, pp, x.dv[db]);
+    x.dk[db] = mfma16(aqt, dsp, x.dk[db]);
+  }
+}
+
+struct QStages {
+  lds_t *q0, *q1, *o0, *o1;
+  lds_f32 *l0, *l1, *d0, *d1;
+};
+
+// Query tile t from stage ST (0/1); loads tile t+1 into the other stage.
+template <int ST, bool MASK>
+__device__ __forceinline__ void dkdv_tile(KVCtx& x, const QStages& s, int t, int ntiles,
+                                          const __bf16* Qb, const __bf16* dOb, const float* Lb,
+                                          const float* Db, int Nq, int wave, const int* voff,
+                                          float c) {
+  if (t + 1 < ntiles) {
+    const int r1 = (t + 1) * TR;
+    stage_rows(Qb, r1, Nq, ST ? s.q0 : s.q1, wave, voff);
+    stage_rows(dOb, r1, Nq, ST ? s.o0 : s.o1, wave, voff);
+    if (wave == 0) stage_vec(Lb, r1, Nq, ST ? s.l0 : s.l1, x.lane);
+    if (wave == 1) stage_vec(Db, r1, Nq, ST ? s.d0 : s.d1, x.lane);
+  }
+  const lds_t* qt = ST ? s.q1 : s.q0;
+  const lds_t* ot = ST ? s.o1 : s.o0;
+  const lds_f32* lt = ST ? s.l1 : s.l0;
+  const lds_f32* dt = ST ? s.d1 : s.d0;
+  dkdv_step<MASK>(x, qt, ot, lt, dt, 0, t * TR, Nq, c);
+  dkdv_step<MASK>(x, qt, ot, lt, dt, 1, t * TR, Nq, c);
+  tile_barrier();  // tile t+1 landed; every wave is done with tile t
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                 const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                 const float* __restrict__ LSE, const float* __restrict__ Dl,
+                 float* __restrict__ dK, float* __restrict__ dV, int Nq, int Nkv, int n_ktiles,
+                 int total, float c, float scale) {
+  __shared__ __attribute__((aligned(1024))) char q0s[TILE];
+  __shared__ __attribute__((aligned(1024))) char q1s[TILE];
+  __shared__ __attribute__((aligned(1024))) char o0s[TILE];
+  __shared__ __attribute__((aligned(1024))) char o1s[TILE];
+  __shared__ __attribute__((aligned(256))) float l0s[TR];
+  __shared__ __attribute__((aligned(256))) float l1s[TR];
+  __shared__ __attribute__((aligned(256))) float d0s[TR];
+  __shared__ __attribute__((aligned(256))) float d1s[TR];
+
+  const int tile = remap_xcd(blockIdx.x, total);
+  const int bh = tile / n_ktiles;
+  const int kt = tile - bh * n_ktiles;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c16 = lane & 15, g = lane >> 4;
+  const __bf16* Qb = Q + (int64_t)bh * Nq * D;
+  const __bf16* dOb = dO + (int64_t)bh * Nq * D;
+  const float* Lb = LSE + (int64_t)bh * Nq;
+  const float* Db = Dl + (int64_t)bh * Nq;
+
+  KVCtx x;
+  x.g = g;
+  x.lane = lane;
+  const int key = kt * KEYS_PER_WG + wave * 16 + c16;
+  const int krow = min(key, Nkv - 1);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    x.k[ks] = *reinterpret_cast<const bf16x8*>(K + ((int64_t)bh * Nkv + krow) * D + 32 * ks + 8 * g);
+    x.v[ks] = *reinterpret_cast<const bf16x8*>(V + ((int64_t)bh * Nkv + krow) * D + 32 * ks + 8 * g);
+    x.aoff[ks] = a_off(c16, g, ks);
+  }
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    x.dk[db] = f32x4{};
+    x.dv[db] = f32x4{};
+  }
+  x.trb = tr_base(lane);
+  int voff[PIECES / kWaves];
+  piece_offsets(voff, wave, lane);
+
+  QStages s{(lds_t*)q0s, (lds_t*)q1s, (lds_t*)o0s, (lds_t*)o1s,
+            (lds_f32*)l0s, (lds_f32*)l1s, (lds_f32*)d0s, (lds_f32*)d1s};
+  const int ntiles = (Nq + TR - 1) / TR;
+  stage_rows(Qb, 0, Nq, s.q0, wave, voff);
+  stage_rows(dOb, 0, Nq, s.o0, wave, voff);
+  if (wave == 0) stage_vec(Lb, 0, Nq, s.l0, lane);
+  if (wave == 1) stage_vec(Db, 0, Nq, s.d0, lane);
+  tile_barrier();
+  const bool partial = (Nq % TR) != 0;
+  const int nfull = partial ? ntiles - 1 : ntiles;
+  int t = 0;
+  for (; t + 2 <= nfull; t += 2) {
+    dkdv_tile<0, false>(x, s, t, ntiles, Qb, dOb, Lb, Db, Nq, wave, voff, c);
+    dkdv_tile<1, false>(x, s, t + 1, ntiles, Qb, dOb, Lb, Db, Nq, wave, voff, c);
+  }
+  if (t < nfull) {
+    dkdv_tile<0, false>(x, s, t, ntiles, Qb, dOb, Lb, Db, Nq, wave, voff, c);
+    ++t;
+  }
+  if (partial) {
+    if ((t & 1) == 0)
+      dkdv_tile<0, true>(x, s, t, ntiles, Qb, dOb, Lb, Db, Nq, wave, voff, c);
+    else
+      dkdv_tile<1, true>(x, s, t, ntiles, Qb, dOb, Lb, Db, Nq, wave, voff, c);
+  }
+
+  if (key < Nkv) {
+    const int64_t base = ((int64_t)bh * Nkv + key) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      *reinterpret_cast<f32x4*>(dK + base + 16 * db + 4 * g) = x.dk[db] * scale;
+      *reinterpret_cast<f32x4*>(dV + base + 16 * db + 4 * g) = x.dv[db];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+struct QCtx {
+  bf16x8 q[2][KS], o[2][KS];  // B operands: lane holds query c16 of block qb, channels 32ks + 8g ..
+  f32x4 dq[2][DB];            // dQ^T blocks: lane holds channels 16db + 4g + r of its query
+  float lse2[2], del[2];
+  int aoff[KS];
+  int trb;
+  int g;
+};
+
+// One 32-key step from the stage (kt, vt), keys k0 .. k0+31 at rows [32 st, 32 st + 32).
+template <bool MASK>
+__device__ __forceinline__ void dq_step(QCtx& x, const lds_t* kt, const lds_t* vt, int st, int k0,
+                                        int Nkv, float c) {
+  const lds_t* ks_ = kt + 32 * st * ROWB;
+  const lds_t* vs_ = vt + 32 * st * ROWB;
+  f32x4 S[2][2], dP[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      S[kb][qb] = f32x4{};
+      dP[kb][qb] = f32x4{};
+    }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 ak = *reinterpret_cast<const lds_bf16x8*>(ks_ + 16 * kb * ROWB + x.aoff[ks]);
+      const bf16x8 av = *reinterpret_cast<const lds_bf16x8*>(vs_ + 16 * kb * ROWB + x.aoff[ks]);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        S[kb][qb] = mfma16(ak, x.q[qb][ks], S[kb][qb]);
+        dP[kb][qb] = mfma16(av, x.o[qb][ks], dP[kb][qb]);
+      }
+    }
+  // S[kb][qb] holds keys 16kb + 4g + r (rows) for the lane's query of block qb.
+  bf16x8 dsp[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float p = __builtin_amdgcn_exp2f(fmaf(S[kb][qb][r], c, -x.lse2[qb]));
+        if (MASK && k0 + 32 * st + 16 * kb + 4 * x.g + r >= Nkv) p = 0.f;
+        dsp[qb][4 * kb + r] = (__bf16)(p * (dP[kb][qb][r] - x.del[qb]));
+      }
+  // dQ^T += K^T dS^T; k index 8g + j <-> key 4g + j (j < 4), 16 + 4g + j - 4 (j >= 4).
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const bf16x8 akt = tr_frag(ks_ + (x.trb ^ (32 * db)));
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) x.dq[qb][db] = mfma16(akt, dsp[qb], x.dq[qb][db]);
+  }
+}
+
+struct KStages {
+  lds_t *k0, *k1, *v0, *v1;
+};
+
+template <int ST, bool MASK>
+__device__ __forceinline__ void dq_tile(QCtx& x, const KStages& s, int t, int ntiles,
+                                        const __bf16* Kb, const __bf16* Vb, int Nkv, int wave,
+                                        const int* voff, float c) {
+  if (t + 1 < ntiles) {
+    stage_rows(Kb, (t + 1) * TR, Nkv, ST ? s.k0 : s.k1, wave, voff);
+    stage_rows(Vb, (t + 1) * TR, Nkv, ST ? s.v0 : s.v1, wave, voff);
+  }
+  const lds_t* kt = ST ? s.k1 : s.k0;
+  const lds_t* vt = ST ? s.v1 : s.v0;
+  dq_step<MASK>(x, kt, vt, 0, t * TR, Nkv, c);
+  dq_step<MASK>(x, kt, vt, 1, t * TR, Nkv, c);
+  tile_barrier();
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+               const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+               const float* __restrict__ LSE, const float* __restrict__ Dl,
+               float* __restrict__ dQ, int Nq, int Nkv, int n_qtiles, int total, float c,
+               float scale) {
+  __shared__ __attribute__((aligned(1024))) char k0s[TILE];
+  __shared__ __attribute__((aligned(1024))) char k1s[TILE];
+  __shared__ __attribute__((aligned(1024))) char v0s[TILE];
+  __shared__ __attribute__((aligned(1024))) char v1s[TILE];
+
+  const int tile = remap_xcd(blockIdx.x, total);
+  const int bh = tile / n_qtiles;
+  const int qt = tile - bh * n_qtiles;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c16 = lane & 15, g = lane >> 4;
+  const __bf16* Kb = K + (int64_t)bh * Nkv * D;
+  const __bf16* Vb = V + (int64_t)bh * Nkv * D;
+
+  QCtx x;
+  x.g = g;
+  const int qrow0 = qt * QUERIES_PER_WG + wave * 32 + c16;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = min(qrow0 + 16 * qb, Nq - 1);
+    const int64_t rb = ((int64_t)bh * Nq + row) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      x.q[qb][ks] = *reinterpret_cast<const bf16x8*>(Q + rb + 32 * ks + 8 * g);
+      x.o[qb][ks] = *reinterpret_cast<const bf16x8*>(dO + rb + 32 * ks + 8 * g);
+    }
+    x.lse2[qb] = LSE[(int64_t)bh * Nq + row] * kLog2e;
+    x.del[qb] = Dl[(int64_t)bh * Nq + row];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) x.dq[qb][db] = f32x4{};
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) x.aoff[ks] = a_off(c16, g, ks);
+  x.trb = tr_base(lane);
+  int voff[PIECES / kWaves];
+  piece_offsets(voff, wave, lane);
+
+  KStages s{(lds_t*)k0s, (lds_t*)k1s, (lds_t*)v0s, (lds_t*)v1s};
+  const int ntiles = (Nkv + TR - 1) / TR;
+  stage_rows(Kb, 0, Nkv, s.k0, wave, voff);
+  stage_rows(Vb, 0, Nkv, s.v0, wave, voff);
+  tile_barrier();
+  const bool partial = (Nkv % TR) != 0;
+  const int nfull = partial ? ntiles - 1 : ntiles;
+  int t = 0;
+  for (; t + 2 <= nfull; t += 2) {
+    dq_tile<0, false>(x, s, t, ntiles, Kb, Vb, Nkv, wave, voff, c);
+    dq_tile<1, false>(x, s, t + 1, ntiles, Kb, Vb, Nkv, wave, voff, c);
+  }
+  if (t < nfull) {
+    dq_tile<0, false>(x, s, t, ntiles, Kb, Vb, Nkv, wave, voff, c);
+    ++t;
+  }
+  if (partial) {
+    if ((t & 1) == 0)
+      dq_tile<0, true>(x, s, t, ntiles, Kb, Vb, Nkv, wave, voff, c);
+    else
+      dq_tile<1, true>(x, s, t, ntiles, Kb, Vb, Nkv, wave, voff, c);
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = qrow0 + 16 * qb;
+    if (row < Nq) {
+      const int64_t base = ((int64_t)bh * Nq + row) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<f32x4*>(dQ + base + 16 * db + 4 * g) = x.dq[qb][db] * scale;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                                const void* dout, const float* lse, float* delta, float* dq,
+                                float* dk, float* dv, int B, int H, int Nq, int Nkv, float scale,
+                                hipStream_t stream) {
+  const int64_t rows = (int64_t)B * H * Nq;
+  const int64_t dgrid = (rows + 15) / 16;
+  const int n_ktiles = (Nkv + KEYS_PER_WG - 1) / KEYS_PER_WG;
+  const int n_qtiles = (Nq + QUERIES_PER_WG - 1) / QUERIES_PER_WG;
+  const int64_t kv_total = (int64_t)B * H * n_ktiles, q_total = (int64_t)B * H * n_qtiles;
+  if (dgrid > 0x7fffffff || kv_total > 0x7fffffff || q_total > 0x7fffffff)
+    return hipErrorInvalidValue;
+  const float c = scale * kLog2e;
+  const __bf16* Qp = static_cast<const __bf16*>(q);
+  const __bf16* Kp = static_cast<const __bf16*>(k);
+  const __bf16* Vp = static_cast<const __bf16*>(v);
+  const __bf16* Op = static_cast<const __bf16*>(o);
+  const __bf16* dOp = static_cast<const __bf16*>(dout);
+  hipLaunchKernelGGL(delta_kernel, dim3((unsigned)dgrid), dim3(256), 0, stream, Op, dOp, delta, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dkdv_kernel, dim3((unsigned)kv_total), dim3(kThreads), 0, stream, Qp, Kp, Vp,
+                     dOp, lse, (const float*)delta, dk, dv, Nq, Nkv, n_ktiles, (int)kv_total, c,
+                     scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dq_kernel, dim3((unsigned)q_total), dim3(kThreads), 0, stream, Qp, Kp, Vp, dOp,
+                     lse, (const float*)delta, dq, Nq, Nkv, n_qtiles, (int)q_total, c, scale);
+  return hipGetLastError();
+}
+
+}  // namespace ditattn

@@ -18,6 +18,13 @@ hipError_t launch_attn_bf16_ulysses(const void* q, const void* k, const void* v,
                                     float* lse, int P, int r, int B, int H, int N, int D,
                                     float scale, hipStream_t stream);
 
+// Backward, bf16 q/k/v/o/dout (head dim 128), float32 lse in, delta out
+// ([B,H,Nq]), float32 dq/dk/dv.
+hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                                const void* dout, const float* lse, float* delta, float* dq,
+                                float* dk, float* dv, int B, int H, int Nq, int Nkv, float scale,
+                                hipStream_t stream);
+
 // float32 q/k/v/o.  lse may be null.
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                            int B, int H, int Nq, int Nkv, int D, float scale, hipStream_t stream);

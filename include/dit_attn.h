@@ -93,6 +93,34 @@ int dit_attn_fwd_block(const void* q, const void* k, const void* v, void* o, flo
                        int in_dtype, int o_dtype, void* stream);
 
 /*
+ * Attention backward: the gradients of sum(dout * O) for O = attention(q, k, v)
+ * ([PR] "Ring kernel selection": the ring kernels pair with a real backward
+ * kernel and return the LSE it needs; Validation: dQ/dK/dV compared against
+ * a full-sequence reference, and bitwise repeatable in deterministic mode).
+ * The chain rule of dit_attn_fwd's definition, with P recomputed from the
+ * forward's LSE:
+ *
+ *   P_ij     = exp(scale * q_i . k_j - LSE_i)
+ *   delta_i  = sum_d dout_id * o_id
+ *   dS_ij    = P_ij * (dout_i . v_j - delta_i)
+ *   dv_j = sum_i P_ij dout_i,  dk_j = scale sum_i dS_ij q_i,  dq_i = scale sum_j dS_ij k_j
+ *
+ *   q, o, dout : bf16 [B,H,Nq,D];  k, v : bf16 [B,H,Nkv,D];  D must be 128
+ *   lse        : float32 [B,H,Nq], the forward's LSE (required)
+ *   delta      : float32 [B,H,Nq], written (rowsum(dout * o)); caller-owned
+ *   dq         : float32 [B,H,Nq,D];  dk, dv : float32 [B,H,Nkv,D]  (written)
+ *   dtype must be DIT_BF16 and grad_dtype DIT_F32.
+ * For one Ring K/V block, pass the merged o and lse of the full row: dk, dv
+ * are that block's gradients and dq its share (sum the shares over blocks).
+ * Every output element is written once with a fixed summation order, so two
+ * calls give bit-identical results.  Nq and Nkv must be >= 1 (DIT_EINVAL),
+ * unless B or H is 0 (no-op).
+ */
+int dit_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H,
+                 int Nq, int Nkv, int D, float scale, int dtype, int grad_dtype, void* stream);
+
+/*
  * Exact log-sum-exp merge of nblk partials over disjoint key blocks ([HB]
  * Ring paragraph: results of each K/V block merged with a log-sum-exp).
  *

@@ -107,6 +107,25 @@ def test_fused_ulysses_validation(lib):
     assert u(N=0) == dta.DIT_OK              # nothing to compute
 
 
+def test_backward_validation(lib):
+    def b(B=1, Nq=64, Nkv=64, D=128, dt=0, gdt=1, q=A, lse=A, delta=A, dq=A, scale=0.125):
+        return lib.dit_attn_bwd(q, A, A, A, A, lse, delta, dq, A, A, B, 2, Nq, Nkv, D,
+                                ctypes.c_float(scale), dt, gdt, S)
+    assert b(D=64) == dta.DIT_EUNSUPPORTED     # head dim 128 only
+    assert b(dt=1) == dta.DIT_EUNSUPPORTED     # bf16 inputs only
+    assert b(gdt=0) == dta.DIT_EUNSUPPORTED    # float32 gradients only
+    assert b(Nq=0) == dta.DIT_EINVAL           # gradients of an empty problem are not a no-op
+    assert b(Nkv=0) == dta.DIT_EINVAL
+    assert b(B=0) == dta.DIT_OK
+    assert b(q=NULL) == dta.DIT_EINVAL
+    assert b(lse=NULL) == dta.DIT_EINVAL
+    assert b(delta=NULL) == dta.DIT_EINVAL
+    assert b(dq=MIS) == dta.DIT_EALIGN
+    assert b(lse=V(0x10002)) == dta.DIT_EALIGN
+    assert b(scale=float("nan")) == dta.DIT_EINVAL
+    assert b(Nq=-1) == dta.DIT_EINVAL
+
+
 @pytest.mark.parametrize("fn", ["ulysses_seq2head", "ulysses_head2seq"])
 def test_permute_validation(lib, fn):
     f = getattr(lib, fn)

@@ -1,0 +1,137 @@
+"""GPU parity of the attention backward (dit_attn_bwd) against the fp64 oracle.
+
+The GPU backward takes the GPU forward's bf16 O and float32 LSE, as a
+training step would; the oracle differentiates the exact definition on the
+same bf16 input values.  Tolerances (per gradient tensor, over the whole
+tensor or the sampled rows): relative RMS error <= 1e-2 -- the pages' op-level
+band for bf16 gradients is 8e-3 relative -- and max-abs error <= 3e-2 of the
+tensor's largest reference magnitude; delta to 1e-2 of its RMS.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+import diffusion_transformer_attention_amd as dta
+from _helpers import bits_to_torch_bf16, to_f64
+
+pytestmark = pytest.mark.gpu
+
+GRAD_REL_RMS = 1e-2
+GRAD_MAX_ABS_REL = 3e-2
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+def f64(bits):
+    return datagen.bf16_to_f32(bits).astype(np.float64)
+
+
+def _check_grad(got, ref, name, what):
+    err = got - ref
+    rr = float(np.linalg.norm(err.ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300))
+    ma = float(np.abs(err).max() / max(np.abs(ref).max(), 1e-300))
+    say(f"{what} {name}: rel-RMS {rr:.2e}  max-abs/max|ref| {ma:.2e}")
+    assert rr <= GRAD_REL_RMS, f"{what} {name} rel-RMS {rr:.3e}"
+    assert ma <= GRAD_MAX_ABS_REL, f"{what} {name} max-abs {ma:.3e}"
+
+
+def _inputs(B, H, Nq, Nkv, seed):
+    qb, kb, vb = datagen.small_bf16(B, H, Nq, 128, seed=seed, Nkv=Nkv)
+    dob = datagen.small_bf16(B, H, Nq, 128, seed=seed + 1)[0]
+    return qb, kb, vb, dob
+
+
+def _gpu_fwd_bwd(qb, kb, vb, dob, scale=None):
+    tq, tk, tv, tdo = (bits_to_torch_bf16(x) for x in (qb, kb, vb, dob))
+    O, L = dta.dit_attn_fwd_block(tq, tk, tv, scale=scale, out_dtype=torch.bfloat16)
+    return (tq, tk, tv, tdo, O, L), dta.dit_attn_bwd(tq, tk, tv, O, tdo, L, scale=scale)
+
+
+@pytest.mark.parametrize("B,H,Nq,Nkv", [
+    (1, 2, 128, 128),
+    (2, 3, 300, 200),      # ragged query and key tiles
+    (1, 1, 1, 1),          # one token
+    (1, 2, 64, 1000),
+    (1, 1, 257, 129),
+    (1, 2, 1000, 1000),
+])
+def test_backward_small_full_compare(B, H, Nq, Nkv):
+    say("bwd", B, H, Nq, Nkv)
+    qb, kb, vb, dob = _inputs(B, H, Nq, Nkv, seed=Nq * 5 + Nkv)
+    _, (dq, dk, dv, delta) = _gpu_fwd_bwd(qb, kb, vb, dob)
+    rq, rk, rv, rd = oracle.attention_backward(f64(qb), f64(kb), f64(vb), f64(dob))
+    what = f"B{B} H{H} Nq{Nq} Nkv{Nkv}"
+    for got, ref, n in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+        _check_grad(to_f64(got), ref, n, what)
+    dd = to_f64(delta) - rd
+    assert np.linalg.norm(dd) <= 1e-2 * max(np.linalg.norm(rd), 1e-12)
+
+
+def test_backward_explicit_scale_and_large_scores():
+    say("bwd explicit scale, wide score range")
+    qb, kb, vb, dob = _inputs(1, 2, 200, 300, seed=77)
+    q3 = datagen.bf16_bits(datagen.bf16_to_f32(qb) * 3.0)
+    _, (dq, dk, dv, _) = _gpu_fwd_bwd(q3, kb, vb, dob, scale=0.2)
+    rq, rk, rv, _ = oracle.attention_backward(f64(q3), f64(kb), f64(vb), f64(dob), 0.2)
+    for got, ref, n in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+        _check_grad(to_f64(got), ref, n, "scale 0.2, q x3")
+
+
+def test_backward_deterministic_and_per_head():
+    """Bitwise repeatable, and a head's gradients do not depend on the other
+    heads of the call (the Ulysses split computes whole heads)."""
+    say("bwd determinism / head independence")
+    qb, kb, vb, dob = _inputs(1, 4, 500, 500, seed=5)
+    (tq, tk, tv, tdo, O, L), g1 = _gpu_fwd_bwd(qb, kb, vb, dob)
+    g2 = dta.dit_attn_bwd(tq, tk, tv, O, tdo, L)
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))
+    sl = slice(1, 3)
+    sub = [t[:, sl].contiguous() for t in (tq, tk, tv, O, tdo)]
+    g3 = dta.dit_attn_bwd(*sub, L[:, sl].contiguous())
+    assert all(torch.equal(a[:, sl], b) for a, b in zip(g1, g3))
+
+
+def test_backward_ring_blocks():
+    """Per K/V block with the merged O and LSE: each block's dk, dv equal the
+    full call's rows bit for bit; the dq shares sum to the full dq."""
+    say("bwd ring blocks")
+    qb, kb, vb, dob = _inputs(1, 2, 512, 768, seed=9)
+    (tq, tk, tv, tdo, O, L), (dq, dk, dv, _) = _gpu_fwd_bwd(qb, kb, vb, dob)
+    dq_sum = torch.zeros_like(dq)
+    for i in range(3):
+        ks = slice(256 * i, 256 * (i + 1))
+        dqi, dki, dvi, _ = dta.dit_attn_bwd(tq, tk[:, :, ks].contiguous(), tv[:, :, ks].contiguous(),
+                                            O, tdo, L)
+        assert torch.equal(dki, dk[:, :, ks]) and torch.equal(dvi, dv[:, :, ks])
+        dq_sum += dqi
+    rel = (dq_sum - dq).norm() / dq.norm()
+    assert rel < 1e-5, rel
+
+
+def test_backward_image_share_full():
+    say("bwd image share B1 H24 N4096 D128, full compare")
+    qb, kb, vb = datagen.workload_inputs("image_share")
+    dob = datagen.small_bf16(1, 24, 4096, 128, seed=1001)[0]
+    _, (dq, dk, dv, _) = _gpu_fwd_bwd(qb, kb, vb, dob)
+    rq, rk, rv, _ = oracle.attention_backward(f64(qb), f64(kb), f64(vb), f64(dob))
+    for got, ref, n in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+        _check_grad(to_f64(got), ref, n, "image share")
+
+
+def test_backward_ulysses_share_sampled_rows():
+    say("bwd Ulysses share B1 H10 N32768 D128, sampled dq rows")
+    qb, kb, vb = (x[:, :10] for x in datagen.workload_inputs("ulysses_share"))
+    dob = datagen.small_bf16(1, 10, 32768, 128, seed=1002)[0]
+    _, (dq, dk, dv, delta) = _gpu_fwd_bwd(qb, kb, vb, dob)
+    rows = datagen.sample_rows(32768, 32, 1003)
+    rq, rd = oracle.attention_backward_rows(f64(qb), f64(kb), f64(vb), f64(dob), rows)
+    ri = torch.from_numpy(rows).cuda()
+    _check_grad(to_f64(dq[:, :, ri]), rq, "dq", "ulysses share sampled")
+    assert np.abs(to_f64(delta[:, :, ri]) - rd).max() <= 1e-2 * np.abs(rd).max()
+    assert torch.isfinite(dk).all() and torch.isfinite(dv).all()
