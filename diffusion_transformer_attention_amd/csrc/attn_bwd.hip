@@ -29,9 +29,10 @@
 //  * dq_kernel: the forward's arrangement: 8 waves x 32 query rows with Q and
 //    dO in registers, K and V streamed in 64-key LDS tiles; per 32-key step
 //      S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T.
-// The tiles' 16-byte chunks are XOR-swizzled with 2(row & 7) + ((row >> 3) & 1)
-// so both read patterns are bank-conflict-free: ds_read_b128 of 16 rows at
-// one column, and ds_read_b64_tr_b16 of 8 rows x 2 chunks per 32 lanes.
+// The tiles' 16-byte chunks are XOR-swizzled with 2(row & 7), the swizzle of
+// the forward kernel's V tile, so both read patterns are bank-conflict-free:
+// ds_read_b128 of 16 rows at one column, and ds_read_b64_tr_b16 of 8 rows x 2
+// chunks per 32 lanes.
 // Head dimension 128 only.
 #include <math.h>
 
@@ -65,7 +66,11 @@ constexpr int KEYS_PER_WG = 16 * kWaves;     // dkdv_kernel
 constexpr int QUERIES_PER_WG = 32 * kWaves;  // dq_kernel
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ int swz(int row) { return 2 * (row & 7) + ((row >> 3) & 1); }
+// Chunk swizzle of the LDS tiles.  With it neither the row-major fragment
+// reads (ds_read_b128) nor the transposing reads (ds_read_b64_tr_b16) of
+// tr_frag meet a bank conflict; both patterns were counted on gfx950 with
+// SQ_LDS_BANK_CONFLICT.
+__device__ __forceinline__ int swz(int row) { return 2 * (row & 7); }
 
 __device__ __forceinline__ int remap_xcd(int i, int total) {
   const int x = i & 7, j = i >> 3;
@@ -122,16 +127,16 @@ __device__ __forceinline__ int a_off(int c16, int g, int ks) {
   return c16 * ROWB + (((4 * ks + g) ^ swz(c16)) << 4);
 }
 
-// Transposing read base: lane t of 16-lane group g reads row 4g + t/4,
+// Transposing read base: lane t of 16-lane group g reads row r = 4g + t/4,
 // channels 16db + 4(t%4) .. +3 (the second read is 16 rows further, same
-// swizzle).  The channel block only flips bits 5-7 of the in-row offset:
-// block db is at trb ^ (32 db).
+// swizzle), i.e. chunk 2db + a, a = (t%4)/2.  (2db + a) ^ swz(r) =
+// 2(db ^ (r & 7)) + a, so the channel block only flips bits 5-7 of the
+// in-row offset: block db is at trb ^ (32 db).
 __device__ __forceinline__ int tr_base(int lane) {
   const int t = lane & 15, g = lane >> 4;
   const int r = 4 * g + (t >> 2);
   const int a = (t & 3) >> 1;
-  const int b = (r >> 3) & 1;
-  return r * ROWB + 32 * (r & 7) + 16 * (a ^ b) + 8 * (t & 1);
+  return r * ROWB + 32 * (r & 7) + 16 * a + 8 * (t & 1);
 }
 
 __device__ __forceinline__ bf16x8 tr_frag(const lds_t* base) {
