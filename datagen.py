@@ -142,3 +142,37 @@ def sample_rows(N, count, seed, tile=128):
     pool = np.setdiff1d(np.arange(N), np.array(forced))
     extra = rng.choice(pool, size=max(0, count - len(forced)), replace=False)
     return np.sort(np.concatenate([np.array(forced, dtype=np.int64), extra.astype(np.int64)]))
+
+
+# --------------------------------------------------------------------------
+# Joint text + image inputs.  The rotary angle schedule is the model's choice,
+# so it is an input here: pairs [0, D/4) follow the token's row on the patch
+# grid and pairs [D/4, D/2) its column, pair j of each half turning at
+# frequency base**(-j / (D/4)).  Image token n sits at (n // cols, n % cols);
+# text token t sits at (g + t, g + t) with g = max(rows, cols), on the
+# diagonal past the grid.  Tables are float32 [N, D/2] (cosine, sine).
+# --------------------------------------------------------------------------
+def _axial_tables(pos_r, pos_c, D, base):
+    quarter = D // 4
+    freq = base ** (-np.arange(quarter, dtype=np.float64) / quarter)
+    ang = np.concatenate([np.outer(pos_r, freq), np.outer(pos_c, freq)], axis=1)
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def rope_tables_image(rows, cols, D, base=10000.0):
+    n = np.arange(rows * cols, dtype=np.float64)
+    return _axial_tables(n // cols, n % cols, D, base)
+
+
+def rope_tables_text(Nt, rows, cols, D, base=10000.0):
+    p = max(rows, cols) + np.arange(Nt, dtype=np.float64)
+    return _axial_tables(p, p, D, base)
+
+
+def joint_bf16(B, Ht, Nt, H, Ni, D, seed):
+    """Text q, k, v [B,Ht,Nt,D] then image q, k, v [B,H,Ni,D], N(0,1) bf16
+    bits, drawn in that order from ``default_rng(seed)``."""
+    rng = np.random.default_rng(seed)
+    txt = [bf16_bits(rng.standard_normal((B, Ht, Nt, D), dtype=np.float32)) for _ in range(3)]
+    img = [bf16_bits(rng.standard_normal((B, H, Ni, D), dtype=np.float32)) for _ in range(3)]
+    return tuple(txt), tuple(img)

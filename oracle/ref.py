@@ -21,6 +21,10 @@ Sources (web pages; sections named, not quoted):
   kernels must return the LSE; "Limitations": no mask, dropout, causal flag
   or explicit scale under SP, head count divisible by the Ulysses degree,
   sequence length divisible by the SP degree.
+* "Parallelism Acceleration Guide" (vLLM-Omni docs), "How to parallelize a
+  new model": joint attention over concatenated text and image tokens, text
+  replicated on every sequence-parallel rank, image rotary tables cut along
+  the token axis.
 
 Readings where the pages are silent:
 * LSE is the natural log of sum_j exp(scale * q.k_j) (the scale included).
@@ -275,3 +279,51 @@ def ulysses_send_bytes_per_rank(B, H, N, D, P, elem_bytes, ntensors=3):
     """Bytes one rank sends in one seq->head exchange of ``ntensors`` tensors:
     it keeps 1/P of each [B,H,N/P,D] shard and sends the other (P-1)/P."""
     return ntensors * B * H * (N // P) * D * elem_bytes * (P - 1) // P
+
+
+# --------------------------------------------------------------------------
+# Joint text + image attention with rotary position embedding ("Parallelism
+# Acceleration Guide", vLLM-Omni docs, "How to parallelize a new model": a dual-stream
+# model attends jointly over the concatenated text and image tokens; under
+# sequence parallelism the text stays whole on every rank, and the image
+# rotary tables are cut along the token axis together with the image tokens).
+# The pages name the rotary tables but not the rotation itself; the reading
+# taken is the rotary position embedding of RoFormer in its interleaved form:
+# channels (2i, 2i+1) of a token are one pair, turned by that token's angle
+# for pair i, given as cos and sin tables [N, D/2].  Text tokens come first
+# in the joint sequence.
+# --------------------------------------------------------------------------
+def rope(x, cos, sin):
+    """Turn each channel pair (2i, 2i+1) of token n by the angle whose cosine
+    and sine are cos[n, i] and sin[n, i]:
+        y[2i]   = x[2i] cos - x[2i+1] sin
+        y[2i+1] = x[2i] sin + x[2i+1] cos
+    x: [..., N, D]; cos, sin: [N, D/2].  Returns float64 [..., N, D]."""
+    x, c, s = _f64(x), _f64(cos), _f64(sin)
+    even, odd = x[..., 0::2], x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = even * c - odd * s
+    y[..., 1::2] = even * s + odd * c
+    return y
+
+
+def joint_sequence(x_txt, x_img, cos_txt=None, sin_txt=None, cos_img=None, sin_img=None):
+    """[B,H,Nt,D] text and [B,H,Ni,D] image tokens -> [B,H,Nt+Ni,D], text
+    first, each part turned by its own rotary tables when they are given."""
+    t = _f64(x_txt) if cos_txt is None else rope(x_txt, cos_txt, sin_txt)
+    i = _f64(x_img) if cos_img is None else rope(x_img, cos_img, sin_img)
+    return np.concatenate([t, i], axis=2)
+
+
+def joint_attention(q_txt, k_txt, v_txt, q_img, k_img, v_img, cos_txt=None, sin_txt=None,
+                    cos_img=None, sin_img=None, scale=None, rows=None):
+    """Attention of every text and image query over every text and image key,
+    with RoPE on queries and keys (not values).  Returns (O, LSE) of the joint
+    sequence [B,H,Nt+Ni,...]; ``rows`` restricts the queries to those joint
+    rows."""
+    q = joint_sequence(q_txt, q_img, cos_txt, sin_txt, cos_img, sin_img)
+    k = joint_sequence(k_txt, k_img, cos_txt, sin_txt, cos_img, sin_img)
+    v = joint_sequence(v_txt, v_img)
+    if rows is not None:
+        q = q[:, :, np.asarray(rows, dtype=np.int64)]
+    return attention(q, k, v, scale)
