@@ -18,6 +18,11 @@ The backward leg times dit_attn_bwd (dQ, dK, dV from the forward's O and
 LSE) on one head group; its TFLOP/s counts the five products of the
 backward, 10*B*H*N^2*D.
 
+The joint leg times dit_attn_fwd_joint (RoPE + packing of text and image
+tokens, then attention) on 512 text + 4096 image tokens, B1 H24 D128, and the
+attention alone; the cross leg times dit_attn_fwd_block of the 10-head share's
+32768 queries over 512 text keys.
+
 The ring leg (K/V in 4 blocks of 8192: four dit_attn_fwd_block calls with
 float32 partials, then dit_attn_merge, B1 H40 N32768 D128) is timed after the
 steps and reported under "legs"; it is not part of `value`.
@@ -232,6 +237,37 @@ def main():
                  "bwd_TFLOPs": 2.5 * flops_launch / (bwd_ms * 1e-3) / 1e12,
                  "fwd_plus_bwd_ms": attn_avg_ms + bwd_ms})
     del g_dq, g_dk, g_dv, dout
+
+    # joint leg: 512 text + 4096 image tokens (1024x1024 picture, 64x64
+    # patches), 24 heads of 128, RoPE on q and k: dit_attn_fwd_joint (one
+    # pack launch + the attention) and the attention alone on the packed
+    # buffers; FLOPs 4*B*H*N^2*D over the N = 4608 joint tokens.
+    print("[bench] joint text+image leg", file=sys.stderr, flush=True)
+    jt, ji = datagen.joint_bf16(1, 24, 512, 24, 4096, D, seed=31)
+    jt, ji = [to_dev(x) for x in jt], [to_dev(x) for x in ji]
+    tabs = [torch.from_numpy(x).to(dev) for x in
+            (*datagen.rope_tables_text(512, 64, 64, D), *datagen.rope_tables_image(64, 64, D))]
+    jws = torch.empty((3, 1, 24, 4608, D), device=dev, dtype=torch.bfloat16)
+    jo = torch.empty((1, 24, 4608, D), device=dev, dtype=torch.bfloat16)
+    jl = torch.empty((1, 24, 4608), device=dev, dtype=torch.float32)
+    joint_ms = time_it(lambda: dta.dit_attn_fwd_joint(*jt, *ji, *tabs, workspace=jws, out=jo,
+                                                      lse=jl), reps=20)
+    jattn_ms = time_it(lambda: dta.dit_attn_fwd(jws[0], jws[1], jws[2], out=jo, lse=jl), reps=20)
+    jflops = attn_flops(1, 24, 4608, 4608, D)
+    legs.update({"joint_ms": joint_ms, "joint_TFLOPs": jflops / (joint_ms * 1e-3) / 1e12,
+                 "joint_attn_only_ms": jattn_ms, "joint_pack_ms": joint_ms - jattn_ms})
+    del jt, ji, jws, jo
+
+    # cross leg: the 10-head share's 32768 image queries over 512 text keys
+    # and values (dit_attn_fwd_block, bf16 out).
+    print("[bench] cross attention leg", file=sys.stderr, flush=True)
+    _, ck, cv = (to_dev(x) for x in datagen.small_bf16(1, H, 1, D, seed=51, Nkv=512))
+    co = torch.empty((B, H, N, D), device=dev, dtype=torch.bfloat16)
+    cl = torch.empty((B, H, N), device=dev, dtype=torch.float32)
+    cross_ms = time_it(lambda: dta.dit_attn_fwd_block(groups[0][0], ck, cv, out=co, lse=cl), reps=20)
+    legs.update({"cross_ms": cross_ms,
+                 "cross_TFLOPs": attn_flops(B, H, N, 512, D) / (cross_ms * 1e-3) / 1e12})
+    del co, cl
 
     if not args.no_ring:
         print("[bench] ring leg", file=sys.stderr, flush=True)

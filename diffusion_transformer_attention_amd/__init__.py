@@ -22,8 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libditattn.so")
 DIT_BF16, DIT_F32 = 0, 1
 DIT_OK, DIT_EINVAL, DIT_EUNSUPPORTED, DIT_EALIGN, DIT_ELAUNCH, DIT_ERANGE = 0, -1, -2, -3, -4, -5
 EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_ulysses", "dit_attn_bwd",
-            "dit_attn_merge", "ulysses_seq2head", "ulysses_head2seq", "dit_strerror",
-            "dit_abi_version")
+            "dit_attn_merge", "dit_rope_pack", "dit_attn_fwd_joint", "ulysses_seq2head",
+            "ulysses_head2seq", "dit_strerror", "dit_abi_version")
 
 _lib = None
 
@@ -43,10 +43,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dit_attn_fwd_ulysses.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, P]
     lib.dit_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P]
     lib.dit_attn_merge.argtypes = [P, P, I, P, P, I, I, I, I, I, P]
+    lib.dit_rope_pack.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+    lib.dit_attn_fwd_joint.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                       I, I, I, I, I, I, I, F, P]
     lib.ulysses_seq2head.argtypes = [P, P, I, I, I, I, I, I, P]
     lib.ulysses_head2seq.argtypes = [P, P, I, I, I, I, I, I, P]
     for name in ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_ulysses", "dit_attn_bwd",
-                 "dit_attn_merge", "ulysses_seq2head", "ulysses_head2seq", "dit_abi_version"):
+                 "dit_attn_merge", "dit_rope_pack", "dit_attn_fwd_joint", "ulysses_seq2head", "ulysses_head2seq", "dit_abi_version"):
         getattr(lib, name).restype = ctypes.c_int
     lib.dit_strerror.argtypes = [ctypes.c_int]
     lib.dit_strerror.restype = ctypes.c_char_p
@@ -249,6 +252,94 @@ def dit_attn_merge(o_parts, lse_parts, out_dtype=torch.bfloat16, out=None, lse=N
     return o, lse
 
 
+def _joint_shapes(x_txt, x_img, h0):
+    _need(x_txt, "text tensor", 4)
+    _need(x_img, "image tensor", 4)
+    if x_txt.dtype != torch.bfloat16 or x_img.dtype != torch.bfloat16:
+        raise ValueError("text and image tensors must be bf16")
+    B, Ht, Nt, D = x_txt.shape
+    Bi, H, Ni, Di = x_img.shape
+    if B != Bi or D != Di:
+        raise ValueError("text [B,Ht,Nt,D] and image [B,H,Ni,D] must share B and D")
+    if Nt and not (0 <= h0 and h0 + H <= Ht):
+        raise ValueError("text heads h0 .. h0+H-1 must lie in [0, Ht)")
+    return B, H, Ht, Nt, Ni, D
+
+
+def _tables(c, s, n, half, what):
+    if (c is None) != (s is None):
+        raise ValueError(f"{what}: give both cos and sin tables or neither")
+    for t, name in ((c, "cos"), (s, "sin")):
+        if t is not None:
+            _need(t, f"{what} {name}", 2)
+            if t.dtype != torch.float32 or tuple(t.shape) != (n, half):
+                raise ValueError(f"{what} {name} must be float32 [{n}, {half}]")
+
+
+def dit_rope_pack(x_txt, x_img, cos_txt=None, sin_txt=None, cos_img=None, sin_img=None, h0=0,
+                  out=None):
+    """Joint sequence of one tensor: text bf16 [B,Ht,Nt,D] (heads h0 .. h0+H-1
+    used) then image bf16 [B,H,Ni,D], each part turned by its rotary tables
+    (float32 [N, D/2]) when given.  Returns out bf16 [B,H,Nt+Ni,D]."""
+    lib = load_library()
+    B, H, Ht, Nt, Ni, D = _joint_shapes(x_txt, x_img, h0)
+    _tables(cos_txt, sin_txt, Nt, D // 2, "text")
+    _tables(cos_img, sin_img, Ni, D // 2, "image")
+    o = torch.empty((B, H, Nt + Ni, D), device=x_img.device, dtype=torch.bfloat16) \
+        if out is None else out
+    _need(o, "out", 4)
+    if tuple(o.shape) != (B, H, Nt + Ni, D) or o.dtype != torch.bfloat16:
+        raise ValueError("out must be bf16 [B,H,Nt+Ni,D]")
+    rc = lib.dit_rope_pack(_ptr(x_txt), _ptr(x_img), _ptr(cos_txt), _ptr(sin_txt), _ptr(cos_img),
+                           _ptr(sin_img), _ptr(o), B, H, Ht, int(h0), Nt, Ni, D, _stream())
+    _check(rc, "dit_rope_pack")
+    return o
+
+
+def dit_attn_fwd_joint(q_txt, k_txt, v_txt, q_img, k_img, v_img, cos_txt=None, sin_txt=None,
+                       cos_img=None, sin_img=None, h0=0, scale=None, workspace=None, out=None,
+                       lse=None, return_lse=True):
+    """Joint text + image attention with RoPE on q and k.
+
+    Text q/k/v bf16 [B,Ht,Nt,D] (heads h0 .. h0+H-1 used), image q/k/v bf16
+    [B,H,Ni,D], rotary tables float32 [Nt, D/2] / [Ni, D/2] or None.  Returns
+    (O bf16 [B,H,Nt+Ni,D] with the text rows first, LSE float32 [B,H,Nt+Ni]
+    or None).  ``workspace`` (bf16 [3,B,H,Nt+Ni,D]) is allocated when None.
+    """
+    lib = load_library()
+    B, H, Ht, Nt, Ni, D = _joint_shapes(q_txt, q_img, h0)
+    for t, r in ((k_txt, q_txt), (v_txt, q_txt), (k_img, q_img), (v_img, q_img)):
+        _need(t, "k/v", 4)
+        if t.shape != r.shape or t.dtype != r.dtype:
+            raise ValueError("text (image) q, k, v must share shape and dtype")
+    _tables(cos_txt, sin_txt, Nt, D // 2, "text")
+    _tables(cos_img, sin_img, Ni, D // 2, "image")
+    N = Nt + Ni
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dev = q_img.device
+    ws = torch.empty((3, B, H, N, D), device=dev, dtype=torch.bfloat16) \
+        if workspace is None else workspace
+    _need(ws, "workspace", 5)
+    if tuple(ws.shape) != (3, B, H, N, D) or ws.dtype != torch.bfloat16:
+        raise ValueError("workspace must be bf16 [3,B,H,Nt+Ni,D]")
+    o = torch.empty((B, H, N, D), device=dev, dtype=torch.bfloat16) if out is None else out
+    _need(o, "out", 4)
+    if tuple(o.shape) != (B, H, N, D) or o.dtype != torch.bfloat16:
+        raise ValueError("out must be bf16 [B,H,Nt+Ni,D]")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), device=dev, dtype=torch.float32)
+    if lse is not None:
+        _need(lse, "lse", 3)
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N):
+            raise ValueError("lse must be float32 [B,H,Nt+Ni]")
+    rc = lib.dit_attn_fwd_joint(_ptr(q_txt), _ptr(k_txt), _ptr(v_txt), _ptr(q_img), _ptr(k_img),
+                                _ptr(v_img), _ptr(cos_txt), _ptr(sin_txt), _ptr(cos_img),
+                                _ptr(sin_img), _ptr(ws), _ptr(o), _ptr(lse), B, H, Ht, int(h0),
+                                Nt, Ni, D, ctypes.c_float(scale), _stream())
+    _check(rc, "dit_attn_fwd_joint")
+    return o, lse
+
+
 def ulysses_seq2head(shards, out=None):
     """[P,B,H,N/P,D] token shards -> [P,B,H/P,N,D] head groups (bit-exact, any dtype)."""
     lib = load_library()
@@ -282,6 +373,6 @@ def ulysses_head2seq(groups, out=None):
 
 
 __all__ = ["dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_ulysses", "dit_attn_bwd",
-           "dit_attn_merge", "ulysses_seq2head",
+           "dit_attn_merge", "dit_rope_pack", "dit_attn_fwd_joint", "ulysses_seq2head",
            "ulysses_head2seq", "dit_strerror", "dit_abi_version", "load_library", "DitError",
            "LIB_PATH", "EXPORTED", "DIT_BF16", "DIT_F32"]

@@ -67,6 +67,30 @@ int permute_common(const void* in, void* out, int P, int B, int H, int N, int D,
                                             static_cast<hipStream_t>(stream)));
 }
 
+// Sizes and table pairs shared by the joint-sequence calls.
+int joint_check(int B, int H, int Ht, int h0, int Nt, int Ni, int D) {
+  if (B < 0 || H < 0 || Nt < 0 || Ni < 0 || D <= 0) return DIT_EINVAL;
+  if (Nt > 0 && (h0 < 0 || Ht < 1 || H > Ht || h0 > Ht - H)) return DIT_EINVAL;
+  if (!supported_head_dim(D)) return DIT_EUNSUPPORTED;
+  const int64_t N = (int64_t)Nt + Ni;
+  if (N > 0x7fffffff || !size_ok(B, H, N, 3 * (int64_t)D) || !size_ok(B, Ht, Nt, D))
+    return DIT_ERANGE;
+  return DIT_OK;
+}
+
+int tables_check(const float* c, const float* s) {
+  if ((c == nullptr) != (s == nullptr)) return DIT_EINVAL;
+  if (c && (!aligned(c, 16) || !aligned(s, 16))) return DIT_EALIGN;
+  return DIT_OK;
+}
+
+// Pointers of one packed tensor: each part present when its length is.
+int part_check(const void* txt, const void* img, int Nt, int Ni) {
+  if ((Nt > 0 && !txt) || (Ni > 0 && !img)) return DIT_EINVAL;
+  if ((Nt > 0 && !aligned(txt, 16)) || (Ni > 0 && !aligned(img, 16))) return DIT_EALIGN;
+  return DIT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,6 +155,53 @@ int dit_attn_bwd(const void* q, const void* k, const void* v, const void* o, con
   return map_launch(ditattn::launch_attn_bwd_bf16(
       q, k, v, o, dout, lse, delta, static_cast<float*>(dq), static_cast<float*>(dk),
       static_cast<float*>(dv), B, H, Nq, Nkv, scale, static_cast<hipStream_t>(stream)));
+}
+
+int dit_rope_pack(const void* x_txt, const void* x_img, const float* cos_txt,
+                  const float* sin_txt, const float* cos_img, const float* sin_img, void* out,
+                  int B, int H, int Ht, int h0, int Nt, int Ni, int D, void* stream) {
+  int rc = joint_check(B, H, Ht, h0, Nt, Ni, D);
+  if (rc != DIT_OK) return rc;
+  if (B == 0 || H == 0 || Nt + Ni == 0) return DIT_OK;
+  if ((rc = part_check(x_txt, x_img, Nt, Ni)) != DIT_OK) return rc;
+  if ((rc = tables_check(cos_txt, sin_txt)) != DIT_OK) return rc;
+  if ((rc = tables_check(cos_img, sin_img)) != DIT_OK) return rc;
+  if (!out) return DIT_EINVAL;
+  if (!aligned(out, 16)) return DIT_EALIGN;
+  const ditattn::RopePackTensor t{x_txt, x_img, out, cos_txt, sin_txt, cos_img, sin_img};
+  return map_launch(ditattn::launch_rope_pack(&t, 1, B, H, Ht, h0, Nt, Ni, D,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int dit_attn_fwd_joint(const void* q_txt, const void* k_txt, const void* v_txt,
+                       const void* q_img, const void* k_img, const void* v_img,
+                       const float* cos_txt, const float* sin_txt, const float* cos_img,
+                       const float* sin_img, void* workspace, void* o, float* lse, int B, int H,
+                       int Ht, int h0, int Nt, int Ni, int D, float scale, void* stream) {
+  int rc = joint_check(B, H, Ht, h0, Nt, Ni, D);
+  if (rc != DIT_OK) return rc;
+  if (!(isfinite(scale) && scale > 0.0f)) return DIT_EINVAL;
+  if (B == 0 || H == 0 || Nt + Ni == 0) return DIT_OK;
+  if ((rc = part_check(q_txt, q_img, Nt, Ni)) != DIT_OK) return rc;
+  if ((rc = part_check(k_txt, k_img, Nt, Ni)) != DIT_OK) return rc;
+  if ((rc = part_check(v_txt, v_img, Nt, Ni)) != DIT_OK) return rc;
+  if ((rc = tables_check(cos_txt, sin_txt)) != DIT_OK) return rc;
+  if ((rc = tables_check(cos_img, sin_img)) != DIT_OK) return rc;
+  if (!workspace || !o) return DIT_EINVAL;
+  if (!aligned(workspace, 16) || !aligned(o, 16)) return DIT_EALIGN;
+  if (lse && !aligned(lse, 4)) return DIT_EALIGN;
+  const int N = Nt + Ni;
+  const int64_t elems = (int64_t)B * H * N * D;
+  __bf16* ws = static_cast<__bf16*>(workspace);
+  const ditattn::RopePackTensor t[3] = {
+      {q_txt, q_img, ws, cos_txt, sin_txt, cos_img, sin_img},
+      {k_txt, k_img, ws + elems, cos_txt, sin_txt, cos_img, sin_img},
+      {v_txt, v_img, ws + 2 * elems, nullptr, nullptr, nullptr, nullptr}};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = ditattn::launch_rope_pack(t, 3, B, H, Ht, h0, Nt, Ni, D, s);
+  if (e != hipSuccess) return DIT_ELAUNCH;
+  return map_launch(ditattn::launch_attn_bf16(ws, ws + elems, ws + 2 * elems, o, lse, B, H, N, N,
+                                              D, scale, false, s));
 }
 
 int ulysses_seq2head(const void* in, void* out, int P, int B, int H, int N, int D, int elem_bytes,

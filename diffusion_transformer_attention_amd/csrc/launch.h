@@ -25,6 +25,23 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
                                 float* dk, float* dv, int B, int H, int Nq, int Nkv, float scale,
                                 hipStream_t stream);
 
+// One tensor of a joint-sequence pack: text part [B,Ht,Nt,D] (heads h0 ..
+// h0+H-1 used), image part [B,H,Ni,D], output [B,H,Nt+Ni,D], all bf16.  A
+// part's rotary tables ([N, D/2] float32) may be null: that part is copied.
+struct RopePackTensor {
+  const void* txt;
+  const void* img;
+  void* out;
+  const float* cos_txt;
+  const float* sin_txt;
+  const float* cos_img;
+  const float* sin_img;
+};
+
+// Packs 1 to 3 tensors in one launch.
+hipError_t launch_rope_pack(const RopePackTensor* tensors, int ntensors, int B, int H, int Ht,
+                            int h0, int Nt, int Ni, int D, hipStream_t stream);
+
 // float32 q/k/v/o.  lse may be null.
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                            int B, int H, int Nq, int Nkv, int D, float scale, hipStream_t stream);

@@ -15,6 +15,11 @@
  *         "Limitations" (everything outside the envelope fails loudly: head
  *         count divisible by the Ulysses degree, sequence length divisible by
  *         the SP degree, no mask / dropout / causal flag under SP).
+ *   [VO]  "Parallelism Acceleration Guide" (vLLM-Omni docs), section "How
+ *         to parallelize a new model": a dual-stream (text + image) model
+ *         runs joint attention over the concatenated sequences; the text
+ *         stays whole on every sequence-parallel rank and the image rotary
+ *         tables are cut along the token axis with the image tokens.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -47,11 +52,13 @@ typedef enum { DIT_BF16 = 0, DIT_F32 = 1 } dit_dtype;
 enum {
   DIT_OK = 0,
   DIT_EINVAL = -1,       /* null pointer, negative size, Nkv == 0, scale not finite or <= 0,
-                            H % P != 0, N % P != 0, nblk < 1, P < 1, r outside [0, P) */
+                            H % P != 0, N % P != 0, nblk < 1, P < 1, r outside [0, P),
+                            text head range outside [0, Ht), cos without sin */
   DIT_EUNSUPPORTED = -2, /* D not in {32, 64, 128}, a dtype combination not built, elem_bytes
                             not in {1, 2, 4, 8}, fused Ulysses shard length not a multiple
                             of 64 */
-  DIT_EALIGN = -3,       /* q/k/v/o/o_parts not 16-byte aligned, lse not 4-byte aligned,
+  DIT_EALIGN = -3,       /* q/k/v/o/o_parts/rotary tables not 16-byte aligned, lse not
+                            4-byte aligned,
                             permute buffers not aligned to elem_bytes */
   DIT_ELAUNCH = -4,      /* the HIP runtime reported an error at launch */
   DIT_ERANGE = -5        /* a size product does not fit the 64-bit index space */
@@ -164,6 +171,55 @@ int dit_attn_merge(const float* o_parts, const float* lse_parts, int nblk,
 int dit_attn_fwd_ulysses(const void* q, const void* k, const void* v, void* o, float* lse,
                          int P, int r, int B, int H, int N, int D, float scale, int dtype,
                          void* stream);
+
+/*
+ * Joint text + image sequence with rotary position embedding ([VO]): per
+ * (b, h), the Nt text tokens of head h0 + h of the text tensor, then the Ni
+ * image tokens of head h of the image tensor.  The pages name the rotary
+ * tables but not the rotation; the reading taken is RoFormer's rotary
+ * embedding in interleaved form: channels (2i, 2i+1) of token n are one pair,
+ * turned by that token's angle for pair i,
+ *
+ *   y[2i] = x[2i] cos[n,i] - x[2i+1] sin[n,i],  y[2i+1] = x[2i] sin[n,i] + x[2i+1] cos[n,i]
+ *
+ * in float32, rounded to bf16 (nearest, ties to even).
+ *
+ *   x_txt            : bf16 [B,Ht,Nt,D]; heads h0 .. h0+H-1 are used (the
+ *                      text stays replicated with all Ht heads on every rank,
+ *                      the call covers one head group of it)
+ *   x_img            : bf16 [B,H,Ni,D]
+ *   cos_txt, sin_txt : float32 [Nt, D/2], or both NULL: text copied unturned
+ *   cos_img, sin_img : float32 [Ni, D/2], or both NULL: image copied unturned
+ *   out              : bf16 [B,H,Nt+Ni,D]
+ * x_txt may be NULL when Nt == 0 and x_img when Ni == 0.  Requires
+ * 0 <= h0, h0 + H <= Ht when Nt > 0, and one of cos / sin of a part given
+ * without the other is DIT_EINVAL.  Tables must be 16-byte aligned.
+ */
+int dit_rope_pack(const void* x_txt, const void* x_img, const float* cos_txt,
+                  const float* sin_txt, const float* cos_img, const float* sin_img, void* out,
+                  int B, int H, int Ht, int h0, int Nt, int Ni, int D, void* stream);
+
+/*
+ * Joint attention ([VO]): every text and image query attends over every text
+ * and image key, with the rotary embedding on queries and keys (not values):
+ * dit_rope_pack of q and k (with the tables) and of v (without), then
+ * dit_attn_fwd over the N = Nt + Ni joint tokens.
+ *
+ *   q_txt, k_txt, v_txt : bf16 [B,Ht,Nt,D] (heads h0 .. h0+H-1 used)
+ *   q_img, k_img, v_img : bf16 [B,H,Ni,D]
+ *   tables              : as in dit_rope_pack
+ *   workspace           : bf16 [3][B,H,N,D] scratch owned by the caller (the
+ *                         packed q, k, v; overwritten)
+ *   o                   : bf16 [B,H,N,D], text rows first
+ *   lse                 : float32 [B,H,N], or NULL to skip
+ * Cross attention (image queries over text keys only) needs no packing: it
+ * is dit_attn_fwd_block with Nq = Ni and Nkv = Nt.
+ */
+int dit_attn_fwd_joint(const void* q_txt, const void* k_txt, const void* v_txt,
+                       const void* q_img, const void* k_img, const void* v_img,
+                       const float* cos_txt, const float* sin_txt, const float* cos_img,
+                       const float* sin_img, void* workspace, void* o, float* lse, int B, int H,
+                       int Ht, int h0, int Nt, int Ni, int D, float scale, void* stream);
 
 /*
  * Ulysses sequence -> head exchange as it lands on one device ([HB] Ulysses

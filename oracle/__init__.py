@@ -7,10 +7,12 @@ from .ref import (attention, attention_rows, probabilities, split_kv, merge,
                   attention_backward, attention_backward_rows, attention_backward_keys,
                   ring_attention, shard_tokens, seq2head, head2seq,
                   unshard_tokens, ulysses_attention, ulysses_send_bytes_per_rank,
-                  default_scale, rope, joint_sequence, joint_attention)
+                  default_scale, rope, round_bf16, joint_sequence,
+                  joint_attention)
 
 __all__ = ["attention", "attention_rows", "probabilities", "split_kv", "merge",
            "attention_backward", "attention_backward_rows", "attention_backward_keys",
            "ring_attention", "shard_tokens", "seq2head", "head2seq",
            "unshard_tokens", "ulysses_attention", "ulysses_send_bytes_per_rank",
-           "default_scale", "rope", "joint_sequence", "joint_attention"]
+           "default_scale", "rope", "round_bf16", "joint_sequence",
+           "joint_attention"]

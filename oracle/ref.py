@@ -307,22 +307,38 @@ def rope(x, cos, sin):
     return y
 
 
-def joint_sequence(x_txt, x_img, cos_txt=None, sin_txt=None, cos_img=None, sin_img=None):
+def round_bf16(x):
+    """Round float64 values to the nearest bfloat16 value (8 significant bits),
+    ties to even; zero stays zero.  Finite inputs in bfloat16's normal range."""
+    x = _f64(x)
+    out = np.zeros_like(x)
+    nz = x != 0
+    ulp = np.ldexp(1.0, np.floor(np.log2(np.abs(x[nz]))).astype(np.int64) - 7)
+    out[nz] = np.round(x[nz] / ulp) * ulp   # numpy rounds halves to even
+    return out
+
+
+def joint_sequence(x_txt, x_img, cos_txt=None, sin_txt=None, cos_img=None, sin_img=None,
+                   to_bf16=False):
     """[B,H,Nt,D] text and [B,H,Ni,D] image tokens -> [B,H,Nt+Ni,D], text
-    first, each part turned by its own rotary tables when they are given."""
+    first, each part turned by its own rotary tables when they are given.
+    to_bf16: round the result to bfloat16, the type the attention takes its
+    inputs in (the reading for a bf16 model: the turned tokens are handed to
+    attention in the model's type)."""
     t = _f64(x_txt) if cos_txt is None else rope(x_txt, cos_txt, sin_txt)
     i = _f64(x_img) if cos_img is None else rope(x_img, cos_img, sin_img)
-    return np.concatenate([t, i], axis=2)
+    y = np.concatenate([t, i], axis=2)
+    return round_bf16(y) if to_bf16 else y
 
 
 def joint_attention(q_txt, k_txt, v_txt, q_img, k_img, v_img, cos_txt=None, sin_txt=None,
-                    cos_img=None, sin_img=None, scale=None, rows=None):
+                    cos_img=None, sin_img=None, scale=None, rows=None, to_bf16=False):
     """Attention of every text and image query over every text and image key,
     with RoPE on queries and keys (not values).  Returns (O, LSE) of the joint
     sequence [B,H,Nt+Ni,...]; ``rows`` restricts the queries to those joint
-    rows."""
-    q = joint_sequence(q_txt, q_img, cos_txt, sin_txt, cos_img, sin_img)
-    k = joint_sequence(k_txt, k_img, cos_txt, sin_txt, cos_img, sin_img)
+    rows; ``to_bf16`` rounds the turned queries and keys to bfloat16 first."""
+    q = joint_sequence(q_txt, q_img, cos_txt, sin_txt, cos_img, sin_img, to_bf16)
+    k = joint_sequence(k_txt, k_img, cos_txt, sin_txt, cos_img, sin_img, to_bf16)
     v = joint_sequence(v_txt, v_img)
     if rows is not None:
         q = q[:, :, np.asarray(rows, dtype=np.int64)]

@@ -126,6 +126,48 @@ def test_backward_validation(lib):
     assert b(Nq=-1) == dta.DIT_EINVAL
 
 
+def test_rope_pack_validation(lib):
+    def r(xt=A, xi=A, ct=A, st=A, ci=A, si=A, out=A, B=1, H=2, Ht=8, h0=2, Nt=16, Ni=64, D=128):
+        return lib.dit_rope_pack(xt, xi, ct, st, ci, si, out, B, H, Ht, h0, Nt, Ni, D, S)
+    assert r(h0=7) == dta.DIT_EINVAL           # text heads 7, 8 past Ht = 8
+    assert r(h0=-1) == dta.DIT_EINVAL
+    assert r(Ht=1) == dta.DIT_EINVAL           # fewer text heads than the launch covers
+    # no text (image): its pointer and heads are not looked at; the misaligned
+    # output then fails the last check, so no call here reaches a launch
+    assert r(Nt=0, Ht=0, h0=0, xt=NULL, out=MIS) == dta.DIT_EALIGN
+    assert r(Ni=0, xi=NULL, out=MIS) == dta.DIT_EALIGN
+    assert r(xt=NULL) == dta.DIT_EINVAL
+    assert r(xi=NULL) == dta.DIT_EINVAL
+    assert r(out=NULL) == dta.DIT_EINVAL
+    assert r(ct=NULL) == dta.DIT_EINVAL        # cos without sin
+    assert r(si=NULL) == dta.DIT_EINVAL
+    assert r(ct=MIS) == dta.DIT_EALIGN
+    assert r(xi=MIS) == dta.DIT_EALIGN
+    assert r(out=MIS) == dta.DIT_EALIGN
+    assert r(D=96) == dta.DIT_EUNSUPPORTED
+    assert r(Nt=-1) == dta.DIT_EINVAL
+    assert r(Nt=0, Ni=0) == dta.DIT_OK         # nothing to pack
+    assert r(B=0) == dta.DIT_OK
+    assert r(Nt=2 ** 30, Ni=2 ** 30) == dta.DIT_ERANGE
+
+
+def test_joint_validation(lib):
+    def j(q=A, ws=A, o=A, lse=A, ct=A, st=A, Ht=4, h0=0, Nt=16, Ni=64, D=128, scale=0.125):
+        return lib.dit_attn_fwd_joint(q, A, A, q, A, A, ct, st, A, A, ws, o, lse, 1, 4, Ht, h0,
+                                      Nt, Ni, D, ctypes.c_float(scale), S)
+    assert j(ws=NULL) == dta.DIT_EINVAL
+    assert j(o=NULL) == dta.DIT_EINVAL
+    assert j(q=NULL) == dta.DIT_EINVAL
+    assert j(ct=NULL) == dta.DIT_EINVAL
+    assert j(ct=NULL, st=NULL, o=MIS) == dta.DIT_EALIGN
+    assert j(ws=MIS) == dta.DIT_EALIGN
+    assert j(lse=V(0x10002)) == dta.DIT_EALIGN
+    assert j(scale=0.0) == dta.DIT_EINVAL
+    assert j(h0=1) == dta.DIT_EINVAL           # heads 1..4 of a 4-head text tensor
+    assert j(D=16) == dta.DIT_EUNSUPPORTED
+    assert j(Nt=0, Ni=0) == dta.DIT_OK
+
+
 @pytest.mark.parametrize("fn", ["ulysses_seq2head", "ulysses_head2seq"])
 def test_permute_validation(lib, fn):
     f = getattr(lib, fn)

@@ -15,6 +15,10 @@ Python complex arithmetic, math.exp / math.fsum) on tiny inputs, by the empty
 text case reducing to plain attention of the turned image tokens, and by key
 order not mattering (image-first concatenation gives the same rows).
 
+round_bf16 (the reading that the turned tokens enter attention as bf16) is
+pinned by the halfway cases (ties go to the even neighbour) and by agreement
+with datagen's integer bit-pattern rounding of float32 values.
+
 The planted-mistake tests check that each mistake in a copy of the oracle is
 rejected by at least one pin.
 """
@@ -186,6 +190,25 @@ def test_datagen_tables_are_unit_and_axial():
     assert abs(float(si[6, 0]) - math.sin(1.0)) < 1e-7 and float(si[6, 4]) == 0.0
     assert abs(float(si[1, 4]) - math.sin(1.0)) < 1e-7 and float(si[1, 0]) == 0.0
     assert abs(float(ct[0, 0]) - math.cos(6.0)) < 1e-7
+
+
+def test_round_bf16_ties_to_even():
+    r = oracle.round_bf16
+    # bf16 spacing at 1 is 2**-7: 1 + 2**-8 is halfway to 1 + 2**-7 (odd), so it stays 1;
+    # 1 + 3 * 2**-8 is halfway between 1 + 2**-7 (odd) and 1 + 2**-6 (even)
+    assert r(1 + 2 ** -8) == 1.0 and r(-(1 + 2 ** -8)) == -1.0
+    assert r(1 + 3 * 2 ** -8) == 1 + 2 ** -6
+    assert r(1 + 2 ** -8 + 2 ** -30) == 1 + 2 ** -7     # just past halfway
+    assert r(0.0) == 0.0 and r(2.0 ** -100) == 2.0 ** -100
+    assert r(255.5) == 256.0 and r(254.5) == 254.0       # spacing 1 in [128, 256)
+
+
+def test_round_bf16_matches_bit_pattern_rounding():
+    x = (_rng(20).standard_normal(200000) * np.exp(_rng(21).uniform(-20, 20, 200000))).astype(np.float32)
+    want = datagen.bf16_to_f32(datagen.bf16_bits(x)).astype(np.float64)
+    got = oracle.round_bf16(x.astype(np.float64))
+    assert np.array_equal(got, want)
+    assert np.array_equal(oracle.round_bf16(got), got)
 
 
 # ---------------------------------------------------- planted mistakes
