@@ -8,11 +8,13 @@ from .ref import (attention, attention_rows, probabilities, split_kv, merge,
                   ring_attention, shard_tokens, seq2head, head2seq,
                   unshard_tokens, ulysses_attention, ulysses_send_bytes_per_rank,
                   default_scale, rope, round_bf16, joint_sequence,
-                  joint_attention)
+                  joint_attention, E4M3_MAX, e4m3_decode, e4m3_round, e4m3_encode,
+                  quantize_fp8, attention_fp8)
 
 __all__ = ["attention", "attention_rows", "probabilities", "split_kv", "merge",
            "attention_backward", "attention_backward_rows", "attention_backward_keys",
            "ring_attention", "shard_tokens", "seq2head", "head2seq",
            "unshard_tokens", "ulysses_attention", "ulysses_send_bytes_per_rank",
            "default_scale", "rope", "round_bf16", "joint_sequence",
-           "joint_attention"]
+           "joint_attention", "E4M3_MAX", "e4m3_decode", "e4m3_round", "e4m3_encode",
+           "quantize_fp8", "attention_fp8"]

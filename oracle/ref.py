@@ -343,3 +343,77 @@ def joint_attention(q_txt, k_txt, v_txt, q_img, k_img, v_img, cos_txt=None, sin_
     if rows is not None:
         q = q[:, :, np.asarray(rows, dtype=np.int64)]
     return attention(q, k, v, scale)
+
+
+# --------------------------------------------------------------------------
+# FP8 attention.  The handbook ("Multi-GPU parallelism: spreading one step
+# over several cards", section "Combining: what xDiT does") stacks FP8 low
+# precision on top of the parallel split and caching, without saying which
+# tensors are 8-bit.  The reading taken: queries and keys are quantized to the
+# OCP 8-bit floating-point format E4M3 (1 sign, 4 exponent bits with bias 7,
+# 3 mantissa bits, subnormals, largest finite 448, no infinities, S.1111.111
+# is NaN), one scale per (b, h) from the tensor's largest magnitude; the
+# scores are their exact product times both scales; P and V stay in the
+# model's type.
+# --------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes):
+    """E4M3 codes (uint8) -> float64 values (NaN for the two NaN codes)."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def e4m3_round(x):
+    """Nearest E4M3 value to each finite float64 x, ties to even, magnitudes
+    beyond 448 clamped to 448.  The spacing is 2**(e-3) in the binade
+    [2**e, 2**(e+1)) for e >= -6 and 2**-9 below 2**-6 (subnormals)."""
+    x = _f64(x)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    ulp = np.where(a >= 2.0 ** -6, np.ldexp(1.0, (e - 3).astype(np.int64)), 2.0 ** -9)
+    r = np.round(a / ulp) * ulp                      # halves to even
+    return np.copysign(np.minimum(r, E4M3_MAX), x)
+
+
+def e4m3_encode(x):
+    """Codes of e4m3_round(x) (uint8); -0 encodes as 0x80."""
+    v = e4m3_round(x)
+    a = np.abs(v)
+    sub = a < 2.0 ** -6
+    e = np.floor(np.log2(np.where(sub, 1.0, a)))
+    m_norm = np.round((a / np.ldexp(1.0, e.astype(np.int64)) - 1.0) * 8.0)
+    m_sub = np.round(a / 2.0 ** -9)
+    code = np.where(sub, m_sub, ((e + 7) * 8 + m_norm))
+    return (code.astype(np.uint8) | np.where(np.signbit(v), 0x80, 0).astype(np.uint8))
+
+
+def quantize_fp8(x):
+    """Per-(b, h) E4M3 quantization of x [B,H,N,D] (float32 values).
+
+    descale[b,h] = amax / 448 in float32 (1 when the head is all zeros);
+    code = E4M3 rounding of the float32 quotient x / descale, clamped to
+    +-448.  Returns (codes uint8 [B,H,N,D], descale float32 [B,H]).  The
+    quotient is taken in float32, the type the scale is kept in, so both the
+    scale and each code are fixed by float32 arithmetic."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.abs(x32).max(axis=(2, 3)) if x32.size else np.zeros(x32.shape[:2], np.float32)
+    descale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    quotient = x32 / descale[:, :, None, None]
+    return e4m3_encode(quotient.astype(np.float64)), descale
+
+
+def attention_fp8(q_codes, k_codes, v, q_descale, k_descale, scale=None, rows=None):
+    """Attention of E4M3 queries and keys: q = decode(q_codes) * q_descale[b,h],
+    likewise k; v as given.  ``scale`` defaults to 1/sqrt(D)."""
+    q = e4m3_decode(q_codes) * _f64(q_descale)[:, :, None, None]
+    k = e4m3_decode(k_codes) * _f64(k_descale)[:, :, None, None]
+    if rows is not None:
+        q = q[:, :, np.asarray(rows, dtype=np.int64)]
+    return attention(q, k, v, scale)
