@@ -23,6 +23,9 @@ tokens, then attention) on 512 text + 4096 image tokens, B1 H24 D128, and the
 attention alone; the cross leg times dit_attn_fwd_block of the 10-head share's
 32768 queries over 512 text keys.
 
+The fp8 leg quantizes the share's q and k per head to E4M3 (dit_quant_fp8)
+and times dit_attn_fwd_fp8 on them (same FLOP count as the bf16 launch).
+
 The ring leg (K/V in 4 blocks of 8192: four dit_attn_fwd_block calls with
 float32 partials, then dit_attn_merge, B1 H40 N32768 D128) is timed after the
 steps and reported under "legs"; it is not part of `value`.
@@ -268,6 +271,21 @@ def main():
     legs.update({"cross_ms": cross_ms,
                  "cross_TFLOPs": attn_flops(B, H, N, 512, D) / (cross_ms * 1e-3) / 1e12})
     del co, cl
+
+    # fp8 leg: the same 10-head share with q and k quantized per head to
+    # E4M3 (dit_quant_fp8, timed for both tensors) and the fp8 attention.
+    print("[bench] fp8 leg", file=sys.stderr, flush=True)
+    q0, k0, v0 = groups[0][0], groups[1][0], groups[2][0]
+    qc, qd = dta.dit_quant_fp8(q0)
+    kc, kd = dta.dit_quant_fp8(k0)
+    fo, fl = torch.empty_like(outs[0]), torch.empty_like(lses[0])
+    quant_ms = time_it(lambda: (dta.dit_quant_fp8(q0, qc, qd), dta.dit_quant_fp8(k0, kc, kd)),
+                       reps=10)
+    fp8_ms = time_it(lambda: dta.dit_attn_fwd_fp8(qc, kc, v0, qd, kd, out=fo, lse=fl), reps=5)
+    legs.update({"fp8_attn_ms": fp8_ms,
+                 "fp8_attn_TFLOPs": flops_launch / (fp8_ms * 1e-3) / 1e12,
+                 "fp8_quant_qk_ms": quant_ms})
+    del qc, kc, fo, fl
 
     if not args.no_ring:
         print("[bench] ring leg", file=sys.stderr, flush=True)

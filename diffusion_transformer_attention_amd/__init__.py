@@ -22,8 +22,9 @@ LIB_PATH = os.path.join(_HERE, "libditattn.so")
 DIT_BF16, DIT_F32 = 0, 1
 DIT_OK, DIT_EINVAL, DIT_EUNSUPPORTED, DIT_EALIGN, DIT_ELAUNCH, DIT_ERANGE = 0, -1, -2, -3, -4, -5
 EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_ulysses", "dit_attn_bwd",
-            "dit_attn_merge", "dit_rope_pack", "dit_attn_fwd_joint", "ulysses_seq2head",
-            "ulysses_head2seq", "dit_strerror", "dit_abi_version")
+            "dit_attn_merge", "dit_rope_pack", "dit_attn_fwd_joint", "dit_quant_fp8",
+            "dit_attn_fwd_fp8", "ulysses_seq2head", "ulysses_head2seq", "dit_strerror",
+            "dit_abi_version")
 
 _lib = None
 
@@ -43,13 +44,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dit_attn_fwd_ulysses.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, P]
     lib.dit_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P]
     lib.dit_attn_merge.argtypes = [P, P, I, P, P, I, I, I, I, I, P]
+    lib.dit_quant_fp8.argtypes = [P, P, P, I, I, I, I, P]
+    lib.dit_attn_fwd_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, I, P]
     lib.dit_rope_pack.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
     lib.dit_attn_fwd_joint.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P,
                                        I, I, I, I, I, I, I, F, P]
     lib.ulysses_seq2head.argtypes = [P, P, I, I, I, I, I, I, P]
     lib.ulysses_head2seq.argtypes = [P, P, I, I, I, I, I, I, P]
     for name in ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_ulysses", "dit_attn_bwd",
-                 "dit_attn_merge", "dit_rope_pack", "dit_attn_fwd_joint", "ulysses_seq2head", "ulysses_head2seq", "dit_abi_version"):
+                 "dit_attn_merge", "dit_rope_pack", "dit_attn_fwd_joint", "dit_quant_fp8",
+           "dit_attn_fwd_fp8", "ulysses_seq2head", "ulysses_head2seq", "dit_abi_version"):
         getattr(lib, name).restype = ctypes.c_int
     lib.dit_strerror.argtypes = [ctypes.c_int]
     lib.dit_strerror.restype = ctypes.c_char_p
@@ -340,6 +344,75 @@ def dit_attn_fwd_joint(q_txt, k_txt, v_txt, q_img, k_img, v_img, cos_txt=None, s
     return o, lse
 
 
+def _codes(t, name):
+    _need(t, name, 4)
+    if t.element_size() != 1 or t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise ValueError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn)")
+
+
+def dit_quant_fp8(x, codes=None, descale=None):
+    """Per-(b, h) E4M3 quantization of bf16 x [B,H,N,D].
+
+    Returns (codes uint8 [B,H,N,D], descale float32 [B,H]) with
+    x ~= decode(codes) * descale[b, h].
+    """
+    lib = load_library()
+    _need(x, "x", 4)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bf16")
+    B, H, N, D = x.shape
+    c = torch.empty((B, H, N, D), device=x.device, dtype=torch.uint8) if codes is None else codes
+    _codes(c, "codes")
+    if tuple(c.shape) != (B, H, N, D):
+        raise ValueError("codes must match x")
+    ds = torch.empty((B, H), device=x.device, dtype=torch.float32) if descale is None else descale
+    _need(ds, "descale", 2)
+    if ds.dtype != torch.float32 or tuple(ds.shape) != (B, H):
+        raise ValueError("descale must be float32 [B,H]")
+    rc = lib.dit_quant_fp8(_ptr(x), _ptr(c), _ptr(ds), B, H, N, D, _stream())
+    _check(rc, "dit_quant_fp8")
+    return c, ds
+
+
+def dit_attn_fwd_fp8(q, k, v, q_descale, k_descale, scale=None, out_dtype=torch.bfloat16,
+                     out=None, lse=None, return_lse=True):
+    """Attention with E4M3 q [B,H,Nq,128] and k [B,H,Nkv,128] (codes, with
+    float32 [B,H] descales) and bf16 v [B,H,Nkv,128].
+
+    Returns (O [B,H,Nq,D] in out_dtype, LSE float32 [B,H,Nq] or None).
+    """
+    lib = load_library()
+    _codes(q, "q")
+    _codes(k, "k")
+    _need(v, "v", 4)
+    B, H, Nq, D = q.shape
+    Nkv = k.shape[2]
+    if k.shape[:2] != q.shape[:2] or k.shape[3] != D or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k, v must be [B,H,Nkv,D] matching q")
+    if v.dtype != torch.bfloat16:
+        raise ValueError("v must be bf16")
+    for t, n in ((q_descale, "q_descale"), (k_descale, "k_descale")):
+        _need(t, n, 2)
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, H):
+            raise ValueError(f"{n} must be float32 [B,H]")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o = torch.empty((B, H, Nq, D), device=q.device, dtype=out_dtype) if out is None else out
+    _need(o, "out", 4)
+    if tuple(o.shape) != (B, H, Nq, D):
+        raise ValueError("out must be [B,H,Nq,D]")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Nq), device=q.device, dtype=torch.float32)
+    if lse is not None:
+        _need(lse, "lse", 3)
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq):
+            raise ValueError("lse must be float32 [B,H,Nq]")
+    rc = lib.dit_attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(q_descale), _ptr(k_descale), _ptr(o),
+                              _ptr(lse), B, H, Nq, Nkv, D, ctypes.c_float(scale),
+                              _dtype_code(o.dtype), _stream())
+    _check(rc, "dit_attn_fwd_fp8")
+    return o, lse
+
+
 def ulysses_seq2head(shards, out=None):
     """[P,B,H,N/P,D] token shards -> [P,B,H/P,N,D] head groups (bit-exact, any dtype)."""
     lib = load_library()
@@ -373,6 +446,7 @@ def ulysses_head2seq(groups, out=None):
 
 
 __all__ = ["dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_ulysses", "dit_attn_bwd",
-           "dit_attn_merge", "dit_rope_pack", "dit_attn_fwd_joint", "ulysses_seq2head",
+           "dit_attn_merge", "dit_rope_pack", "dit_attn_fwd_joint", "dit_quant_fp8",
+           "dit_attn_fwd_fp8", "ulysses_seq2head",
            "ulysses_head2seq", "dit_strerror", "dit_abi_version", "load_library", "DitError",
            "LIB_PATH", "EXPORTED", "DIT_BF16", "DIT_F32"]

@@ -204,6 +204,38 @@ int dit_attn_fwd_joint(const void* q_txt, const void* k_txt, const void* v_txt,
                                               D, scale, false, s));
 }
 
+int dit_quant_fp8(const void* x, void* codes, float* descale, int B, int H, int N, int D,
+                  void* stream) {
+  if (B < 0 || H < 0 || N < 0 || D <= 0) return DIT_EINVAL;
+  if (!supported_head_dim(D)) return DIT_EUNSUPPORTED;
+  if (!size_ok(B, H, N, D) || (int64_t)B * H > 0x7fffffff) return DIT_ERANGE;
+  if (B == 0 || H == 0) return DIT_OK;
+  if (!descale || (N > 0 && (!x || !codes))) return DIT_EINVAL;
+  if (!aligned(descale, 4)) return DIT_EALIGN;
+  if (N > 0 && (!aligned(x, 16) || !aligned(codes, 8))) return DIT_EALIGN;
+  return map_launch(ditattn::launch_quant_fp8(x, codes, descale, B, H, N, D,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int dit_attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
+                     const float* k_descale, void* o, float* lse, int B, int H, int Nq, int Nkv,
+                     int D, float scale, int o_dtype, void* stream) {
+  if (B < 0 || H < 0 || Nq < 0 || Nkv < 0 || D <= 0) return DIT_EINVAL;
+  if (!(isfinite(scale) && scale > 0.0f)) return DIT_EINVAL;
+  if (o_dtype != DIT_BF16 && o_dtype != DIT_F32) return DIT_EUNSUPPORTED;
+  if (D != 128) return DIT_EUNSUPPORTED;
+  if (!size_ok(B, H, Nq, D) || !size_ok(B, H, Nkv, D)) return DIT_ERANGE;
+  if (B == 0 || H == 0 || Nq == 0) return DIT_OK;
+  if (Nkv == 0) return DIT_EINVAL;
+  if (!q || !k || !v || !q_descale || !k_descale || !o) return DIT_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return DIT_EALIGN;
+  if (!aligned(q_descale, 4) || !aligned(k_descale, 4) || (lse && !aligned(lse, 4)))
+    return DIT_EALIGN;
+  return map_launch(ditattn::launch_attn_fp8(q, k, v, q_descale, k_descale, o, lse, B, H, Nq, Nkv,
+                                             scale, o_dtype == DIT_F32,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int ulysses_seq2head(const void* in, void* out, int P, int B, int H, int N, int D, int elem_bytes,
                      void* stream) {
   return permute_common(in, out, P, B, H, N, D, elem_bytes, false, stream);

@@ -66,12 +66,14 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // LDS pointers are 32-bit address-space-3 pointers throughout.
 typedef __attribute__((address_space(3))) char lds_t;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) const u32x4 lds_cu32x4;
 
 constexpr int kWaves = 8;               // two waves per SIMD
 constexpr int kThreads = 64 * kWaves;
@@ -104,6 +106,70 @@ __device__ __forceinline__ int swz_v(int row) {
   constexpr int CPR = D / 8;
   return (2 * (row & 7)) & (CPR - 1);
 }
+
+// The Q.K^T operands.  bf16: K rows of 2D bytes, fragments of 8 channels
+// (v_mfma_f32_16x16x32_bf16, D/32 k-steps).  fp8 (OCP E4M3, D = 128 only):
+// K rows of 128 bytes, one fragment of 32 channels per lane covering all of
+// D in one v_mfma_f32_16x16x128_f8f6f4 (lane group g holds channels
+// 32g .. 32g+31 of its key row in A and of its query column in B: the
+// instruction pairs byte j of lane group g in A with the same byte of the
+// same group in B, checked on gfx950).
+template <int D, bool F8>
+struct QKOps;
+
+template <int D>
+struct QKOps<D, false> {
+  using Frag = bf16x8;
+  static constexpr int KS = D / 32;       // k-steps (fragments per 16-key block)
+  static constexpr int ROWB = D * 2;      // bytes per K row
+  static constexpr int TILE = kBN * ROWB;
+  static constexpr int PIECES = TILE / 1024;
+  __device__ static int swz(int row) { return swz_k<D>(row); }
+  // byte offset of fragment ks within a 16-row block: row c16, chunk 4ks + g
+  __device__ static int frag_off(int c16, int g, int ks) {
+    return c16 * ROWB + (((4 * ks + g) ^ swz(c16)) << 4);
+  }
+  __device__ static Frag load(const lds_t* blk, int off) {
+    return *reinterpret_cast<const lds_bf16x8*>(blk + off);
+  }
+  __device__ static Frag load_q(const void* row, int g, int ks) {
+    return *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(row) + ks * 32 + g * 8);
+  }
+  __device__ static f32x4 mma(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <int D>
+struct QKOps<D, true> {
+  static_assert(D == 128, "fp8 Q.K^T is built for head dim 128");
+  using Frag = i32x8;
+  static constexpr int KS = 1;
+  static constexpr int ROWB = D;
+  static constexpr int TILE = kBN * ROWB;
+  static constexpr int PIECES = TILE / 1024;
+  // The 16 rows read together at one chunk fall in 16 distinct bank slots
+  // (rows 2i and 2i+1 share a 256-byte bank line).
+  __device__ static int swz(int row) { return (row >> 1) & 7; }
+  // first 16 bytes of the lane's 32: row c16, chunk 2g; the second chunk
+  // 2g + 1 sits at (offset ^ 16).
+  __device__ static int frag_off(int c16, int g, int) { return c16 * ROWB + (((2 * g) ^ swz(c16)) << 4); }
+  __device__ static Frag load(const lds_t* blk, int off) {
+    const u32x4 lo = *reinterpret_cast<lds_cu32x4*>(blk + off);
+    const u32x4 hi = *reinterpret_cast<lds_cu32x4*>(blk + (off ^ 16));
+    return Frag{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
+                (int)hi[3]};
+  }
+  __device__ static Frag load_q(const void* row, int g, int) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(row) + 32 * g);
+    const u32x4 lo = p[0], hi = p[1];
+    return Frag{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
+                (int)hi[3]};
+  }
+  __device__ static f32x4 mma(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  }
+};
 
 // Workgroups are dispatched round-robin over the 8 XCDs (id i -> XCD i % 8).
 // Hand each XCD a contiguous range of tiles (a bijection on [0, total)).
@@ -140,14 +206,13 @@ __device__ __forceinline__ void tile_barrier() {
 // 1 KB contiguously (lane i -> bytes [16i, 16i+16)); voff[n] is the byte
 // offset, within a tile, of the global chunk whose swizzled position that
 // is (see piece_offsets).  The keys of one (b, h) lie in segments of kseg
-// rows, sstride elements apart (a single segment unless the keys come from
+// rows, sstride bytes apart (a single segment unless the keys come from
 // Ulysses token shards, whose length is then a multiple of the tile).  The
 // descriptor covers the tile's rows up to the end of its segment, so rows
 // past the end read as zero.
-template <int D>
-__device__ __forceinline__ void stage_tile(const __bf16* __restrict__ G, int k0, int kseg,
+template <int ROWB, int PIECES>
+__device__ __forceinline__ void stage_tile(const char* __restrict__ G, int k0, int kseg,
                                            int64_t sstride, lds_t* buf, int wave, const int* voff) {
-  using Gm = Geo<D>;
   int local = k0;
   if (k0 >= kseg) {
     const int sg = k0 / kseg;
@@ -155,50 +220,52 @@ __device__ __forceinline__ void stage_tile(const __bf16* __restrict__ G, int k0,
     G += sg * sstride;
   }
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(G + (int64_t)local * D), (short)0, (kseg - local) * Gm::ROWB, 0x00020000);
+      (void*)(G + (int64_t)local * ROWB), (short)0, (kseg - local) * ROWB, 0x00020000);
 #pragma unroll
-  for (int n = 0; n < (Gm::PIECES + kWaves - 1) / kWaves; ++n) {
+  for (int n = 0; n < (PIECES + kWaves - 1) / kWaves; ++n) {
     const int inst = n * kWaves + wave;
-    if (Gm::PIECES % kWaves != 0 && inst >= Gm::PIECES) break;
+    if (PIECES % kWaves != 0 && inst >= PIECES) break;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsrc, (__attribute__((address_space(3))) void*)(buf + inst * 1024), 16, voff[n], 0, 0, 0);
   }
 }
 
 // Per-lane source offsets of the wave's load pieces (loop-invariant).
-template <int D, bool IS_V>
-__device__ __forceinline__ void piece_offsets(int* voff, int wave, int lane) {
-  using Gm = Geo<D>;
+template <int ROWB, int PIECES, typename Swz>
+__device__ __forceinline__ void piece_offsets(int* voff, int wave, int lane, Swz swz) {
+  constexpr int CPR = ROWB / 16;
 #pragma unroll
-  for (int n = 0; n < (Gm::PIECES + kWaves - 1) / kWaves; ++n) {
+  for (int n = 0; n < (PIECES + kWaves - 1) / kWaves; ++n) {
     const int p = (n * kWaves + wave) * 64 + lane;
-    const int row = p / Gm::CPR, pc = p % Gm::CPR;
-    const int lc = pc ^ (IS_V ? swz_v<D>(row) : swz_k<D>(row));
-    voff[n] = row * Gm::ROWB + lc * 16;
+    const int row = p / CPR, pc = p % CPR;
+    voff[n] = row * ROWB + (pc ^ swz(row)) * 16;
   }
 }
 
-template <int D>
+template <int D, bool F8>
 struct Frags {
-  f32x4 o[kQB][Geo<D>::DB];   // O^T blocks: lane holds channels 16db+4g+r of its query
-  bf16x8 q[kQB][Geo<D>::KS];  // Q^T operand: lane holds channels 32ks+8g..+7 of its query
+  using QK = QKOps<D, F8>;
+  f32x4 o[kQB][Geo<D>::DB];           // O^T blocks: lane holds channels 16db+4g+r of its query
+  typename QK::Frag q[kQB][QK::KS];   // Q^T operand of the lane's query (bf16: channels 32ks+8g..+7)
   float m[kQB], l[kQB], lb[kQB];
 };
 
 // Everything one pass over the keys needs.
-template <int D>
+template <int D, bool F8>
 struct PassCtx {
-  const __bf16* Kb;  // keys / values of this (b, h): segment 0
-  const __bf16* Vb;
+  using QK = QKOps<D, F8>;
+  const char* Kb;    // keys / values of this (b, h): segment 0
+  const char* Vb;
   int kseg;          // keys per segment (Nkv for contiguous keys)
-  int64_t sstride;   // elements from one segment to the next
+  int64_t kstride;   // bytes from one K segment to the next
+  int64_t vstride;   // bytes from one V segment to the next
   lds_t *k0, *k1, *k2;  // K stages (separate scalars: never an indexed array)
   lds_t *v0, *v1, *v2;  // V stages
   int Nkv, ntiles, wave, lane, g;
   float c;
-  int koff[Geo<D>::KS];  // K fragment (ks) byte offset within a 16-key block
+  int koff[QK::KS];      // K fragment (ks) byte offset within a 16-key block
   int vxb;               // V^T fragment (db) byte offset within a 32-key step = vxb ^ (32 db)
-  int kld[(Geo<D>::PIECES + kWaves - 1) / kWaves];  // K load-piece source offsets
+  int kld[(QK::PIECES + kWaves - 1) / kWaves];      // K load-piece source offsets
   int vld[(Geo<D>::PIECES + kWaves - 1) / kWaves];  // V load-piece source offsets
 };
 
@@ -212,20 +279,21 @@ __device__ __forceinline__ lds_t* stage_of(lds_t* s0, lds_t* s1, lds_t* s2, int 
 
 // S^T of one 32-key step (rows [0, 32) at kst): S[kb][qb] holds keys
 // 16kb + 4g + r for the lane's query of block qb.
-template <int D>
+template <int D, bool F8>
 __device__ __forceinline__ void qk_step(f32x4 (&S)[2][kQB], const lds_t* kst,
-                                        const PassCtx<D>& x, const Frags<D>& f) {
+                                        const PassCtx<D, F8>& x, const Frags<D, F8>& f) {
+  using QK = QKOps<D, F8>;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) S[kb][qb] = f32x4{};
 #pragma unroll
-  for (int ks = 0; ks < Geo<D>::KS; ++ks)
+  for (int ks = 0; ks < QK::KS; ++ks)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 a = *reinterpret_cast<const lds_bf16x8*>(kst + kb * 16 * Geo<D>::ROWB + x.koff[ks]);
+      const typename QK::Frag a = QK::load(kst + kb * 16 * QK::ROWB, x.koff[ks]);
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) S[kb][qb] = mfma16(a, f.q[qb][ks], S[kb][qb]);
+      for (int qb = 0; qb < kQB; ++qb) S[kb][qb] = QK::mma(a, f.q[qb][ks], S[kb][qb]);
     }
 }
 
@@ -258,27 +326,29 @@ __device__ __forceinline__ void rowmax_step(const f32x4 (&S)[2][kQB], float (&m)
 // and issues the LDS reads of the fragments first needed LA groups later.
 // The P^T operand of block qb packs the keys 4g + r (kb 0) and 16 + 4g + r
 // (kb 1): MFMA k index 8g + j <-> key 4g + j (j < 4), 16 + 4g + j - 4 (j >= 4).
-template <int D, bool MASK>
-__device__ __forceinline__ void slot(Frags<D>& f, const f32x4 (&Sc)[2][kQB], f32x4 (&Sn)[2][kQB],
+template <int D, bool F8, bool MASK>
+__device__ __forceinline__ void slot(Frags<D, F8>& f, const f32x4 (&Sc)[2][kQB], f32x4 (&Sn)[2][kQB],
                                      const bf16x8 (&Pp)[kQB], bf16x8 (&Pc)[kQB],
                                      const lds_t* k_next, const lds_t* v_prev,
-                                     const PassCtx<D>& x, int key0) {
+                                     const PassCtx<D, F8>& x, int key0) {
   using Gm = Geo<D>;
+  using QK = QKOps<D, F8>;
   constexpr int NG = 16;                       // groups
-  constexpr int NQK = 2 * kQB * Gm::KS;        // QK^T MFMAs
+  constexpr int NQK = 2 * kQB * QK::KS;        // QK^T MFMAs
   constexpr int NPV = kQB * Gm::DB;            // PV MFMAs
   constexpr int NS = 8 * kQB;                  // softmax scores per lane
-  constexpr int NKF = 2 * Gm::KS;              // K fragments (ks, kb), ks-major
+  constexpr int NKF = 2 * QK::KS;              // K fragments (ks, kb), ks-major
   constexpr int NVF = Gm::DB;                  // V^T fragments (db)
   constexpr int LA = 2;                        // read lookahead, in groups
-  bf16x8 kf[NKF], vf[NVF];
+  typename QK::Frag kf[NKF];
+  bf16x8 vf[NVF];
   // Keep one register for the V^T offsets: hide vxb from loop-invariant code
   // motion so the per-fragment XORs are not hoisted into one register each
   // for the whole loop.
   int vxb = x.vxb;
   asm volatile("" : "+v"(vxb));
   auto load_k = [&](int i) {
-    kf[i] = *reinterpret_cast<const lds_bf16x8*>(k_next + (i & 1) * 16 * Gm::ROWB + x.koff[i >> 1]);
+    kf[i] = QK::load(k_next + (i & 1) * 16 * QK::ROWB, x.koff[i >> 1]);
   };
   auto load_v = [&](int i) {
     const lds_t* base = v_prev + (vxb ^ (32 * i));
@@ -320,7 +390,7 @@ __device__ __forceinline__ void slot(Frags<D>& f, const f32x4 (&Sc)[2][kQB], f32
 #pragma unroll
     for (int i = g * NQK / NG; i < (g + 1) * NQK / NG; ++i) {
       const int ks = i / (2 * kQB), kb = (i / kQB) % 2, qb = i % kQB;
-      Sn[kb][qb] = mfma16(kf[ks * 2 + kb], f.q[qb][ks], Sn[kb][qb]);
+      Sn[kb][qb] = QK::mma(kf[ks * 2 + kb], f.q[qb][ks], Sn[kb][qb]);
     }
 #pragma unroll
     for (int j = g * NPV / NG; j < (g + 1) * NPV / NG; ++j) {
@@ -363,30 +433,33 @@ __device__ __forceinline__ void slot(Frags<D>& f, const f32x4 (&Sc)[2][kQB], f32
 // On entry S0 holds S^T of step 2t and Pa holds P of step 2t-1; on exit S0
 // holds S^T of step 2t+2 (garbage past the last tile, never used) and Pa
 // holds P of step 2t+1.
-template <int D, int PH, bool MASK>
-__device__ __forceinline__ void tile_trip(int t, Frags<D>& f, f32x4 (&S0)[2][kQB], f32x4 (&S1)[2][kQB],
+template <int D, bool F8, int PH, bool MASK>
+__device__ __forceinline__ void tile_trip(int t, Frags<D, F8>& f, f32x4 (&S0)[2][kQB], f32x4 (&S1)[2][kQB],
                                           bf16x8 (&Pa)[kQB], bf16x8 (&Pb)[kQB],
-                                          const PassCtx<D>& x) {
+                                          const PassCtx<D, F8>& x) {
   using Gm = Geo<D>;
+  using QK = QKOps<D, F8>;
   tile_barrier();  // K_{t+1}, V_t landed; every wave is done with tile t-1
   const int p2 = PH >= 0 ? PH + 2 : -1, p1 = PH >= 0 ? PH + 1 : -1;
   if (t + 2 < x.ntiles)
-    stage_tile<D>(x.Kb, (t + 2) * kBN, x.kseg, x.sstride, KSTAGE(x, p2, t + 2), x.wave, x.kld);
+    stage_tile<QK::ROWB, QK::PIECES>(x.Kb, (t + 2) * kBN, x.kseg, x.kstride, KSTAGE(x, p2, t + 2),
+                                     x.wave, x.kld);
   if (t + 1 < x.ntiles)
-    stage_tile<D>(x.Vb, (t + 1) * kBN, x.kseg, x.sstride, VSTAGE(x, p1, t + 1), x.wave, x.vld);
+    stage_tile<Gm::ROWB, Gm::PIECES>(x.Vb, (t + 1) * kBN, x.kseg, x.vstride, VSTAGE(x, p1, t + 1),
+                                     x.wave, x.vld);
   const lds_t* kcur = KSTAGE(x, PH, t);
   const lds_t* knext = KSTAGE(x, p1, t + 1);
   const lds_t* vcur = VSTAGE(x, PH, t);
   const lds_t* vprev = VSTAGE(x, p2, t + 2);  // stage of tile t-1
   const int key0 = t * kBN;
-  slot<D, MASK>(f, S0, S1, Pa, Pb, kcur + 32 * Gm::ROWB, vprev + 32 * Gm::ROWB, x, key0);
-  slot<D, MASK>(f, S1, S0, Pb, Pa, knext, vcur, x, key0 + 32);
+  slot<D, F8, MASK>(f, S0, S1, Pa, Pb, kcur + 32 * QK::ROWB, vprev + 32 * Gm::ROWB, x, key0);
+  slot<D, F8, MASK>(f, S1, S0, Pb, Pa, knext, vcur, x, key0 + 32);
 }
 
 // O^T += V^T P^T for one 32-key step (used once, after the loop).
-template <int D>
-__device__ __forceinline__ void pv_step(Frags<D>& f, const bf16x8 (&P)[kQB], const lds_t* vst,
-                                        const PassCtx<D>& x) {
+template <int D, bool F8>
+__device__ __forceinline__ void pv_step(Frags<D, F8>& f, const bf16x8 (&P)[kQB], const lds_t* vst,
+                                        const PassCtx<D, F8>& x) {
   using Gm = Geo<D>;
 #pragma unroll
   for (int db = 0; db < Gm::DB; ++db) {
@@ -403,22 +476,24 @@ __device__ __forceinline__ void pv_step(Frags<D>& f, const bf16x8 (&P)[kQB], con
 // One full pass over the keys: stage, the unmasked tiles (unrolled by the
 // stage count), the partial last tile (if any) with masking, then the PV of
 // the last step.  Returns true if some row's sum outgrew its reference.
-template <int D>
-__device__ __forceinline__ bool run_pass(Frags<D>& f, const PassCtx<D>& x) {
+template <int D, bool F8>
+__device__ __forceinline__ bool run_pass(Frags<D, F8>& f, const PassCtx<D, F8>& x) {
   using Gm = Geo<D>;
+  using QK = QKOps<D, F8>;
   // The first slot multiplies P = 0 by the V stage of tile -1 (stage 2): zero
   // it so no stale Inf/NaN bit pattern can turn 0 * V into NaN.
   for (int i = threadIdx.x; i < Gm::TILE / 16; i += kThreads)
     reinterpret_cast<lds_u32x4*>(x.v2)[i] = u32x4{0u, 0u, 0u, 0u};
-  stage_tile<D>(x.Kb, 0, x.kseg, x.sstride, x.k0, x.wave, x.kld);
-  if (x.ntiles > 1) stage_tile<D>(x.Kb, kBN, x.kseg, x.sstride, x.k1, x.wave, x.kld);
-  stage_tile<D>(x.Vb, 0, x.kseg, x.sstride, x.v0, x.wave, x.vld);
+  stage_tile<QK::ROWB, QK::PIECES>(x.Kb, 0, x.kseg, x.kstride, x.k0, x.wave, x.kld);
+  if (x.ntiles > 1)
+    stage_tile<QK::ROWB, QK::PIECES>(x.Kb, kBN, x.kseg, x.kstride, x.k1, x.wave, x.kld);
+  stage_tile<Gm::ROWB, Gm::PIECES>(x.Vb, 0, x.kseg, x.vstride, x.v0, x.wave, x.vld);
   f32x4 S0[2][kQB], S1[2][kQB];
   bf16x8 Pa[kQB], Pb[kQB];
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) Pa[qb] = bf16x8{};
   tile_barrier();  // K tile 0 (and K 1, V 0) landed
-  qk_step<D>(S0, x.k0, x, f);
+  qk_step<D, F8>(S0, x.k0, x, f);
   if (f.m[0] == -INFINITY) {  // first attempt: reference max = max of step 0
     float m[kQB];
 #pragma unroll
@@ -434,13 +509,13 @@ __device__ __forceinline__ bool run_pass(Frags<D>& f, const PassCtx<D>& x) {
   const int nfull = partial ? x.ntiles - 1 : x.ntiles;
   int t = 0;
   for (; t + kStages <= nfull; t += kStages) {
-    tile_trip<D, 0, false>(t, f, S0, S1, Pa, Pb, x);
-    tile_trip<D, 1, false>(t + 1, f, S0, S1, Pa, Pb, x);
-    tile_trip<D, 2, false>(t + 2, f, S0, S1, Pa, Pb, x);
+    tile_trip<D, F8, 0, false>(t, f, S0, S1, Pa, Pb, x);
+    tile_trip<D, F8, 1, false>(t + 1, f, S0, S1, Pa, Pb, x);
+    tile_trip<D, F8, 2, false>(t + 2, f, S0, S1, Pa, Pb, x);
   }
-  for (; t < nfull; ++t) tile_trip<D, -1, false>(t, f, S0, S1, Pa, Pb, x);
-  if (partial) tile_trip<D, -1, true>(t, f, S0, S1, Pa, Pb, x);
-  pv_step<D>(f, Pa, VSTAGE(x, -1, x.ntiles - 1) + 32 * Gm::ROWB, x);
+  for (; t < nfull; ++t) tile_trip<D, F8, -1, false>(t, f, S0, S1, Pa, Pb, x);
+  if (partial) tile_trip<D, F8, -1, true>(t, f, S0, S1, Pa, Pb, x);
+  pv_step<D, F8>(f, Pa, VSTAGE(x, -1, x.ntiles - 1) + 32 * Gm::ROWB, x);
   bool flag = false;
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) flag |= !(quad_sum(f.l[qb]) < kMaxSum);
@@ -448,20 +523,20 @@ __device__ __forceinline__ bool run_pass(Frags<D>& f, const PassCtx<D>& x) {
 }
 
 // Exact row max over all keys (only when the fixed-reference loop flagged).
-template <int D>
-__device__ __forceinline__ void exact_max_pass(Frags<D>& f, const PassCtx<D>& x) {
-  using Gm = Geo<D>;
+template <int D, bool F8>
+__device__ __forceinline__ void exact_max_pass(Frags<D, F8>& f, const PassCtx<D, F8>& x) {
+  using QK = QKOps<D, F8>;
   float m[kQB];
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) m[qb] = -INFINITY;
   for (int t = 0; t < x.ntiles; ++t) {
     __syncthreads();  // every wave is done reading the stage
-    stage_tile<D>(x.Kb, t * kBN, x.kseg, x.sstride, x.k0, x.wave, x.kld);
+    stage_tile<QK::ROWB, QK::PIECES>(x.Kb, t * kBN, x.kseg, x.kstride, x.k0, x.wave, x.kld);
     tile_barrier();  // landed
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       f32x4 S[2][kQB];
-      qk_step<D>(S, x.k0 + sub * 32 * Gm::ROWB, x, f);
+      qk_step<D, F8>(S, x.k0 + sub * 32 * QK::ROWB, x, f);
       if (t * kBN + kBN > x.Nkv)
         rowmax_step<true>(S, m, t * kBN + sub * 32, x.Nkv, x.g);
       else
@@ -494,16 +569,22 @@ __device__ __forceinline__ int64_t token_offset(int n, int seg, int64_t head_ele
   return head_elems + sg * sstride + (int64_t)(n - sg * seg) * D;
 }
 
-template <int D, bool OUT_F32>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
-void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                          const __bf16* __restrict__ V, void* __restrict__ Oout,
-                          float* __restrict__ LSE, int Nq, int Nkv, int n_qtiles, int total_tiles,
-                          float c, Layout lay) {
+// The kernel body.  F8: q and k are E4M3 codes (1 byte per element) whose
+// scores are rescaled by the per-(b, h) factors qds[bh] * kds[bh]; else q
+// and k are bf16 and qds, kds are unused.
+template <int D, bool OUT_F32, bool F8>
+__device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const void* __restrict__ K,
+                                              const __bf16* __restrict__ V, void* __restrict__ Oout,
+                                              float* __restrict__ LSE, int Nq, int Nkv,
+                                              int n_qtiles, int total_tiles, float c, Layout lay,
+                                              const float* __restrict__ qds,
+                                              const float* __restrict__ kds) {
   using Gm = Geo<D>;
-  __shared__ __attribute__((aligned(1024))) char k0s[Gm::TILE];
-  __shared__ __attribute__((aligned(1024))) char k1s[Gm::TILE];
-  __shared__ __attribute__((aligned(1024))) char k2s[Gm::TILE];
+  using QK = QKOps<D, F8>;
+  constexpr int QKB = F8 ? 1 : 2;  // bytes per q / k element
+  __shared__ __attribute__((aligned(1024))) char k0s[QK::TILE];
+  __shared__ __attribute__((aligned(1024))) char k1s[QK::TILE];
+  __shared__ __attribute__((aligned(1024))) char k2s[QK::TILE];
   __shared__ __attribute__((aligned(1024))) char v0s[Gm::TILE];
   __shared__ __attribute__((aligned(1024))) char v1s[Gm::TILE];
   __shared__ __attribute__((aligned(1024))) char v2s[Gm::TILE];
@@ -520,11 +601,13 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   const int hh = lay.hoff + (bh - bb * lay.hg);
   const int64_t qhead = ((int64_t)bb * lay.htot + hh) * lay.qseg * D;
   const int64_t qsstride = (int64_t)lay.B * lay.htot * lay.qseg * D;
-  PassCtx<D> x;
-  x.Kb = K + ((int64_t)bb * lay.htot + hh) * lay.kseg * D;
-  x.Vb = V + ((int64_t)bb * lay.htot + hh) * lay.kseg * D;
+  if (F8) c *= qds[bh] * kds[bh];
+  PassCtx<D, F8> x;
+  x.Kb = static_cast<const char*>(K) + ((int64_t)bb * lay.htot + hh) * lay.kseg * D * QKB;
+  x.Vb = reinterpret_cast<const char*>(V + ((int64_t)bb * lay.htot + hh) * lay.kseg * D);
   x.kseg = lay.kseg;
-  x.sstride = (int64_t)lay.B * lay.htot * lay.kseg * D;
+  x.kstride = (int64_t)lay.B * lay.htot * lay.kseg * D * QKB;
+  x.vstride = (int64_t)lay.B * lay.htot * lay.kseg * D * 2;
   x.k0 = (lds_t*)k0s; x.k1 = (lds_t*)k1s; x.k2 = (lds_t*)k2s;
   x.v0 = (lds_t*)v0s; x.v1 = (lds_t*)v1s; x.v2 = (lds_t*)v2s;
   x.Nkv = Nkv;
@@ -533,12 +616,11 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   x.lane = lane;
   x.g = g;
   x.c = c;
-  piece_offsets<D, false>(x.kld, wave, lane);
-  piece_offsets<D, true>(x.vld, wave, lane);
-  // K fragment (ks): row c16 of a 16-key block, chunk 4ks + g.
+  piece_offsets<QK::ROWB, QK::PIECES>(x.kld, wave, lane, [](int r) { return QK::swz(r); });
+  piece_offsets<Gm::ROWB, Gm::PIECES>(x.vld, wave, lane, [](int r) { return swz_v<D>(r); });
+  // K fragment (ks): row c16 of a 16-key block (bf16: chunk 4ks + g).
 #pragma unroll
-  for (int ks = 0; ks < Gm::KS; ++ks)
-    x.koff[ks] = c16 * Gm::ROWB + (((4 * ks + g) ^ swz_k<D>(c16)) << 4);
+  for (int ks = 0; ks < QK::KS; ++ks) x.koff[ks] = QK::frag_off(c16, g, ks);
   // V^T fragment (db), first of two transposing reads: lane t of its 16-lane
   // group g loads row 4g + t/4, channels 16db + 4(t%4) .. +3; the second read
   // is 16 rows further (same swizzle).  Chunk (2db + a) ^ 2(row & 7), a =
@@ -552,15 +634,15 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     x.vxb = row * Gm::ROWB + (((ce0 >> 3) ^ swz_v<D>(row)) << 4) + (ce0 & 7) * 2;
   }
 
-  Frags<D> f;
+  Frags<D, F8> f;
   const int qrow0 = qt * kBM + wave * (16 * kQB) + c16;
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     const int row = min(qrow0 + 16 * qb, Nq - 1);
+    const char* qrow_p =
+        static_cast<const char*>(Q) + token_offset(row, lay.qseg, qhead, qsstride, D) * QKB;
 #pragma unroll
-    for (int ks = 0; ks < Gm::KS; ++ks)
-      f.q[qb][ks] = *reinterpret_cast<const bf16x8*>(
-          Q + token_offset(row, lay.qseg, qhead, qsstride, D) + ks * 32 + g * 8);
+    for (int ks = 0; ks < QK::KS; ++ks) f.q[qb][ks] = QK::load_q(qrow_p, g, ks);
     f.m[qb] = -INFINITY;
     f.l[qb] = 0.f;
     f.lb[qb] = 0.f;
@@ -571,9 +653,9 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   // Second attempt only if some row's sum outgrew its reference max: then
   // redo the tile with the exact row max (all waves decide together).
   for (int attempt = 0;; ++attempt) {
-    const bool flag = run_pass<D>(f, x);
+    const bool flag = run_pass<D, F8>(f, x);
     if (attempt == 1 || !__syncthreads_or(flag)) break;
-    exact_max_pass<D>(f, x);
+    exact_max_pass<D, F8>(f, x);
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
       f.l[qb] = 0.f;
@@ -610,6 +692,27 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
 }
 
 template <int D, bool OUT_F32>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
+void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                          const __bf16* __restrict__ V, void* __restrict__ Oout,
+                          float* __restrict__ LSE, int Nq, int Nkv, int n_qtiles, int total_tiles,
+                          float c, Layout lay) {
+  attn_fwd_body<D, OUT_F32, false>(Q, K, V, Oout, LSE, Nq, Nkv, n_qtiles, total_tiles, c, lay,
+                                   nullptr, nullptr);
+}
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
+void attn_fwd_fp8_kernel(const unsigned char* __restrict__ Q, const unsigned char* __restrict__ K,
+                         const __bf16* __restrict__ V, void* __restrict__ Oout,
+                         float* __restrict__ LSE, int Nq, int Nkv, int n_qtiles, int total_tiles,
+                         float c, Layout lay, const float* __restrict__ qds,
+                         const float* __restrict__ kds) {
+  attn_fwd_body<128, OUT_F32, true>(Q, K, V, Oout, LSE, Nq, Nkv, n_qtiles, total_tiles, c, lay,
+                                    qds, kds);
+}
+
+template <int D, bool OUT_F32>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float* lse, int Nq,
                     int Nkv, float c, const Layout& lay, hipStream_t stream) {
   const int n_qtiles = (Nq + kBM - 1) / kBM;
@@ -618,6 +721,20 @@ hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float*
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OUT_F32>), dim3((unsigned)total), dim3(kThreads), 0,
                      stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                      static_cast<const __bf16*>(v), o, lse, Nq, Nkv, n_qtiles, (int)total, c, lay);
+  return hipGetLastError();
+}
+
+template <bool OUT_F32>
+hipError_t launch_fp8(const void* q, const void* k, const void* v, const float* qds,
+                      const float* kds, void* o, float* lse, int Nq, int Nkv, float c,
+                      const Layout& lay, hipStream_t stream) {
+  const int n_qtiles = (Nq + kBM - 1) / kBM;
+  const int64_t total = (int64_t)lay.B * lay.hg * n_qtiles;
+  if (total > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<OUT_F32>), dim3((unsigned)total), dim3(kThreads), 0,
+                     stream, static_cast<const unsigned char*>(q),
+                     static_cast<const unsigned char*>(k), static_cast<const __bf16*>(v), o, lse,
+                     Nq, Nkv, n_qtiles, (int)total, c, lay, qds, kds);
   return hipGetLastError();
 }
 
@@ -640,6 +757,15 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
   const Layout lay{Nq, Nkv, H, H, 0, B};
   return o_f32 ? launch_layout<true>(q, k, v, o, lse, Nq, Nkv, D, scale, lay, stream)
                : launch_layout<false>(q, k, v, o, lse, Nq, Nkv, D, scale, lay, stream);
+}
+
+hipError_t launch_attn_fp8(const void* q, const void* k, const void* v, const float* q_descale,
+                           const float* k_descale, void* o, float* lse, int B, int H, int Nq,
+                           int Nkv, float scale, bool o_f32, hipStream_t stream) {
+  const Layout lay{Nq, Nkv, H, H, 0, B};
+  const float c = scale * 1.4426950408889634f;
+  return o_f32 ? launch_fp8<true>(q, k, v, q_descale, k_descale, o, lse, Nq, Nkv, c, lay, stream)
+               : launch_fp8<false>(q, k, v, q_descale, k_descale, o, lse, Nq, Nkv, c, lay, stream);
 }
 
 hipError_t launch_attn_bf16_ulysses(const void* q, const void* k, const void* v, void* o,

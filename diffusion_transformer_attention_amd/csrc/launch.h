@@ -18,6 +18,16 @@ hipError_t launch_attn_bf16_ulysses(const void* q, const void* k, const void* v,
                                     float* lse, int P, int r, int B, int H, int N, int D,
                                     float scale, hipStream_t stream);
 
+// q, k: E4M3 codes [B,H,N,D] (D = 128) with per-(b, h) float32 descales;
+// v bf16; o bf16 (o_f32 == false) or float32; lse may be null.
+hipError_t launch_attn_fp8(const void* q, const void* k, const void* v, const float* q_descale,
+                           const float* k_descale, void* o, float* lse, int B, int H, int Nq,
+                           int Nkv, float scale, bool o_f32, hipStream_t stream);
+
+// bf16 x [B,H,N,D] -> E4M3 codes [B,H,N,D] and float32 descale [B,H] (D % 8 == 0).
+hipError_t launch_quant_fp8(const void* x, void* codes, float* descale, int B, int H, int N, int D,
+                            hipStream_t stream);
+
 // Backward, bf16 q/k/v/o/dout (head dim 128), float32 lse in, delta out
 // ([B,H,Nq]), float32 dq/dk/dv.
 hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,

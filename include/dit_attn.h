@@ -15,6 +15,9 @@
  *         "Limitations" (everything outside the envelope fails loudly: head
  *         count divisible by the Ulysses degree, sequence length divisible by
  *         the SP degree, no mask / dropout / causal flag under SP).
+ *   [HC]  [HB] section "Combining: what xDiT does": FP8 low precision is the
+ *         last step of the latency ladder, on top of the parallel split and
+ *         caching (the pages do not say which tensors are 8-bit).
  *   [VO]  "Parallelism Acceleration Guide" (vLLM-Omni docs), section "How
  *         to parallelize a new model": a dual-stream (text + image) model
  *         runs joint attention over the concatenated sequences; the text
@@ -220,6 +223,44 @@ int dit_attn_fwd_joint(const void* q_txt, const void* k_txt, const void* v_txt,
                        const float* cos_txt, const float* sin_txt, const float* cos_img,
                        const float* sin_img, void* workspace, void* o, float* lse, int B, int H,
                        int Ht, int h0, int Nt, int Ni, int D, float scale, void* stream);
+
+/*
+ * Per-(b, h) quantization to 8-bit floating point for dit_attn_fwd_fp8 ([HC];
+ * format and scaling are this library's reading: OCP E4M3 -- 1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits, subnormals, largest finite
+ * 448, no infinities):
+ *
+ *   descale[b,h] = amax / 448 in float32 (correctly rounded), amax = max |x|
+ *                  over the head; 1 for an all-zero (or empty) head
+ *   code         = E4M3 of the float32 quotient x / descale (correctly
+ *                  rounded), clamped to +-448, rounded to nearest-even
+ *
+ *   x       : bf16 [B,H,N,D]
+ *   codes   : uint8 [B,H,N,D] E4M3 codes (written), 8-byte aligned
+ *   descale : float32 [B,H] (written)
+ * Deterministic (the max is exact).  NaN inputs get no special handling.
+ */
+int dit_quant_fp8(const void* x, void* codes, float* descale, int B, int H, int N, int D,
+                  void* stream);
+
+/*
+ * FP8 attention ([HC], reading as above): scores from E4M3 queries and keys,
+ *
+ *   s_ij = scale * q_descale[b,h] * k_descale[b,h] * (q_i . k_j)   (codes decoded)
+ *
+ * then the softmax, O and LSE of dit_attn_fwd_block with P and V in bf16.
+ * The products q_i . k_j run on the fp8 matrix cores
+ * (v_mfma_f32_16x16x128_f8f6f4) with float32 accumulation.
+ *
+ *   q       : uint8 [B,H,Nq,D] E4M3 codes;  k : uint8 [B,H,Nkv,D] E4M3 codes
+ *   v       : bf16 [B,H,Nkv,D];  q_descale, k_descale : float32 [B,H]
+ *   o       : [B,H,Nq,D] in o_dtype (DIT_BF16 or DIT_F32)
+ *   lse     : float32 [B,H,Nq] (natural log, all factors included), or NULL
+ *   D must be 128.  Nkv >= 1 unless B, H or Nq is 0 (no-op).
+ */
+int dit_attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
+                     const float* k_descale, void* o, float* lse, int B, int H, int Nq, int Nkv,
+                     int D, float scale, int o_dtype, void* stream);
 
 /*
  * Ulysses sequence -> head exchange as it lands on one device ([HB] Ulysses

@@ -168,6 +168,37 @@ def test_joint_validation(lib):
     assert j(Nt=0, Ni=0) == dta.DIT_OK
 
 
+def test_quant_fp8_validation(lib):
+    def qz(x=A, c=A, ds=A, B=1, H=2, N=64, D=128):
+        return lib.dit_quant_fp8(x, c, ds, B, H, N, D, S)
+    assert qz(D=96) == dta.DIT_EUNSUPPORTED
+    assert qz(ds=NULL) == dta.DIT_EINVAL
+    assert qz(x=NULL) == dta.DIT_EINVAL
+    assert qz(c=NULL) == dta.DIT_EINVAL
+    assert qz(c=V(0x10004)) == dta.DIT_EALIGN    # codes need 8-byte alignment
+    assert qz(x=MIS) == dta.DIT_EALIGN
+    assert qz(ds=V(0x10002)) == dta.DIT_EALIGN
+    assert qz(N=-1) == dta.DIT_EINVAL
+    assert qz(B=0) == dta.DIT_OK
+    assert qz(B=2 ** 20, H=2 ** 12, N=1, D=32) == dta.DIT_ERANGE
+
+
+def test_attn_fp8_validation(lib):
+    def f(q=A, qd=A, kd=A, o=A, lse=A, Nq=64, Nkv=64, D=128, scale=0.125, od=0):
+        return lib.dit_attn_fwd_fp8(q, A, A, qd, kd, o, lse, 1, 2, Nq, Nkv, D,
+                                    ctypes.c_float(scale), od, S)
+    assert f(D=64) == dta.DIT_EUNSUPPORTED
+    assert f(od=5) == dta.DIT_EUNSUPPORTED
+    assert f(qd=NULL) == dta.DIT_EINVAL
+    assert f(kd=NULL) == dta.DIT_EINVAL
+    assert f(Nkv=0) == dta.DIT_EINVAL
+    assert f(scale=-1.0) == dta.DIT_EINVAL
+    assert f(q=MIS) == dta.DIT_EALIGN
+    assert f(kd=V(0x10002)) == dta.DIT_EALIGN
+    assert f(lse=V(0x10002)) == dta.DIT_EALIGN
+    assert f(Nq=0) == dta.DIT_OK
+
+
 @pytest.mark.parametrize("fn", ["ulysses_seq2head", "ulysses_head2seq"])
 def test_permute_validation(lib, fn):
     f = getattr(lib, fn)
