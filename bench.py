@@ -1,6 +1,7 @@
 """Benchmark of the DiT sequence-parallel attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-ring]
+                    [--no-legs]
 
 One step is the Ulysses round trip of one P=4 sequence-parallel attention
 layer of a Wan-shaped tensor [1,40,32768,128] bf16, run on one GPU:
@@ -89,6 +90,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ring", action="store_true")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the fused, backward, joint, cross and fp8 legs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
@@ -212,80 +215,81 @@ def main():
             "seq2head_ms": s2h_ms, "seq2head_GBps": perm_bytes / (s2h_ms * 1e-3) / 1e9,
             "head2seq_ms": h2s_ms, "head2seq_GBps": perm_bytes / (h2s_ms * 1e-3) / 1e9}
 
-    # fused leg: the same step with dit_attn_fwd_ulysses reading the shards
-    # and writing the token-shard output directly (no exchange buffers)
-    print("[bench] fused Ulysses leg", file=sys.stderr, flush=True)
-    fused_out = torch.empty_like(back)
+    if not args.no_legs:
+        # fused leg: the same step with dit_attn_fwd_ulysses reading the shards
+        # and writing the token-shard output directly (no exchange buffers)
+        print("[bench] fused Ulysses leg", file=sys.stderr, flush=True)
+        fused_out = torch.empty_like(back)
 
-    def fused_step():
-        for r in range(P):
-            dta.dit_attn_fwd_ulysses(*shards, r, out=fused_out, lse=lses[r])
+        def fused_step():
+            for r in range(P):
+                dta.dit_attn_fwd_ulysses(*shards, r, out=fused_out, lse=lses[r])
 
-    fused_ms = time_it(fused_step, reps=3)
-    legs.update({"fused_step_ms": fused_ms,
-                 "fused_step_TFLOPs": P * flops_launch / (fused_ms * 1e-3) / 1e12,
-                 "unfused_step_ms": ms_per_step})
+        fused_ms = time_it(fused_step, reps=3)
+        legs.update({"fused_step_ms": fused_ms,
+                     "fused_step_TFLOPs": P * flops_launch / (fused_ms * 1e-3) / 1e12,
+                     "unfused_step_ms": ms_per_step})
 
-    # backward leg: dit_attn_bwd on the same head group (the forward's O and
-    # LSE, a seeded dO); algorithmic FLOPs of the five products 10*B*H*N^2*D.
-    print("[bench] backward leg", file=sys.stderr, flush=True)
-    dout = torch.empty_like(outs[0]).normal_(generator=torch.Generator(device=dev).manual_seed(5))
-    g_dq = torch.empty((B, H, N, D), device=dev, dtype=torch.float32)
-    g_dk, g_dv = torch.empty_like(g_dq), torch.empty_like(g_dq)
-    g_delta = torch.empty((B, H, N), device=dev, dtype=torch.float32)
-    bwd_ms = time_it(lambda: dta.dit_attn_bwd(groups[0][0], groups[1][0], groups[2][0], outs[0], dout,
-                                              lses[0], dq=g_dq, dk=g_dk, dv=g_dv, delta=g_delta),
-                     reps=3)
-    legs.update({"bwd_ms": bwd_ms,
-                 "bwd_TFLOPs": 2.5 * flops_launch / (bwd_ms * 1e-3) / 1e12,
-                 "fwd_plus_bwd_ms": attn_avg_ms + bwd_ms})
-    del g_dq, g_dk, g_dv, dout
+        # backward leg: dit_attn_bwd on the same head group (the forward's O and
+        # LSE, a seeded dO); algorithmic FLOPs of the five products 10*B*H*N^2*D.
+        print("[bench] backward leg", file=sys.stderr, flush=True)
+        dout = torch.empty_like(outs[0]).normal_(generator=torch.Generator(device=dev).manual_seed(5))
+        g_dq = torch.empty((B, H, N, D), device=dev, dtype=torch.float32)
+        g_dk, g_dv = torch.empty_like(g_dq), torch.empty_like(g_dq)
+        g_delta = torch.empty((B, H, N), device=dev, dtype=torch.float32)
+        bwd_ms = time_it(lambda: dta.dit_attn_bwd(groups[0][0], groups[1][0], groups[2][0], outs[0], dout,
+                                                  lses[0], dq=g_dq, dk=g_dk, dv=g_dv, delta=g_delta),
+                         reps=3)
+        legs.update({"bwd_ms": bwd_ms,
+                     "bwd_TFLOPs": 2.5 * flops_launch / (bwd_ms * 1e-3) / 1e12,
+                     "fwd_plus_bwd_ms": attn_avg_ms + bwd_ms})
+        del g_dq, g_dk, g_dv, dout
 
-    # joint leg: 512 text + 4096 image tokens (1024x1024 picture, 64x64
-    # patches), 24 heads of 128, RoPE on q and k: dit_attn_fwd_joint (one
-    # pack launch + the attention) and the attention alone on the packed
-    # buffers; FLOPs 4*B*H*N^2*D over the N = 4608 joint tokens.
-    print("[bench] joint text+image leg", file=sys.stderr, flush=True)
-    jt, ji = datagen.joint_bf16(1, 24, 512, 24, 4096, D, seed=31)
-    jt, ji = [to_dev(x) for x in jt], [to_dev(x) for x in ji]
-    tabs = [torch.from_numpy(x).to(dev) for x in
-            (*datagen.rope_tables_text(512, 64, 64, D), *datagen.rope_tables_image(64, 64, D))]
-    jws = torch.empty((3, 1, 24, 4608, D), device=dev, dtype=torch.bfloat16)
-    jo = torch.empty((1, 24, 4608, D), device=dev, dtype=torch.bfloat16)
-    jl = torch.empty((1, 24, 4608), device=dev, dtype=torch.float32)
-    joint_ms = time_it(lambda: dta.dit_attn_fwd_joint(*jt, *ji, *tabs, workspace=jws, out=jo,
-                                                      lse=jl), reps=20)
-    jattn_ms = time_it(lambda: dta.dit_attn_fwd(jws[0], jws[1], jws[2], out=jo, lse=jl), reps=20)
-    jflops = attn_flops(1, 24, 4608, 4608, D)
-    legs.update({"joint_ms": joint_ms, "joint_TFLOPs": jflops / (joint_ms * 1e-3) / 1e12,
-                 "joint_attn_only_ms": jattn_ms, "joint_pack_ms": joint_ms - jattn_ms})
-    del jt, ji, jws, jo
+        # joint leg: 512 text + 4096 image tokens (1024x1024 picture, 64x64
+        # patches), 24 heads of 128, RoPE on q and k: dit_attn_fwd_joint (one
+        # pack launch + the attention) and the attention alone on the packed
+        # buffers; FLOPs 4*B*H*N^2*D over the N = 4608 joint tokens.
+        print("[bench] joint text+image leg", file=sys.stderr, flush=True)
+        jt, ji = datagen.joint_bf16(1, 24, 512, 24, 4096, D, seed=31)
+        jt, ji = [to_dev(x) for x in jt], [to_dev(x) for x in ji]
+        tabs = [torch.from_numpy(x).to(dev) for x in
+                (*datagen.rope_tables_text(512, 64, 64, D), *datagen.rope_tables_image(64, 64, D))]
+        jws = torch.empty((3, 1, 24, 4608, D), device=dev, dtype=torch.bfloat16)
+        jo = torch.empty((1, 24, 4608, D), device=dev, dtype=torch.bfloat16)
+        jl = torch.empty((1, 24, 4608), device=dev, dtype=torch.float32)
+        joint_ms = time_it(lambda: dta.dit_attn_fwd_joint(*jt, *ji, *tabs, workspace=jws, out=jo,
+                                                          lse=jl), reps=20)
+        jattn_ms = time_it(lambda: dta.dit_attn_fwd(jws[0], jws[1], jws[2], out=jo, lse=jl), reps=20)
+        jflops = attn_flops(1, 24, 4608, 4608, D)
+        legs.update({"joint_ms": joint_ms, "joint_TFLOPs": jflops / (joint_ms * 1e-3) / 1e12,
+                     "joint_attn_only_ms": jattn_ms, "joint_pack_ms": joint_ms - jattn_ms})
+        del jt, ji, jws, jo
 
-    # cross leg: the 10-head share's 32768 image queries over 512 text keys
-    # and values (dit_attn_fwd_block, bf16 out).
-    print("[bench] cross attention leg", file=sys.stderr, flush=True)
-    _, ck, cv = (to_dev(x) for x in datagen.small_bf16(1, H, 1, D, seed=51, Nkv=512))
-    co = torch.empty((B, H, N, D), device=dev, dtype=torch.bfloat16)
-    cl = torch.empty((B, H, N), device=dev, dtype=torch.float32)
-    cross_ms = time_it(lambda: dta.dit_attn_fwd_block(groups[0][0], ck, cv, out=co, lse=cl), reps=20)
-    legs.update({"cross_ms": cross_ms,
-                 "cross_TFLOPs": attn_flops(B, H, N, 512, D) / (cross_ms * 1e-3) / 1e12})
-    del co, cl
+        # cross leg: the 10-head share's 32768 image queries over 512 text keys
+        # and values (dit_attn_fwd_block, bf16 out).
+        print("[bench] cross attention leg", file=sys.stderr, flush=True)
+        _, ck, cv = (to_dev(x) for x in datagen.small_bf16(1, H, 1, D, seed=51, Nkv=512))
+        co = torch.empty((B, H, N, D), device=dev, dtype=torch.bfloat16)
+        cl = torch.empty((B, H, N), device=dev, dtype=torch.float32)
+        cross_ms = time_it(lambda: dta.dit_attn_fwd_block(groups[0][0], ck, cv, out=co, lse=cl), reps=20)
+        legs.update({"cross_ms": cross_ms,
+                     "cross_TFLOPs": attn_flops(B, H, N, 512, D) / (cross_ms * 1e-3) / 1e12})
+        del co, cl
 
-    # fp8 leg: the same 10-head share with q and k quantized per head to
-    # E4M3 (dit_quant_fp8, timed for both tensors) and the fp8 attention.
-    print("[bench] fp8 leg", file=sys.stderr, flush=True)
-    q0, k0, v0 = groups[0][0], groups[1][0], groups[2][0]
-    qc, qd = dta.dit_quant_fp8(q0)
-    kc, kd = dta.dit_quant_fp8(k0)
-    fo, fl = torch.empty_like(outs[0]), torch.empty_like(lses[0])
-    quant_ms = time_it(lambda: (dta.dit_quant_fp8(q0, qc, qd), dta.dit_quant_fp8(k0, kc, kd)),
-                       reps=10)
-    fp8_ms = time_it(lambda: dta.dit_attn_fwd_fp8(qc, kc, v0, qd, kd, out=fo, lse=fl), reps=5)
-    legs.update({"fp8_attn_ms": fp8_ms,
-                 "fp8_attn_TFLOPs": flops_launch / (fp8_ms * 1e-3) / 1e12,
-                 "fp8_quant_qk_ms": quant_ms})
-    del qc, kc, fo, fl
+        # fp8 leg: the same 10-head share with q and k quantized per head to
+        # E4M3 (dit_quant_fp8, timed for both tensors) and the fp8 attention.
+        print("[bench] fp8 leg", file=sys.stderr, flush=True)
+        q0, k0, v0 = groups[0][0], groups[1][0], groups[2][0]
+        qc, qd = dta.dit_quant_fp8(q0)
+        kc, kd = dta.dit_quant_fp8(k0)
+        fo, fl = torch.empty_like(outs[0]), torch.empty_like(lses[0])
+        quant_ms = time_it(lambda: (dta.dit_quant_fp8(q0, qc, qd), dta.dit_quant_fp8(k0, kc, kd)),
+                           reps=10)
+        fp8_ms = time_it(lambda: dta.dit_attn_fwd_fp8(qc, kc, v0, qd, kd, out=fo, lse=fl), reps=5)
+        legs.update({"fp8_attn_ms": fp8_ms,
+                     "fp8_attn_TFLOPs": flops_launch / (fp8_ms * 1e-3) / 1e12,
+                     "fp8_quant_qk_ms": quant_ms})
+        del qc, kc, fo, fl
 
     if not args.no_ring:
         print("[bench] ring leg", file=sys.stderr, flush=True)
