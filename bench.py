@@ -125,8 +125,10 @@ def cpu_baseline(qb, kb, vb, target_s):
                 list(ex.map(one, tasks))
             return time.perf_counter() - t0
 
-    probe = run(64)                      # 64 rows per head: calibrates the sample size
-    rows_per_head = int(min(N, max(64, 64 * round(target_s / max(probe, 1e-3)))))
+    # 256 rows per head (40 tasks, enough to keep every worker busy) calibrate
+    # the sample size
+    probe = run(256)
+    rows_per_head = int(min(N, max(256, 256 * target_s / max(probe, 1e-3))))
     rows_per_head = 64 * max(1, rows_per_head // 64)
     dt = run(rows_per_head)
     flops = attn_flops(1, H, rows_per_head, N, D)

@@ -7,10 +7,10 @@
 //                  head), amax = max |x| over the head
 //   code         = E4M3(clamp(x / descale, -448, 448)), the quotient correctly
 //                  rounded in float32, the conversion round-to-nearest-even
-// Three launches: zero the descale buffer, which then holds amax as float
+// Four launches: zero the descale buffer, which then holds amax as float
 // bits (a non-negative float orders like its bit pattern, so an unsigned
 // atomic max is exact and order-independent); one pass for amax; one pass
-// writing the codes and, last, the descales.  HBM-bound: x is read twice and
+// writing the codes; last, amax -> descale in place.  HBM-bound: x is read twice and
 // the codes written once (5 bytes per element).
 #include "launch.h"
 
@@ -29,7 +29,10 @@ __global__ void zero_kernel(float* __restrict__ p, int n) {
   if (i < n) p[i] = 0.0f;
 }
 
-// Block b handles head b / bph, vectors [chunk * kVec * kThreads, ...) of it.
+// Block b handles head b / bph and strides over it, so a head takes at most
+// kAmaxBlocks atomics (thousands of atomics on one address serialize at L2).
+constexpr int kAmaxBlocks = 64;
+
 __global__ __launch_bounds__(kThreads) void amax_kernel(const u32x4* __restrict__ x,
                                                        unsigned* __restrict__ amax,
                                                        int64_t vec_per_head, int bph) {
@@ -37,15 +40,18 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const u32x4* __restrict_
   const int chunk = blockIdx.x - bh * bph;
   const u32x4* src = x + (int64_t)bh * vec_per_head;
   float m = 0.0f;
+  const int64_t step = (int64_t)bph * kVec * kThreads;
+  for (int64_t base = (int64_t)chunk * kVec * kThreads; base < vec_per_head; base += step) {
 #pragma unroll
-  for (int u = 0; u < kVec; ++u) {
-    const int64_t i = ((int64_t)chunk * kVec + u) * kThreads + threadIdx.x;
-    if (i < vec_per_head) {
-      const u32x4 v = src[i];
+    for (int u = 0; u < kVec; ++u) {
+      const int64_t i = base + u * kThreads + threadIdx.x;
+      if (i < vec_per_head) {
+        const u32x4 v = src[i];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        m = fmaxf(m, __uint_as_float((v[w] & 0x7fffu) << 16));
-        m = fmaxf(m, __uint_as_float(v[w] & 0x7fff0000u));
+        for (int w = 0; w < 4; ++w) {
+          m = fmaxf(m, __uint_as_float((v[w] & 0x7fffu) << 16));
+          m = fmaxf(m, __uint_as_float(v[w] & 0x7fff0000u));
+        }
       }
     }
   }
@@ -117,9 +123,10 @@ hipError_t launch_quant_fp8(const void* x, void* codes, float* descale, int B, i
   const unsigned small = (unsigned)((nbh + kThreads - 1) / kThreads);
   hipLaunchKernelGGL(zero_kernel, dim3(small), dim3(kThreads), 0, stream, descale, nbh);
   if (bph > 0) {  // N == 0: every head is empty, amax stays 0 and descale becomes 1
-    hipLaunchKernelGGL(amax_kernel, dim3((unsigned)(bph * nbh)), dim3(kThreads), 0, stream,
+    const int64_t abph = bph < kAmaxBlocks ? bph : kAmaxBlocks;
+    hipLaunchKernelGGL(amax_kernel, dim3((unsigned)(abph * nbh)), dim3(kThreads), 0, stream,
                        static_cast<const u32x4*>(x), reinterpret_cast<unsigned*>(descale),
-                       vec_per_head, (int)bph);
+                       vec_per_head, (int)abph);
     hipLaunchKernelGGL(quant_kernel, dim3((unsigned)(bph * nbh)), dim3(kThreads), 0, stream,
                        static_cast<const u32x4*>(x), static_cast<u32x2*>(codes),
                        reinterpret_cast<const unsigned*>(descale), vec_per_head, (int)bph);
