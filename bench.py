@@ -25,7 +25,9 @@ attention alone; the cross leg times dit_attn_fwd_block of the 10-head share's
 32768 queries over 512 text keys.
 
 The fp8 leg quantizes the share's q and k per head to E4M3 (dit_quant_fp8)
-and times dit_attn_fwd_fp8 on them (same FLOP count as the bf16 launch).
+and times dit_attn_fwd_fp8 on them (same FLOP count as the bf16 launch).  Two
+more bf16 forward legs: all 40 heads of the draw in one call, and the
+[1,10,75600,128] long-video shape.
 
 The ring leg (K/V in 4 blocks of 8192: four dit_attn_fwd_block calls with
 float32 partials, then dit_attn_merge, B1 H40 N32768 D128) is timed after the
@@ -91,7 +93,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ring", action="store_true")
     ap.add_argument("--no-legs", action="store_true",
-                    help="skip the fused, backward, joint, cross and fp8 legs")
+                    help="skip the fused, backward, joint, cross, fp8, H40 and long-video legs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
@@ -292,6 +294,28 @@ def main():
                      "fp8_attn_TFLOPs": flops_launch / (fp8_ms * 1e-3) / 1e12,
                      "fp8_quant_qk_ms": quant_ms})
         del qc, kc, fo, fl
+
+        # single-pass ring-merge shape: all 40 heads of the [1,40,32768,128]
+        # draw in one dit_attn_fwd (the full head count the ring blocks cover)
+        print("[bench] single-pass H40 leg", file=sys.stderr, flush=True)
+        so = torch.empty_like(full[0])
+        sl = torch.empty((B, H_FULL, N), device=dev, dtype=torch.float32)
+        sp_ms = time_it(lambda: dta.dit_attn_fwd(full[0], full[1], full[2], out=so, lse=sl), reps=3)
+        legs.update({"single_pass_h40_ms": sp_ms,
+                     "single_pass_h40_TFLOPs": attn_flops(B, H_FULL, N, N, D) / (sp_ms * 1e-3) / 1e12})
+        del so, sl
+
+        # long video: the 21x45x80 latent grid of a Wan 720p 81-frame clip,
+        # [1,10,75600,128] (N not a multiple of the 256-row query tile)
+        print("[bench] long video leg", file=sys.stderr, flush=True)
+        lv = [to_dev(x) for x in datagen.workload_inputs("long_video")]
+        lo = torch.empty_like(lv[0])
+        ll = torch.empty(lv[0].shape[:3], device=dev, dtype=torch.float32)
+        lv_ms = time_it(lambda: dta.dit_attn_fwd(lv[0], lv[1], lv[2], out=lo, lse=ll), reps=3)
+        nlv = lv[0].shape[2]
+        legs.update({"long_video_ms": lv_ms,
+                     "long_video_TFLOPs": attn_flops(1, 10, nlv, nlv, D) / (lv_ms * 1e-3) / 1e12})
+        del lv, lo, ll
 
     if not args.no_ring:
         print("[bench] ring leg", file=sys.stderr, flush=True)
