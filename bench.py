@@ -218,6 +218,13 @@ def main():
     legs = {"attn_fwd_ms_avg": attn_avg_ms, "attn_fwd_ms_min": float(np.min(attn_ms)),
             "seq2head_ms": s2h_ms, "seq2head_GBps": perm_bytes / (s2h_ms * 1e-3) / 1e9,
             "head2seq_ms": h2s_ms, "head2seq_GBps": perm_bytes / (h2s_ms * 1e-3) / 1e9}
+    # practical ceiling of the HBM-bound kernels: a plain 1 GiB device-to-device
+    # copy (2 GiB moved per copy; larger than the 256 MB Infinity Cache)
+    csrc = torch.empty(1 << 30, device=dev, dtype=torch.uint8)
+    cdst = torch.empty_like(csrc)
+    copy_ms = time_it(lambda: cdst.copy_(csrc), reps=5)
+    legs.update({"copy_1GiB_ms": copy_ms, "copy_GBps": 2.0 * (1 << 30) / (copy_ms * 1e-3) / 1e9})
+    del csrc, cdst
 
     if not args.no_legs:
         # fused leg: the same step with dit_attn_fwd_ulysses reading the shards
