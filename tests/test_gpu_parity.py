@@ -179,7 +179,9 @@ def test_uniform_v_returns_v():
 
 
 # ------------------------------------------------------------ merge
-@pytest.mark.parametrize("nblk,out", [(1, "f32"), (3, "f32"), (4, "bf16"), (2, "bf16")])
+@pytest.mark.parametrize("nblk,out", [(1, "f32"), (3, "f32"), (4, "bf16"), (2, "bf16"),
+                                      (8, "f32"),   # the largest compile-time block count
+                                      (11, "f32")])  # the runtime-count path
 def test_merge_against_oracle(nblk, out):
     say("merge", nblk, out)
     rng = np.random.default_rng(nblk)
