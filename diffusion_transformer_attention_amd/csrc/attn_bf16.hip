@@ -265,8 +265,15 @@ struct PassCtx {
   lds_t *v0, *v1, *v2;  // V stages
   int Nkv, ntiles, wave, lane, g;
   float c;
-  int koff[QK::KS];      // K fragment (ks) byte offset within a 16-key block
-  int vxb;               // V^T fragment (db) byte offset within a 32-key step = vxb ^ (32 db)
+  // Fragment offsets, each plus the LDS address of stage 0 and held in a
+  // register the compiler cannot see through: a read of stage j is then
+  // that register plus the constant (stage j - stage 0 + in-tile offset),
+  // which the instruction encodes, so the key loop does no address
+  // arithmetic (and the reads keep the stage array as their object, so the
+  // compiler still knows they do not touch the stage being loaded).
+  int kof[QK::KS];       // K fragment (ks): byte offset within a 16-key block + kbase
+  int vxo[Geo<D>::DB];   // V^T fragment (db): byte offset within a 32-key step + vbase
+  int kbase, vbase;      // LDS addresses of the stages k0 and v0
   int kld[(QK::PIECES + kWaves - 1) / kWaves];      // K load-piece source offsets
   int vld[(Geo<D>::PIECES + kWaves - 1) / kWaves];  // V load-piece source offsets
 };
@@ -293,7 +300,7 @@ __device__ __forceinline__ void qk_step(f32x4 (&S)[2][kQB], const lds_t* kst,
   for (int ks = 0; ks < QK::KS; ++ks)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const typename QK::Frag a = QK::load(kst + kb * 16 * QK::ROWB, x.koff[ks]);
+      const typename QK::Frag a = QK::load(kst - x.kbase + kb * 16 * QK::ROWB, x.kof[ks]);
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) S[kb][qb] = QK::mma(a, f.q[qb][ks], S[kb][qb]);
     }
@@ -344,16 +351,11 @@ __device__ __forceinline__ void slot(Frags<D, F8>& f, const f32x4 (&Sc)[2][kQB],
   constexpr int LA = 2;                        // read lookahead, in groups
   typename QK::Frag kf[NKF];
   bf16x8 vf[NVF];
-  // Keep one register for the V^T offsets: hide vxb from loop-invariant code
-  // motion so the per-fragment XORs are not hoisted into one register each
-  // for the whole loop.
-  int vxb = x.vxb;
-  asm volatile("" : "+v"(vxb));
   auto load_k = [&](int i) {
-    kf[i] = QK::load(k_next + (i & 1) * 16 * QK::ROWB, x.koff[i >> 1]);
+    kf[i] = QK::load(k_next - x.kbase + (i & 1) * 16 * QK::ROWB, x.kof[i >> 1]);
   };
   auto load_v = [&](int i) {
-    const lds_t* base = v_prev + (vxb ^ (32 * i));
+    const lds_t* base = v_prev - x.vbase + x.vxo[i];
     const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)base));
     const bf16x4 hi = __builtin_bit_cast(
         bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 16 * Gm::ROWB)));
@@ -465,7 +467,7 @@ __device__ __forceinline__ void pv_step(Frags<D, F8>& f, const bf16x8 (&P)[kQB],
   using Gm = Geo<D>;
 #pragma unroll
   for (int db = 0; db < Gm::DB; ++db) {
-    const lds_t* base = vst + (x.vxb ^ (32 * db));
+    const lds_t* base = vst - x.vbase + x.vxo[db];
     const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)base));
     const bf16x4 hi = __builtin_bit_cast(
         bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 16 * Gm::ROWB)));
@@ -621,19 +623,28 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
   piece_offsets<QK::ROWB, QK::PIECES>(x.kld, wave, lane, [](int r) { return QK::swz(r); });
   piece_offsets<Gm::ROWB, Gm::PIECES>(x.vld, wave, lane, [](int r) { return swz_v<D>(r); });
   // K fragment (ks): row c16 of a 16-key block (bf16: chunk 4ks + g).
+  x.kbase = (int)(size_t)x.k0;
+  x.vbase = (int)(size_t)x.v0;
 #pragma unroll
-  for (int ks = 0; ks < QK::KS; ++ks) x.koff[ks] = QK::frag_off(c16, g, ks);
+  for (int ks = 0; ks < QK::KS; ++ks) {
+    x.kof[ks] = QK::frag_off(c16, g, ks) + x.kbase;
+    asm volatile("" : "+v"(x.kof[ks]));
+  }
   // V^T fragment (db), first of two transposing reads: lane t of its 16-lane
   // group g loads row 4g + t/4, channels 16db + 4(t%4) .. +3; the second read
   // is 16 rows further (same swizzle).  Chunk (2db + a) ^ 2(row & 7), a =
   // (t%4)/2, sits at bytes 32 (db ^ (row & 7)) + 16a of the row, and the
   // row, the 16a and the in-chunk offsets occupy bits disjoint from 32 db, so
-  // the offset of fragment db is vxb ^ (32 db) (checked against the direct
-  // formula below for every db).
+  // the offset of fragment db is vxb ^ (32 db).
   {
     const int row = 4 * g + (c16 >> 2);
     const int ce0 = 4 * (c16 & 3);
-    x.vxb = row * Gm::ROWB + (((ce0 >> 3) ^ swz_v<D>(row)) << 4) + (ce0 & 7) * 2;
+    const int vxb = row * Gm::ROWB + (((ce0 >> 3) ^ swz_v<D>(row)) << 4) + (ce0 & 7) * 2;
+#pragma unroll
+    for (int db = 0; db < Gm::DB; ++db) {
+      x.vxo[db] = (vxb ^ (32 * db)) + x.vbase;
+      asm volatile("" : "+v"(x.vxo[db]));
+    }
   }
 
   Frags<D, F8> f;
