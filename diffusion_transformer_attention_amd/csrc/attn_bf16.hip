@@ -348,7 +348,7 @@ __device__ __forceinline__ void slot(Frags<D, F8>& f, const f32x4 (&Sc)[2][kQB],
   constexpr int NS = 8 * kQB;                  // softmax scores per lane
   constexpr int NKF = 2 * QK::KS;              // K fragments (ks, kb), ks-major
   constexpr int NVF = Gm::DB;                  // V^T fragments (db)
-  constexpr int LA = 2;                        // read lookahead, in groups
+  constexpr int LA = 1;                        // read lookahead, in groups
   typename QK::Frag kf[NKF];
   bf16x8 vf[NVF];
   auto load_k = [&](int i) {
