@@ -19,13 +19,15 @@
 //  * delta_kernel: delta = rowsum(dO * O) in float32;
 //  * dkdv_kernel: a workgroup of 8 waves owns 128 keys of one (b, h), 16 per
 //    wave, with its K and V rows in registers; it streams the query rows in
-//    64-row LDS tiles (Q, dO, LSE, delta; two stages, loaded with
+//    64-row LDS tiles (Q, dO, LSE, delta; four stages, loaded with
 //    buffer_load ... lds) and per 32-query step computes, with
 //    v_mfma_f32_16x16x32_bf16,
 //      S  = Q K^T and dP = dO V^T  (A = Q / dO rows from LDS, B = K / V),
 //      P, dS per element in float32,
 //      dV^T += dO^T P and dK^T += Q^T dS  (A = transposing LDS reads of the
-//      same tiles, B = P / dS packed to bf16 from the lane's own S layout);
+//      same tiles, B = P / dS packed to bf16 from the lane's own S layout),
+//    software-pipelined so that one slot holds the first product of the
+//    next step, the second of the previous one and the softmax of this one;
 //  * dq_kernel: the forward's arrangement: 8 waves x 32 query rows with Q and
 //    dO in registers, K and V streamed in 64-key LDS tiles; per 32-key step
 //      S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T.
@@ -43,6 +45,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -168,86 +171,190 @@ __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ O
 }
 
 // ---------------------------------------------------------------- dK, dV
+// Software-pipelined over 32-query steps: slot s issues the S / dP MFMAs of
+// step s+1, the dV / dK MFMAs of step s-1 and the P / dS of step s, laid out
+// as 16 groups fenced by scheduling barriers (as in the forward kernel), so
+// one wave's vector work overlaps its own matrix work.  A step's Q / dO tile
+// is read from the slot before the step (S, dP) to the slot after it (dV,
+// dK): four LDS stages per tensor, tile t+2 loaded while tiles t-1 .. t+1
+// are live.
+constexpr int kQStages = 4;
+
+// Per-lane LDS offsets, each plus the LDS address of its tensor's stage 0, in
+// registers the compiler cannot see through: a read of stage j is that
+// register plus a constant below 64 KB that the instruction encodes.  The
+// reads keep their stage array as their object, so the compiler still knows
+// they do not touch the stage being loaded.
 struct KVCtx {
   bf16x8 k[KS], v[KS];  // B operands: lane holds key c16, channels 32ks + 8g .. +7
   f32x4 dk[DB], dv[DB]; // dK^T, dV^T blocks: lane holds channels 16db + 4g + r of key c16
-  int aoff[KS];
-  int trb;
-  int g, lane;
+  int qa[KS], oa[KS];   // row-major fragment (ks) of the Q / dO stages
+  int qt[DB], ot[DB];   // transposing fragment (db) of the Q / dO stages
+  int qbase, obase;     // LDS addresses of Q stage 0 and dO stage 0
+  int g, lane, wave;
+  int Nq, ntiles;
+  float c;
+  const __bf16 *Qb, *dOb;
+  const float *Lb, *Db;
+  int voff[PIECES / kWaves];
+  // stages (separate scalars: never an indexed array); a dO stage holds the
+  // tile, then the tile's 64 LSE values, then its 64 delta values
+  lds_t *q0, *q1, *q2, *q3, *o0, *o1, *o2, *o3;
 };
 
-// One 32-query step of the dK/dV accumulation from the stage (q, o, l, d);
-// queries q0 .. q0+31 of the tile at rows [32 st, 32 st + 32).
-template <bool MASK>
-__device__ __forceinline__ void dkdv_step(KVCtx& x, const lds_t* qt, const lds_t* ot,
-                                          const lds_f32* lt, const lds_f32* dt, int st, int q0,
-                                          int Nq, float c) {
-  const lds_t* qs = qt + 32 * st * ROWB;
-  const lds_t* os = ot + 32 * st * ROWB;
-  f32x4 S[2], dP[2];
+template <typename T>
+__device__ __forceinline__ T pick4(T a0, T a1, T a2, T a3, int i) {
+  return i == 0 ? a0 : (i == 1 ? a1 : (i == 2 ? a2 : a3));
+}
+// Stage of tile t + k, where PH = t % 4 when known at compile time, else -1.
+__device__ __forceinline__ int stage_at(int PH, int t, int k) {
+  return PH >= 0 ? (PH + k) % kQStages : (t + k) % kQStages;
+}
+#define QST(x, i) pick4((x).q0, (x).q1, (x).q2, (x).q3, (i))
+#define OST(x, i) pick4((x).o0, (x).o1, (x).o2, (x).o3, (i))
+#define LST(x, i) reinterpret_cast<lds_f32*>(OST(x, i) + TILE)
+#define DST(x, i) reinterpret_cast<lds_f32*>(OST(x, i) + TILE + 4 * TR)
+
+// S = Q K^T and dP = dO V^T of one 32-query step, unpipelined (first step).
+__device__ __forceinline__ void sdp_step(const KVCtx& x, f32x4 (&S)[2], f32x4 (&dP)[2], const lds_t* qs,
+                                         const lds_t* os) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     S[qb] = f32x4{};
     dP[qb] = f32x4{};
+  }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 aq = *reinterpret_cast<const lds_bf16x8*>(qs + 16 * qb * ROWB + x.aoff[ks]);
-      const bf16x8 ao = *reinterpret_cast<const lds_bf16x8*>(os + 16 * qb * ROWB + x.aoff[ks]);
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const bf16x8 aq = *reinterpret_cast<const lds_bf16x8*>(qs - x.qbase + 16 * qb * ROWB + x.qa[ks]);
+      const bf16x8 ao = *reinterpret_cast<const lds_bf16x8*>(os - x.obase + 16 * qb * ROWB + x.oa[ks]);
       S[qb] = mfma16(aq, x.k[ks], S[qb]);
       dP[qb] = mfma16(ao, x.v[ks], dP[qb]);
     }
-  }
-  // S[qb] holds queries 32st + 16qb + 4g + r (rows) of key c16 (column).
-  bf16x8 pp, dsp;
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qi = 32 * st + 16 * qb + 4 * x.g;
-    const f32x4 lse = *reinterpret_cast<const lds_f32x4*>(lt + qi);
-    const f32x4 del = *reinterpret_cast<const lds_f32x4*>(dt + qi);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float p = __builtin_amdgcn_exp2f(fmaf(S[qb][r], c, -lse[r] * kLog2e));
-      if (MASK && q0 + qi + r >= Nq) p = 0.f;
-      const float ds = p * (dP[qb][r] - del[r]);
-      pp[4 * qb + r] = (__bf16)p;
-      dsp[4 * qb + r] = (__bf16)ds;
-    }
-  }
-  // B operands: k index 8g + j <-> query 4g + j (j < 4), 16 + 4g + j - 4 (j >= 4).
+}
+
+// dV^T += dO^T P and dK^T += Q^T dS of one step, unpipelined (last step).
+__device__ __forceinline__ void dvdk_step(KVCtx& x, bf16x8 pp, bf16x8 dsp, const lds_t* qs,
+                                          const lds_t* os) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
-    const bf16x8 aot = tr_frag(os + (x.trb ^ (32 * db)));
-    const bf16x8 aqt = tr_frag(qs + (x.trb ^ (32 * db)));
-    x.dv[db] = mfma16(aot, pp, x.dv[db]);
-    x.dk[db] = mfma16(aqt, dsp, x.dk[db]);
+    x.dv[db] = mfma16(tr_frag(os - x.obase + x.ot[db]), pp, x.dv[db]);
+    x.dk[db] = mfma16(tr_frag(qs - x.qbase + x.qt[db]), dsp, x.dk[db]);
   }
 }
 
-struct QStages {
-  lds_t *q0, *q1, *o0, *o1;
-  lds_f32 *l0, *l1, *d0, *d1;
-};
-
-// Query tile t from stage ST (0/1); loads tile t+1 into the other stage.
-template <int ST, bool MASK>
-__device__ __forceinline__ void dkdv_tile(KVCtx& x, const QStages& s, int t, int ntiles,
-                                          const __bf16* Qb, const __bf16* dOb, const float* Lb,
-                                          const float* Db, int Nq, int wave, const int* voff,
-                                          float c) {
-  if (t + 1 < ntiles) {
-    const int r1 = (t + 1) * TR;
-    stage_rows(Qb, r1, Nq, ST ? s.q0 : s.q1, wave, voff);
-    stage_rows(dOb, r1, Nq, ST ? s.o0 : s.o1, wave, voff);
-    if (wave == 0) stage_vec(Lb, r1, Nq, ST ? s.l0 : s.l1, x.lane);
-    if (wave == 1) stage_vec(Db, r1, Nq, ST ? s.d0 : s.d1, x.lane);
+// One slot: S / dP of the next step into Sn / dPn (rows at qn / on), dV / dK
+// of the previous step from Pp / dSp (rows at qp / op), P / dS of this step
+// from Sc / dPc into Pc / dSc (LSE and delta at lt / dt, query index q0 of
+// the step's row 0).  Group gi runs the S / dP MFMA gi (index i: ks = i / 4,
+// qb = (i / 2) % 2, S if i is even else dP), the dV / dK MFMA gi (db = gi / 2,
+// dV if gi is even else dK), and, in odd groups, score (qb, r) = ((gi-1)/8,
+// ((gi-1)/2) % 4) of this step; it issues the LDS reads that group gi + 1 needs.
+// The B operands pack query 4g + j (j < 4) and 16 + 4g + j - 4 (j >= 4) of
+// the step: k index 8g + j of v_mfma_f32_16x16x32_bf16.
+template <bool MASK>
+__device__ __forceinline__ void dkdv_slot(KVCtx& x, const f32x4 (&Sc)[2], const f32x4 (&dPc)[2],
+                                          f32x4 (&Sn)[2], f32x4 (&dPn)[2], bf16x8 Pp, bf16x8 dSp,
+                                          bf16x8& Pc, bf16x8& dSc, const lds_t* qn, const lds_t* on,
+                                          const lds_t* qp, const lds_t* op, const lds_f32* lt,
+                                          const lds_f32* dt, int q0) {
+  constexpr int NG = 16;
+  bf16x8 fa[NG], fc[NG];
+  auto load_a = [&](int i) {
+    const int ks = i / 4, qb = (i / 2) % 2;
+    fa[i] = (i & 1) ? *reinterpret_cast<const lds_bf16x8*>(on - x.obase + 16 * qb * ROWB + x.oa[ks])
+                    : *reinterpret_cast<const lds_bf16x8*>(qn - x.qbase + 16 * qb * ROWB + x.qa[ks]);
+  };
+  auto load_c = [&](int j) {
+    const int db = j / 2;
+    fc[j] = (j & 1) ? tr_frag(qp - x.qbase + x.qt[db]) : tr_frag(op - x.obase + x.ot[db]);
+  };
+  // LSE and delta of the lane's rows 16qb + 4g + r.
+  f32x4 lse[2], del[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    lse[qb] = *reinterpret_cast<const lds_f32x4*>(lt + 16 * qb + 4 * x.g);
+    del[qb] = *reinterpret_cast<const lds_f32x4*>(dt + 16 * qb + 4 * x.g);
   }
-  const lds_t* qt = ST ? s.q1 : s.q0;
-  const lds_t* ot = ST ? s.o1 : s.o0;
-  const lds_f32* lt = ST ? s.l1 : s.l0;
-  const lds_f32* dt = ST ? s.d1 : s.d0;
-  dkdv_step<MASK>(x, qt, ot, lt, dt, 0, t * TR, Nq, c);
-  dkdv_step<MASK>(x, qt, ot, lt, dt, 1, t * TR, Nq, c);
-  tile_barrier();  // tile t+1 landed; every wave is done with tile t
+  load_a(0);
+  load_c(0);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    Sn[qb] = f32x4{};
+    dPn[qb] = f32x4{};
+  }
+  float p[8], ds[8];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    if (gi + 1 < NG) {
+      load_a(gi + 1);
+      load_c(gi + 1);
+    }
+    {
+      const int ks = gi / 4, qb = (gi / 2) % 2;
+      if (gi & 1)
+        dPn[qb] = mfma16(fa[gi], x.v[ks], dPn[qb]);
+      else
+        Sn[qb] = mfma16(fa[gi], x.k[ks], Sn[qb]);
+    }
+    {
+      const int db = gi / 2;
+      if (gi & 1)
+        x.dk[db] = mfma16(fc[gi], dSp, x.dk[db]);
+      else
+        x.dv[db] = mfma16(fc[gi], Pp, x.dv[db]);
+    }
+    if (gi & 1) {
+      const int e = gi / 2, qb = e / 4, r = e % 4;
+      float sv = Sc[qb][r];
+      // Pin the element's work to its group (see the forward kernel).
+      asm volatile("" : "+v"(sv));
+      float pv = __builtin_amdgcn_exp2f(fmaf(sv, x.c, -lse[qb][r] * kLog2e));
+      if (MASK && q0 + 16 * qb + 4 * x.g + r >= x.Nq) pv = 0.f;
+      p[e] = pv;
+      ds[e] = pv * (dPc[qb][r] - del[qb][r]);
+      if (e & 1) {
+        bf16x2 pk = {(__bf16)p[e - 1], (__bf16)p[e]};
+        bf16x2 dk = {(__bf16)ds[e - 1], (__bf16)ds[e]};
+        asm volatile("" : "+v"(pk), "+v"(dk));
+        Pc[e - 1] = pk[0];
+        Pc[e] = pk[1];
+        dSc[e - 1] = dk[0];
+        dSc[e] = dk[1];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+__device__ __forceinline__ void stage_q_tile(const KVCtx& x, int t, int st) {
+  const int r0 = t * TR;
+  stage_rows(x.Qb, r0, x.Nq, QST(x, st), x.wave, x.voff);
+  stage_rows(x.dOb, r0, x.Nq, OST(x, st), x.wave, x.voff);
+  if (x.wave == 0) stage_vec(x.Lb, r0, x.Nq, LST(x, st), x.lane);
+  if (x.wave == 1) stage_vec(x.Db, r0, x.Nq, DST(x, st), x.lane);
+}
+
+// Query tile t = steps 2t and 2t+1.  On entry S0 / dP0 hold step 2t and
+// Pa / dSa hold step 2t-1; on exit S0 / dP0 hold step 2t+2 (past the last
+// tile: unused) and Pa / dSa hold step 2t+1.
+template <int PH, bool MASK>
+__device__ __forceinline__ void dkdv_tile(KVCtx& x, int t, f32x4 (&S0)[2], f32x4 (&dP0)[2],
+                                          f32x4 (&S1)[2], f32x4 (&dP1)[2], bf16x8& Pa, bf16x8& dSa,
+                                          bf16x8& Pb, bf16x8& dSb) {
+  tile_barrier();  // tile t+1 landed; every wave is done with tile t-2
+  const int sc = stage_at(PH, t, 0), sn = stage_at(PH, t, 1), sp = stage_at(PH, t, 3);
+  if (t + 2 < x.ntiles) stage_q_tile(x, t + 2, stage_at(PH, t, 2));
+  const lds_t* qc = QST(x, sc);
+  const lds_t* oc = OST(x, sc);
+  const lds_f32* lt = LST(x, sc);
+  const lds_f32* dt = DST(x, sc);
+  dkdv_slot<MASK>(x, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb, qc + 32 * ROWB, oc + 32 * ROWB,
+                  QST(x, sp) + 32 * ROWB, OST(x, sp) + 32 * ROWB, lt, dt, t * TR);
+  dkdv_slot<MASK>(x, S1, dP1, S0, dP0, Pb, dSb, Pa, dSa, QST(x, sn), OST(x, sn), qc, oc, lt + 32,
+                  dt + 32, t * TR + 32);
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -258,12 +365,15 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                  int total, float c, float scale) {
   __shared__ __attribute__((aligned(1024))) char q0s[TILE];
   __shared__ __attribute__((aligned(1024))) char q1s[TILE];
-  __shared__ __attribute__((aligned(1024))) char o0s[TILE];
-  __shared__ __attribute__((aligned(1024))) char o1s[TILE];
-  __shared__ __attribute__((aligned(256))) float l0s[TR];
-  __shared__ __attribute__((aligned(256))) float l1s[TR];
-  __shared__ __attribute__((aligned(256))) float d0s[TR];
-  __shared__ __attribute__((aligned(256))) float d1s[TR];
+  __shared__ __attribute__((aligned(1024))) char q2s[TILE];
+  __shared__ __attribute__((aligned(1024))) char q3s[TILE];
+  // One LDS object per stage and tensor: the compiler tells apart at most
+  // eight objects written by buffer_load ... lds when it decides which
+  // reads must wait for them.
+  __shared__ __attribute__((aligned(1024))) char o0s[TILE + 8 * TR];
+  __shared__ __attribute__((aligned(1024))) char o1s[TILE + 8 * TR];
+  __shared__ __attribute__((aligned(1024))) char o2s[TILE + 8 * TR];
+  __shared__ __attribute__((aligned(1024))) char o3s[TILE + 8 * TR];
 
   const int tile = remap_xcd(blockIdx.x, total);
   const int bh = tile / n_ktiles;
@@ -271,56 +381,69 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15, g = lane >> 4;
-  const __bf16* Qb = Q + (int64_t)bh * Nq * D;
-  const __bf16* dOb = dO + (int64_t)bh * Nq * D;
-  const float* Lb = LSE + (int64_t)bh * Nq;
-  const float* Db = Dl + (int64_t)bh * Nq;
 
   KVCtx x;
   x.g = g;
   x.lane = lane;
+  x.wave = wave;
+  x.Nq = Nq;
+  x.ntiles = (Nq + TR - 1) / TR;
+  x.c = c;
+  x.Qb = Q + (int64_t)bh * Nq * D;
+  x.dOb = dO + (int64_t)bh * Nq * D;
+  x.Lb = LSE + (int64_t)bh * Nq;
+  x.Db = Dl + (int64_t)bh * Nq;
+  x.q0 = (lds_t*)q0s; x.q1 = (lds_t*)q1s; x.q2 = (lds_t*)q2s; x.q3 = (lds_t*)q3s;
+  x.o0 = (lds_t*)o0s; x.o1 = (lds_t*)o1s; x.o2 = (lds_t*)o2s; x.o3 = (lds_t*)o3s;
+  x.qbase = (int)(size_t)x.q0;
+  x.obase = (int)(size_t)x.o0;
   const int key = kt * KEYS_PER_WG + wave * 16 + c16;
   const int krow = min(key, Nkv - 1);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     x.k[ks] = *reinterpret_cast<const bf16x8*>(K + ((int64_t)bh * Nkv + krow) * D + 32 * ks + 8 * g);
     x.v[ks] = *reinterpret_cast<const bf16x8*>(V + ((int64_t)bh * Nkv + krow) * D + 32 * ks + 8 * g);
-    x.aoff[ks] = a_off(c16, g, ks);
+    x.qa[ks] = a_off(c16, g, ks) + x.qbase;
+    x.oa[ks] = a_off(c16, g, ks) + x.obase;
+    asm volatile("" : "+v"(x.qa[ks]), "+v"(x.oa[ks]));
   }
+  const int trb = tr_base(lane);
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     x.dk[db] = f32x4{};
     x.dv[db] = f32x4{};
+    x.qt[db] = (trb ^ (32 * db)) + x.qbase;
+    x.ot[db] = (trb ^ (32 * db)) + x.obase;
+    asm volatile("" : "+v"(x.qt[db]), "+v"(x.ot[db]));
   }
-  x.trb = tr_base(lane);
-  int voff[PIECES / kWaves];
-  piece_offsets(voff, wave, lane);
+  piece_offsets(x.voff, wave, lane);
 
-  QStages s{(lds_t*)q0s, (lds_t*)q1s, (lds_t*)o0s, (lds_t*)o1s,
-            (lds_f32*)l0s, (lds_f32*)l1s, (lds_f32*)d0s, (lds_f32*)d1s};
-  const int ntiles = (Nq + TR - 1) / TR;
-  stage_rows(Qb, 0, Nq, s.q0, wave, voff);
-  stage_rows(dOb, 0, Nq, s.o0, wave, voff);
-  if (wave == 0) stage_vec(Lb, 0, Nq, s.l0, lane);
-  if (wave == 1) stage_vec(Db, 0, Nq, s.d0, lane);
-  tile_barrier();
+  // The first slot multiplies P = dS = 0 by the stage of tile -1 (stage 3):
+  // zero it so no stale Inf/NaN bit pattern can turn 0 * x into NaN.
+  for (int i = threadIdx.x; i < TILE / 16; i += kThreads) {
+    reinterpret_cast<lds_f32x4*>(x.q3)[i] = f32x4{};
+    reinterpret_cast<lds_f32x4*>(x.o3)[i] = f32x4{};
+  }
+  stage_q_tile(x, 0, 0);
+  if (x.ntiles > 1) stage_q_tile(x, 1, 1);
+  tile_barrier();  // tiles 0 and 1 landed, stage 3 zeroed
+  f32x4 S0[2], dP0[2], S1[2], dP1[2];
+  bf16x8 Pa = bf16x8{}, dSa = bf16x8{}, Pb, dSb;
+  sdp_step(x, S0, dP0, x.q0, x.o0);
   const bool partial = (Nq % TR) != 0;
-  const int nfull = partial ? ntiles - 1 : ntiles;
+  const int nfull = partial ? x.ntiles - 1 : x.ntiles;
   int t = 0;
-  for (; t + 2 <= nfull; t += 2) {
-    dkdv_tile<0, false>(x, s, t, ntiles, Qb, dOb, Lb, Db, Nq, wave, voff, c);
-    dkdv_tile<1, false>(x, s, t + 1, ntiles, Qb, dOb, Lb, Db, Nq, wave, voff, c);
+  for (; t + kQStages <= nfull; t += kQStages) {
+    dkdv_tile<0, false>(x, t, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb);
+    dkdv_tile<1, false>(x, t + 1, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb);
+    dkdv_tile<2, false>(x, t + 2, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb);
+    dkdv_tile<3, false>(x, t + 3, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb);
   }
-  if (t < nfull) {
-    dkdv_tile<0, false>(x, s, t, ntiles, Qb, dOb, Lb, Db, Nq, wave, voff, c);
-    ++t;
-  }
-  if (partial) {
-    if ((t & 1) == 0)
-      dkdv_tile<0, true>(x, s, t, ntiles, Qb, dOb, Lb, Db, Nq, wave, voff, c);
-    else
-      dkdv_tile<1, true>(x, s, t, ntiles, Qb, dOb, Lb, Db, Nq, wave, voff, c);
-  }
+  for (; t < nfull; ++t) dkdv_tile<-1, false>(x, t, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb);
+  if (partial) dkdv_tile<-1, true>(x, t, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb);
+  // dV / dK of the last step (rows 32 .. 63 of the last tile).
+  const int sl = (x.ntiles - 1) % kQStages;
+  dvdk_step(x, Pa, dSa, QST(x, sl) + 32 * ROWB, OST(x, sl) + 32 * ROWB);
 
   if (key < Nkv) {
     const int64_t base = ((int64_t)bh * Nkv + key) * D;
