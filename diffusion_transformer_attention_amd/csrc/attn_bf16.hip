@@ -35,10 +35,12 @@
 //    fenced by scheduling barriers, each issuing LDS reads ahead of their
 //    MFMAs, one QK^T and one PV MFMA and a share of the softmax;
 //  * softmax in base 2: p = 2^(s*c - m*c) with c = scale*log2(e).  Two row
-//    sums: lb of the bf16-rounded p that the PV product multiplies (via
-//    v_dot2_f32_bf16) normalises O, so O stays an exact convex combination
-//    of the V rows whatever the rounding of its dominant weight; l of the
-//    float32 p gives the LSE (the rounded sum would carry 2^-9 errors into
+//    sums: lb of the bf16-rounded p that the PV product multiplies
+//    normalises O, so O stays an exact convex combination of the V rows
+//    whatever the rounding of its dominant weight; it comes from the matrix
+//    cores (one more PV MFMA per query block, with an all-ones V^T block),
+//    which frees the vector ALUs that bound the loop.  l of the float32 p
+//    gives the LSE (the rounded sum would carry errors of up to 2^-8 into
 //    rows dominated by a few keys);
 //  * fixed reference max: each row's reference m is the max of its first
 //    32-key step and is then held.  O and l accumulate p against that same m,
@@ -249,7 +251,8 @@ struct Frags {
   using QK = QKOps<D, F8>;
   f32x4 o[kQB][Geo<D>::DB];           // O^T blocks: lane holds channels 16db+4g+r of its query
   typename QK::Frag q[kQB][QK::KS];   // Q^T operand of the lane's query (bf16: channels 32ks+8g..+7)
-  float m[kQB], l[kQB], lb[kQB];
+  float m[kQB], l[kQB];
+  f32x4 lb[kQB];                      // sum of the bf16 p: an all-ones V^T block, every row alike
 };
 
 // Everything one pass over the keys needs.
@@ -370,12 +373,12 @@ __device__ __forceinline__ void slot(Frags<D, F8>& f, const f32x4 (&Sc)[2][kQB],
 #pragma unroll
   for (int fi = 0; fi < NVF; ++fi)
     if (vfirst(fi) < LA) load_v(fi);
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  float l[kQB], lb[kQB], mc[kQB], p[kQB][8];
+  const bf16x8 ones8 = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                        (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+  float l[kQB], mc[kQB], p[kQB][8];
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     l[qb] = f.l[qb];
-    lb[qb] = f.lb[qb];
     mc[qb] = f.m[qb] * x.c;
   }
 #pragma unroll
@@ -401,6 +404,11 @@ __device__ __forceinline__ void slot(Frags<D, F8>& f, const f32x4 (&Sc)[2][kQB],
       const int db = j / kQB, qb = j % kQB;
       f.o[qb][db] = mfma16(vf[db], Pp[qb], f.o[qb][db]);
     }
+    // The row sums of the bf16 P^T the PV product multiplies, on the matrix
+    // cores: an all-ones V^T block, one MFMA per query block.
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb)
+      if (g == NG - 1 - (NG / kQB) * qb) f.lb[qb] = mfma16(ones8, Pp[qb], f.lb[qb]);
 #pragma unroll
     for (int e = g * NS / NG; e < (g + 1) * NS / NG; ++e) {
       const int qb = e / 8, kb = (e / 4) % 2, r = e % 4;
@@ -416,8 +424,7 @@ __device__ __forceinline__ void slot(Frags<D, F8>& f, const f32x4 (&Sc)[2][kQB],
         const float p0 = p[qb][j], p1 = p[qb][j + 1];
         bf16x2 pk = {(__bf16)p0, (__bf16)p1};
         l[qb] += p0 + p1;
-        lb[qb] = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, lb[qb], false);
-        asm volatile("" : "+v"(pk), "+v"(l[qb]), "+v"(lb[qb]));
+        asm volatile("" : "+v"(pk), "+v"(l[qb]));
         Pc[qb][j] = pk[0];
         Pc[qb][j + 1] = pk[1];
       }
@@ -427,7 +434,6 @@ __device__ __forceinline__ void slot(Frags<D, F8>& f, const f32x4 (&Sc)[2][kQB],
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     f.l[qb] = l[qb];
-    f.lb[qb] = lb[qb];
   }
 }
 
@@ -475,6 +481,10 @@ __device__ __forceinline__ void pv_step(Frags<D, F8>& f, const bf16x8 (&P)[kQB],
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) f.o[qb][db] = mfma16(a, P[qb], f.o[qb][db]);
   }
+  const bf16x8 ones8 = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                        (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) f.lb[qb] = mfma16(ones8, P[qb], f.lb[qb]);
 }
 
 // One full pass over the keys: stage, the unmasked tiles (unrolled by the
@@ -658,7 +668,7 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
     for (int ks = 0; ks < QK::KS; ++ks) f.q[qb][ks] = QK::load_q(qrow_p, g, ks);
     f.m[qb] = -INFINITY;
     f.l[qb] = 0.f;
-    f.lb[qb] = 0.f;
+    f.lb[qb] = f32x4{};
 #pragma unroll
     for (int db = 0; db < Gm::DB; ++db) f.o[qb][db] = f32x4{};
   }
@@ -672,7 +682,7 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
       f.l[qb] = 0.f;
-      f.lb[qb] = 0.f;
+      f.lb[qb] = f32x4{};
 #pragma unroll
       for (int db = 0; db < Gm::DB; ++db) f.o[qb][db] = f32x4{};
     }
@@ -682,7 +692,7 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     const float l_tot = quad_sum(f.l[qb]);
-    const float inv = 1.0f / quad_sum(f.lb[qb]);
+    const float inv = 1.0f / f.lb[qb][0];
     const int qrow = qrow0 + 16 * qb;
     if (qrow < Nq) {
       const int64_t obase = token_offset(qrow, lay.qseg, qhead, qsstride, D);
