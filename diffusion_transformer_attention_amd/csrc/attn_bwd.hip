@@ -27,10 +27,15 @@
 //      dV^T += dO^T P and dK^T += Q^T dS  (A = transposing LDS reads of the
 //      same tiles, B = P / dS packed to bf16 from the lane's own S layout),
 //    software-pipelined so that one slot holds the first product of the
-//    next step, the second of the previous one and the softmax of this one;
+//    next step, the second of the previous one and the softmax of this one.
+//    V is held negated and each dP chain starts at delta, so the chain ends
+//    at delta - dP and the softmax yields -dS = p (delta - dP) with one
+//    multiply (dK takes the sign back in its final scale);
 //  * dq_kernel: the forward's arrangement: 8 waves x 32 query rows with Q and
 //    dO in registers, K and V streamed in 64-key LDS tiles; per 32-key step
-//      S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T.
+//      S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T,
+//    each dP^T chain starting at -delta of the lane's query, so that it ends
+//    at dP - delta.
 // The tiles' 16-byte chunks are XOR-swizzled with 2(row & 7), the swizzle of
 // the forward kernel's V tile, so both read patterns are bank-conflict-free:
 // ds_read_b128 of 16 rows at one column, and ds_read_b64_tr_b16 of 8 rows x 2
@@ -215,13 +220,14 @@ __device__ __forceinline__ int stage_at(int PH, int t, int k) {
 #define LST(x, i) reinterpret_cast<lds_f32*>(OST(x, i) + TILE)
 #define DST(x, i) reinterpret_cast<lds_f32*>(OST(x, i) + TILE + 4 * TR)
 
-// S = Q K^T and dP = dO V^T of one 32-query step, unpipelined (first step).
+// S = Q K^T and delta - dP = delta + dO (-V)^T of one 32-query step,
+// unpipelined (first step).
 __device__ __forceinline__ void sdp_step(const KVCtx& x, f32x4 (&S)[2], f32x4 (&dP)[2], const lds_t* qs,
-                                         const lds_t* os) {
+                                         const lds_t* os, const lds_f32* dt) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     S[qb] = f32x4{};
-    dP[qb] = f32x4{};
+    dP[qb] = *reinterpret_cast<const lds_f32x4*>(dt + 16 * qb + 4 * x.g);
   }
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
@@ -258,7 +264,7 @@ __device__ __forceinline__ void dkdv_slot(KVCtx& x, const f32x4 (&Sc)[2], const 
                                           f32x4 (&Sn)[2], f32x4 (&dPn)[2], bf16x8 Pp, bf16x8 dSp,
                                           bf16x8& Pc, bf16x8& dSc, const lds_t* qn, const lds_t* on,
                                           const lds_t* qp, const lds_t* op, const lds_f32* lt,
-                                          const lds_f32* dt, int q0) {
+                                          const lds_f32* dtn, int q0) {
   constexpr int NG = 16;
   bf16x8 fa[NG], fc[NG];
   auto load_a = [&](int i) {
@@ -270,20 +276,17 @@ __device__ __forceinline__ void dkdv_slot(KVCtx& x, const f32x4 (&Sc)[2], const 
     const int db = j / 2;
     fc[j] = (j & 1) ? tr_frag(qp - x.qbase + x.qt[db]) : tr_frag(op - x.obase + x.ot[db]);
   };
-  // LSE and delta of the lane's rows 16qb + 4g + r.
-  f32x4 lse[2], del[2];
+  // LSE of this step's rows 16qb + 4g + r; the next step's dP chains start
+  // at its delta.
+  f32x4 lse[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     lse[qb] = *reinterpret_cast<const lds_f32x4*>(lt + 16 * qb + 4 * x.g);
-    del[qb] = *reinterpret_cast<const lds_f32x4*>(dt + 16 * qb + 4 * x.g);
+    dPn[qb] = *reinterpret_cast<const lds_f32x4*>(dtn + 16 * qb + 4 * x.g);
+    Sn[qb] = f32x4{};
   }
   load_a(0);
   load_c(0);
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    Sn[qb] = f32x4{};
-    dPn[qb] = f32x4{};
-  }
   float p[8], ds[8];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -314,7 +317,7 @@ __device__ __forceinline__ void dkdv_slot(KVCtx& x, const f32x4 (&Sc)[2], const 
       float pv = __builtin_amdgcn_exp2f(fmaf(sv, x.c, -lse[qb][r] * kLog2e));
       if (MASK && q0 + 16 * qb + 4 * x.g + r >= x.Nq) pv = 0.f;
       p[e] = pv;
-      ds[e] = pv * (dPc[qb][r] - del[qb][r]);
+      ds[e] = pv * dPc[qb][r];  // -dS = p (delta - dP)
       if (e & 1) {
         bf16x2 pk = {(__bf16)p[e - 1], (__bf16)p[e]};
         bf16x2 dk = {(__bf16)ds[e - 1], (__bf16)ds[e]};
@@ -352,9 +355,9 @@ __device__ __forceinline__ void dkdv_tile(KVCtx& x, int t, f32x4 (&S0)[2], f32x4
   const lds_f32* lt = LST(x, sc);
   const lds_f32* dt = DST(x, sc);
   dkdv_slot<MASK>(x, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb, qc + 32 * ROWB, oc + 32 * ROWB,
-                  QST(x, sp) + 32 * ROWB, OST(x, sp) + 32 * ROWB, lt, dt, t * TR);
+                  QST(x, sp) + 32 * ROWB, OST(x, sp) + 32 * ROWB, lt, dt + 32, t * TR);
   dkdv_slot<MASK>(x, S1, dP1, S0, dP0, Pb, dSb, Pa, dSa, QST(x, sn), OST(x, sn), qc, oc, lt + 32,
-                  dt + 32, t * TR + 32);
+                  DST(x, sn), t * TR + 32);
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -402,7 +405,11 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     x.k[ks] = *reinterpret_cast<const bf16x8*>(K + ((int64_t)bh * Nkv + krow) * D + 32 * ks + 8 * g);
-    x.v[ks] = *reinterpret_cast<const bf16x8*>(V + ((int64_t)bh * Nkv + krow) * D + 32 * ks + 8 * g);
+    // -V: the dP chains then hold delta - dP, and the softmax yields -dS.
+    x.v[ks] = __builtin_bit_cast(
+        bf16x8, __builtin_bit_cast(u32x4, *reinterpret_cast<const bf16x8*>(
+                                              V + ((int64_t)bh * Nkv + krow) * D + 32 * ks + 8 * g)) ^
+                    u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u});
     x.qa[ks] = a_off(c16, g, ks) + x.qbase;
     x.oa[ks] = a_off(c16, g, ks) + x.obase;
     asm volatile("" : "+v"(x.qa[ks]), "+v"(x.oa[ks]));
@@ -429,7 +436,7 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   tile_barrier();  // tiles 0 and 1 landed, stage 3 zeroed
   f32x4 S0[2], dP0[2], S1[2], dP1[2];
   bf16x8 Pa = bf16x8{}, dSa = bf16x8{}, Pb, dSb;
-  sdp_step(x, S0, dP0, x.q0, x.o0);
+  sdp_step(x, S0, dP0, x.q0, x.o0, DST(x, 0));
   const bool partial = (Nq % TR) != 0;
   const int nfull = partial ? x.ntiles - 1 : x.ntiles;
   int t = 0;
@@ -449,7 +456,7 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int64_t base = ((int64_t)bh * Nkv + key) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      *reinterpret_cast<f32x4*>(dK + base + 16 * db + 4 * g) = x.dk[db] * scale;
+      *reinterpret_cast<f32x4*>(dK + base + 16 * db + 4 * g) = x.dk[db] * -scale;  // of -dS
       *reinterpret_cast<f32x4*>(dV + base + 16 * db + 4 * g) = x.dv[db];
     }
   }
@@ -459,7 +466,8 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 struct QCtx {
   bf16x8 q[2][KS], o[2][KS];  // B operands: lane holds query c16 of block qb, channels 32ks + 8g ..
   f32x4 dq[2][DB];            // dQ^T blocks: lane holds channels 16db + 4g + r of its query
-  float lse2[2], del[2];
+  float lse2[2];
+  f32x4 ndel[2];              // -delta of the lane's query, in every element: the start of each dP^T chain
   int aoff[KS];
   int trb;
   int g;
@@ -477,7 +485,7 @@ __device__ __forceinline__ void dq_step(QCtx& x, const lds_t* kt, const lds_t* v
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       S[kb][qb] = f32x4{};
-      dP[kb][qb] = f32x4{};
+      dP[kb][qb] = x.ndel[qb];
     }
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
@@ -501,7 +509,7 @@ __device__ __forceinline__ void dq_step(QCtx& x, const lds_t* kt, const lds_t* v
       for (int r = 0; r < 4; ++r) {
         float p = __builtin_amdgcn_exp2f(fmaf(S[kb][qb][r], c, -x.lse2[qb]));
         if (MASK && k0 + 32 * st + 16 * kb + 4 * x.g + r >= Nkv) p = 0.f;
-        dsp[qb][4 * kb + r] = (__bf16)(p * (dP[kb][qb][r] - x.del[qb]));
+        dsp[qb][4 * kb + r] = (__bf16)(p * dP[kb][qb][r]);
       }
   // dQ^T += K^T dS^T; k index 8g + j <-> key 4g + j (j < 4), 16 + 4g + j - 4 (j >= 4).
 #pragma unroll
@@ -564,7 +572,8 @@ void dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       x.o[qb][ks] = *reinterpret_cast<const bf16x8*>(dO + rb + 32 * ks + 8 * g);
     }
     x.lse2[qb] = LSE[(int64_t)bh * Nq + row] * kLog2e;
-    x.del[qb] = Dl[(int64_t)bh * Nq + row];
+    const float d = -Dl[(int64_t)bh * Nq + row];
+    x.ndel[qb] = f32x4{d, d, d, d};
 #pragma unroll
     for (int db = 0; db < DB; ++db) x.dq[qb][db] = f32x4{};
   }
