@@ -488,9 +488,9 @@ __device__ __forceinline__ void dq_step(QCtx& x, const lds_t* kt, const lds_t* v
       dP[kb][qb] = x.ndel[qb];
     }
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 ak = *reinterpret_cast<const lds_bf16x8*>(ks_ + 16 * kb * ROWB + x.aoff[ks]);
       const bf16x8 av = *reinterpret_cast<const lds_bf16x8*>(vs_ + 16 * kb * ROWB + x.aoff[ks]);
 #pragma unroll
@@ -502,9 +502,9 @@ __device__ __forceinline__ void dq_step(QCtx& x, const lds_t* kt, const lds_t* v
   // S[kb][qb] holds keys 16kb + 4g + r (rows) for the lane's query of block qb.
   bf16x8 dsp[2];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float p = __builtin_amdgcn_exp2f(fmaf(S[kb][qb][r], c, -x.lse2[qb]));
