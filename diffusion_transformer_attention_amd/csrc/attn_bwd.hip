@@ -192,7 +192,7 @@ constexpr int kQStages = 4;
 // they do not touch the stage being loaded.
 struct KVCtx {
   bf16x8 k[KS], v[KS];  // B operands: lane holds key c16, channels 32ks + 8g .. +7
-  f32x4 dk[DB], dv[DB]; // dK^T, dV^T blocks: lane holds channels 16db + 4g + r of key c16
+  f32x4 dk[DB], dv[DB]; // -dK^T, dV^T blocks: lane holds channels 16db + 4g + r of key c16
   int qa[KS], oa[KS];   // row-major fragment (ks) of the Q / dO stages
   int qt[DB], ot[DB];   // transposing fragment (db) of the Q / dO stages
   int qbase, obase;     // LDS addresses of Q stage 0 and dO stage 0
@@ -240,7 +240,7 @@ __device__ __forceinline__ void sdp_step(const KVCtx& x, f32x4 (&S)[2], f32x4 (&
     }
 }
 
-// dV^T += dO^T P and dK^T += Q^T dS of one step, unpipelined (last step).
+// dV^T += dO^T P and -dK^T += Q^T (-dS) of one step, unpipelined (last step).
 __device__ __forceinline__ void dvdk_step(KVCtx& x, bf16x8 pp, bf16x8 dsp, const lds_t* qs,
                                           const lds_t* os) {
 #pragma unroll
@@ -250,10 +250,10 @@ __device__ __forceinline__ void dvdk_step(KVCtx& x, bf16x8 pp, bf16x8 dsp, const
   }
 }
 
-// One slot: S / dP of the next step into Sn / dPn (rows at qn / on), dV / dK
-// of the previous step from Pp / dSp (rows at qp / op), P / dS of this step
-// from Sc / dPc into Pc / dSc (LSE and delta at lt / dt, query index q0 of
-// the step's row 0).  Group gi runs the S / dP MFMA gi (index i: ks = i / 4,
+// One slot: S / delta - dP of the next step into Sn / dPn (rows at qn / on,
+// delta at dtn), dV / -dK of the previous step from Pp / dSp (rows at qp /
+// op), P / -dS of this step from Sc / dPc into Pc / dSc (LSE at lt, query
+// index q0 of the step's row 0).  Group gi runs the S / dP MFMA gi (index i: ks = i / 4,
 // qb = (i / 2) % 2, S if i is even else dP), the dV / dK MFMA gi (db = gi / 2,
 // dV if gi is even else dK), and, in odd groups, score (qb, r) = ((gi-1)/8,
 // ((gi-1)/2) % 4) of this step; it issues the LDS reads that group gi + 1 needs.
