@@ -32,10 +32,12 @@
 //    at delta - dP and the softmax yields -dS = p (delta - dP) with one
 //    multiply (dK takes the sign back in its final scale);
 //  * dq_kernel: the forward's arrangement: 8 waves x 32 query rows with Q and
-//    dO in registers, K and V streamed in 64-key LDS tiles; per 32-key step
+//    dO in registers, K and V streamed in 64-key LDS tiles (three stages);
+//    per 32-key step
 //      S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T,
 //    each dP^T chain starting at -delta of the lane's query, so that it ends
-//    at dP - delta.
+//    at dP - delta; software-pipelined so that the next step's products
+//    overlap this step's softmax and dQ^T products.
 // The tiles' 16-byte chunks are XOR-swizzled with 2(row & 7), the swizzle of
 // the forward kernel's V tile, so both read patterns are bank-conflict-free:
 // ds_read_b128 of 16 rows at one column, and ds_read_b64_tr_b16 of 8 rows x 2
@@ -463,23 +465,41 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 }
 
 // ---------------------------------------------------------------- dQ
+// Software-pipelined over 32-key steps in a register budget that holds only
+// half of a second S^T / dP^T set: slot s runs, in its first half, the P / dS
+// of step s (all 16 scores of the lane) beside the S^T / dP^T MFMAs of step
+// s+1 for key block 0, and in its second half the dQ^T MFMAs of step s beside
+// those of step s+1 for key block 1.  The S^T / dP^T of step s die during the
+// first half, as the second block of step s+1 starts.  A K tile is read from
+// the slot before its first step (S^T) to the slot of its last (dQ^T), a V
+// tile only in the two slots before its steps: three stages each, tile t+2
+// loaded while t and t+1 are read.
 struct QCtx {
   bf16x8 q[2][KS], o[2][KS];  // B operands: lane holds query c16 of block qb, channels 32ks + 8g ..
   f32x4 dq[2][DB];            // dQ^T blocks: lane holds channels 16db + 4g + r of its query
   float lse2[2];
   f32x4 ndel[2];              // -delta of the lane's query, in every element: the start of each dP^T chain
-  int aoff[KS];
-  int trb;
-  int g;
+  int ka[KS], va[KS];         // row-major fragment (ks) of the K / V stages, + kbase / vbase (opaque)
+  int kt[DB];                 // transposing fragment (db) of the K stages, + kbase (opaque)
+  int kbase, vbase;           // LDS addresses of the K and V stage 0
+  int g, lane, wave, Nkv, ntiles;
+  float c;
+  const __bf16 *Kb, *Vb;
+  int voff[PIECES / kWaves];
+  lds_t *k0, *k1, *k2, *v0, *v1, *v2;  // stages (separate scalars: never an indexed array)
 };
 
-// One 32-key step from the stage (kt, vt), keys k0 .. k0+31 at rows [32 st, 32 st + 32).
-template <bool MASK>
-__device__ __forceinline__ void dq_step(QCtx& x, const lds_t* kt, const lds_t* vt, int st, int k0,
-                                        int Nkv, float c) {
-  const lds_t* ks_ = kt + 32 * st * ROWB;
-  const lds_t* vs_ = vt + 32 * st * ROWB;
-  f32x4 S[2][2], dP[2][2];
+// Stage of tile t + k, where PH = t % 3 when known at compile time, else -1.
+__device__ __forceinline__ int kv_stage_at(int PH, int t, int k) { return PH >= 0 ? (PH + k) % 3 : (t + k) % 3; }
+#define KQST(x, i) pick3((x).k0, (x).k1, (x).k2, (i))
+#define VQST(x, i) pick3((x).v0, (x).v1, (x).v2, (i))
+template <typename T>
+__device__ __forceinline__ T pick3(T a0, T a1, T a2, int i) { return i == 0 ? a0 : (i == 1 ? a1 : a2); }
+
+// S^T and dP^T of one 32-key step, unpipelined (first step): keys at rows
+// [0, 32) of kst / vst.
+__device__ __forceinline__ void sdpt_step(const QCtx& x, f32x4 (&S)[2][2], f32x4 (&dP)[2][2],
+                                          const lds_t* kst, const lds_t* vst) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -491,52 +511,100 @@ __device__ __forceinline__ void dq_step(QCtx& x, const lds_t* kt, const lds_t* v
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 ak = *reinterpret_cast<const lds_bf16x8*>(ks_ + 16 * kb * ROWB + x.aoff[ks]);
-      const bf16x8 av = *reinterpret_cast<const lds_bf16x8*>(vs_ + 16 * kb * ROWB + x.aoff[ks]);
+      const bf16x8 ak = *reinterpret_cast<const lds_bf16x8*>(kst - x.kbase + 16 * kb * ROWB + x.ka[ks]);
+      const bf16x8 av = *reinterpret_cast<const lds_bf16x8*>(vst - x.vbase + 16 * kb * ROWB + x.va[ks]);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         S[kb][qb] = mfma16(ak, x.q[qb][ks], S[kb][qb]);
         dP[kb][qb] = mfma16(av, x.o[qb][ks], dP[kb][qb]);
       }
     }
-  // S[kb][qb] holds keys 16kb + 4g + r (rows) for the lane's query of block qb.
+}
+
+// One slot.  Sc / dPc: S^T, dP^T - delta of this step (keys key0 ..
+// key0 + 31, rows [0, 32) of kc); Sn / dPn: those of the next step (rows
+// [0, 32) of kn / vn).  Group gi < 8: S^T / dP^T MFMAs 2gi, 2gi + 1 of the
+// next step's key block 0 and scores 2gi, 2gi + 1 of this step; group gi >= 8:
+// those MFMAs for key block 1 and dQ^T MFMAs 2(gi - 8), 2(gi - 8) + 1.  MFMA
+// index i of a block: ks = i / 4, dP^T if (i / 2) is odd, qb = i % 2; score e:
+// qb = e / 8, kb = (e / 4) % 2, r = e % 4; dQ^T MFMA j: db = j / 2, qb = j % 2.
+template <bool MASK>
+__device__ __forceinline__ void dq_slot(QCtx& x, const f32x4 (&Sc)[2][2], const f32x4 (&dPc)[2][2],
+                                        f32x4 (&Sn)[2][2], f32x4 (&dPn)[2][2], const lds_t* kc,
+                                        const lds_t* kn, const lds_t* vn, int key0) {
+  constexpr int NG = 16;
+  bf16x8 fa[NG], fc[DB];
+  auto load_a = [&](int gi) {  // fragment used by the two MFMAs of group gi
+    const int kb = gi / 8, i = 2 * (gi % 8), ks = i / 4;
+    fa[gi] = ((i / 2) & 1)
+                 ? *reinterpret_cast<const lds_bf16x8*>(vn - x.vbase + 16 * kb * ROWB + x.va[ks])
+                 : *reinterpret_cast<const lds_bf16x8*>(kn - x.kbase + 16 * kb * ROWB + x.ka[ks]);
+  };
+  auto load_c = [&](int db) { fc[db] = tr_frag(kc - x.kbase + x.kt[db]); };
   bf16x8 dsp[2];
+  float ds[16];
+  load_a(0);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int gi = 0; gi < NG; ++gi) {
+    if (gi + 1 < NG) load_a(gi + 1);
+    if (gi >= 7 && gi - 7 < DB) load_c(gi - 7);  // used one group later
+    {
+      const int kb = gi / 8, i0 = 2 * (gi % 8);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float p = __builtin_amdgcn_exp2f(fmaf(S[kb][qb][r], c, -x.lse2[qb]));
-        if (MASK && k0 + 32 * st + 16 * kb + 4 * x.g + r >= Nkv) p = 0.f;
-        dsp[qb][4 * kb + r] = (__bf16)(p * dP[kb][qb][r]);
+      for (int u = 0; u < 2; ++u) {
+        const int i = i0 + u, ks = i / 4, qb = i % 2;
+        if ((i / 2) & 1)
+          dPn[kb][qb] = mfma16(fa[gi], x.o[qb][ks], ks ? dPn[kb][qb] : x.ndel[qb]);
+        else
+          Sn[kb][qb] = mfma16(fa[gi], x.q[qb][ks], ks ? Sn[kb][qb] : f32x4{});
       }
-  // dQ^T += K^T dS^T; k index 8g + j <-> key 4g + j (j < 4), 16 + 4g + j - 4 (j >= 4).
+    }
+    if (gi < 8) {
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    const bf16x8 akt = tr_frag(ks_ + (x.trb ^ (32 * db)));
+      for (int u = 0; u < 2; ++u) {
+        const int e = 2 * gi + u, qb = e / 8, kb = (e / 4) % 2, r = e % 4;
+        float sv = Sc[kb][qb][r];
+        asm volatile("" : "+v"(sv));
+        float p = __builtin_amdgcn_exp2f(fmaf(sv, x.c, -x.lse2[qb]));
+        if (MASK && key0 + 16 * kb + 4 * x.g + r >= x.Nkv) p = 0.f;
+        ds[e] = p * dPc[kb][qb][r];
+        if (u == 1) {
+          bf16x2 pk = {(__bf16)ds[e - 1], (__bf16)ds[e]};
+          asm volatile("" : "+v"(pk));
+          dsp[qb][4 * kb + r - 1] = pk[0];
+          dsp[qb][4 * kb + r] = pk[1];
+        }
+      }
+    } else {
+      // dQ^T += K^T dS^T; k index 8g + j <-> key 4g + j (j < 4), 16 + 4g + j - 4 (j >= 4).
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) x.dq[qb][db] = mfma16(akt, dsp[qb], x.dq[qb][db]);
+      for (int u = 0; u < 2; ++u) {
+        const int j = 2 * (gi - 8) + u, db = j / 2, qb = j % 2;
+        x.dq[qb][db] = mfma16(fc[db], dsp[qb], x.dq[qb][db]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-struct KStages {
-  lds_t *k0, *k1, *v0, *v1;
-};
+__device__ __forceinline__ void stage_kv_tile(const QCtx& x, int t, int st) {
+  stage_rows(x.Kb, t * TR, x.Nkv, KQST(x, st), x.wave, x.voff);
+  stage_rows(x.Vb, t * TR, x.Nkv, VQST(x, st), x.wave, x.voff);
+}
 
-template <int ST, bool MASK>
-__device__ __forceinline__ void dq_tile(QCtx& x, const KStages& s, int t, int ntiles,
-                                        const __bf16* Kb, const __bf16* Vb, int Nkv, int wave,
-                                        const int* voff, float c) {
-  if (t + 1 < ntiles) {
-    stage_rows(Kb, (t + 1) * TR, Nkv, ST ? s.k0 : s.k1, wave, voff);
-    stage_rows(Vb, (t + 1) * TR, Nkv, ST ? s.v0 : s.v1, wave, voff);
-  }
-  const lds_t* kt = ST ? s.k1 : s.k0;
-  const lds_t* vt = ST ? s.v1 : s.v0;
-  dq_step<MASK>(x, kt, vt, 0, t * TR, Nkv, c);
-  dq_step<MASK>(x, kt, vt, 1, t * TR, Nkv, c);
-  tile_barrier();
+// Key tile t = steps 2t and 2t+1.  On entry S0 / dP0 hold step 2t; on exit
+// they hold step 2t+2 (past the last tile: unused).
+template <int PH, bool MASK>
+__device__ __forceinline__ void dq_tile(QCtx& x, int t, f32x4 (&S0)[2][2], f32x4 (&dP0)[2][2],
+                                        f32x4 (&S1)[2][2], f32x4 (&dP1)[2][2]) {
+  tile_barrier();  // tile t+1 landed; every wave is done with tile t-1
+  const int sc = kv_stage_at(PH, t, 0), sn = kv_stage_at(PH, t, 1);
+  if (t + 2 < x.ntiles) stage_kv_tile(x, t + 2, kv_stage_at(PH, t, 2));
+  const lds_t* kc = KQST(x, sc);
+  const lds_t* vc = VQST(x, sc);
+  dq_slot<MASK>(x, S0, dP0, S1, dP1, kc, kc + 32 * ROWB, vc + 32 * ROWB, t * TR);
+  dq_slot<MASK>(x, S1, dP1, S0, dP0, kc + 32 * ROWB, KQST(x, sn), VQST(x, sn), t * TR + 32);
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -547,8 +615,10 @@ void dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                float scale) {
   __shared__ __attribute__((aligned(1024))) char k0s[TILE];
   __shared__ __attribute__((aligned(1024))) char k1s[TILE];
+  __shared__ __attribute__((aligned(1024))) char k2s[TILE];
   __shared__ __attribute__((aligned(1024))) char v0s[TILE];
   __shared__ __attribute__((aligned(1024))) char v1s[TILE];
+  __shared__ __attribute__((aligned(1024))) char v2s[TILE];
 
   const int tile = remap_xcd(blockIdx.x, total);
   const int bh = tile / n_qtiles;
@@ -556,11 +626,20 @@ void dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15, g = lane >> 4;
-  const __bf16* Kb = K + (int64_t)bh * Nkv * D;
-  const __bf16* Vb = V + (int64_t)bh * Nkv * D;
 
   QCtx x;
   x.g = g;
+  x.lane = lane;
+  x.wave = wave;
+  x.Nkv = Nkv;
+  x.ntiles = (Nkv + TR - 1) / TR;
+  x.c = c;
+  x.Kb = K + (int64_t)bh * Nkv * D;
+  x.Vb = V + (int64_t)bh * Nkv * D;
+  x.k0 = (lds_t*)k0s; x.k1 = (lds_t*)k1s; x.k2 = (lds_t*)k2s;
+  x.v0 = (lds_t*)v0s; x.v1 = (lds_t*)v1s; x.v2 = (lds_t*)v2s;
+  x.kbase = (int)(size_t)x.k0;
+  x.vbase = (int)(size_t)x.v0;
   const int qrow0 = qt * QUERIES_PER_WG + wave * 32 + c16;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -578,33 +657,34 @@ void dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     for (int db = 0; db < DB; ++db) x.dq[qb][db] = f32x4{};
   }
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) x.aoff[ks] = a_off(c16, g, ks);
-  x.trb = tr_base(lane);
-  int voff[PIECES / kWaves];
-  piece_offsets(voff, wave, lane);
+  for (int ks = 0; ks < KS; ++ks) {
+    x.ka[ks] = a_off(c16, g, ks) + x.kbase;
+    x.va[ks] = a_off(c16, g, ks) + x.vbase;
+    asm volatile("" : "+v"(x.ka[ks]), "+v"(x.va[ks]));
+  }
+  const int trb = tr_base(lane);
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    x.kt[db] = (trb ^ (32 * db)) + x.kbase;
+    asm volatile("" : "+v"(x.kt[db]));
+  }
+  piece_offsets(x.voff, wave, lane);
 
-  KStages s{(lds_t*)k0s, (lds_t*)k1s, (lds_t*)v0s, (lds_t*)v1s};
-  const int ntiles = (Nkv + TR - 1) / TR;
-  stage_rows(Kb, 0, Nkv, s.k0, wave, voff);
-  stage_rows(Vb, 0, Nkv, s.v0, wave, voff);
-  tile_barrier();
+  stage_kv_tile(x, 0, 0);
+  if (x.ntiles > 1) stage_kv_tile(x, 1, 1);
+  tile_barrier();  // tiles 0 and 1 landed
+  f32x4 S0[2][2], dP0[2][2], S1[2][2], dP1[2][2];
+  sdpt_step(x, S0, dP0, x.k0, x.v0);
   const bool partial = (Nkv % TR) != 0;
-  const int nfull = partial ? ntiles - 1 : ntiles;
+  const int nfull = partial ? x.ntiles - 1 : x.ntiles;
   int t = 0;
-  for (; t + 2 <= nfull; t += 2) {
-    dq_tile<0, false>(x, s, t, ntiles, Kb, Vb, Nkv, wave, voff, c);
-    dq_tile<1, false>(x, s, t + 1, ntiles, Kb, Vb, Nkv, wave, voff, c);
+  for (; t + 3 <= nfull; t += 3) {
+    dq_tile<0, false>(x, t, S0, dP0, S1, dP1);
+    dq_tile<1, false>(x, t + 1, S0, dP0, S1, dP1);
+    dq_tile<2, false>(x, t + 2, S0, dP0, S1, dP1);
   }
-  if (t < nfull) {
-    dq_tile<0, false>(x, s, t, ntiles, Kb, Vb, Nkv, wave, voff, c);
-    ++t;
-  }
-  if (partial) {
-    if ((t & 1) == 0)
-      dq_tile<0, true>(x, s, t, ntiles, Kb, Vb, Nkv, wave, voff, c);
-    else
-      dq_tile<1, true>(x, s, t, ntiles, Kb, Vb, Nkv, wave, voff, c);
-  }
+  for (; t < nfull; ++t) dq_tile<-1, false>(x, t, S0, dP0, S1, dP1);
+  if (partial) dq_tile<-1, true>(x, t, S0, dP0, S1, dP1);
 
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
