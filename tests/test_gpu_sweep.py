@@ -1,0 +1,120 @@
+"""A seeded sweep of ragged shapes through every forward variant and the
+backward, compared in full with the oracle.
+
+Forty shapes drawn once from a fixed seed: B in {1, 2}, H in {1, 2, 3}, query
+and key counts from 1 to 700, one in five of them from 1 to 8 (so partial key
+tiles, partial query tiles and single tokens meet in every combination), D in
+{32, 64, 128} with half the draws at 128, an explicit softmax scale half the
+time.  Each goes through the bf16 kernel with bf16 and with float32 O, the
+float32-input kernel, the FP8 kernel (D = 128; codes made by the oracle), and
+the merge of the bf16 kernel's float32 partials over two key blocks; sixteen
+more shapes (D = 128) go through the backward.  Every output element is
+compared with the fp64 oracle at the tolerances of the other parity tests.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+import diffusion_transformer_attention_amd as dta
+from _helpers import F32_MAX_ABS, assert_bf16_close, bits_to_torch_bf16, max_abs, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+def _shapes():
+    r = np.random.default_rng(2024)
+    out = []
+    for i in range(40):
+        B, H = int(r.integers(1, 3)), int(r.integers(1, 4))
+        Nq, Nkv = (int(r.integers(1, 9)) if r.random() < 0.2 else int(r.integers(1, 701))
+                   for _ in range(2))
+        D = int(r.choice([32, 64, 128], p=[0.25, 0.25, 0.5]))
+        scale = None if r.random() < 0.5 else float(r.uniform(0.02, 0.3))
+        out.append((i, B, H, Nq, Nkv, D, scale))
+    return out
+
+
+SHAPES = _shapes()
+
+
+def _f64(bits):
+    return datagen.bf16_to_f32(bits).astype(np.float64)
+
+
+@pytest.mark.parametrize("i,B,H,Nq,Nkv,D,scale", SHAPES)
+def test_sweep(i, B, H, Nq, Nkv, D, scale):
+    say(f"sweep {i}: B{B} H{H} Nq{Nq} Nkv{Nkv} D{D} scale {scale}")
+    qb, kb, vb = datagen.small_bf16(B, H, Nq, D, seed=1000 + i, Nkv=Nkv)
+    q, k, v = (bits_to_torch_bf16(x) for x in (qb, kb, vb))
+    Oref, Lref = oracle.attention(_f64(qb), _f64(kb), _f64(vb), scale)
+
+    O, L = dta.dit_attn_fwd_block(q, k, v, scale=scale, out_dtype=torch.bfloat16)
+    assert_bf16_close(to_f64(O), to_f64(L), Oref, Lref, f"sweep {i} bf16 out")
+    O32, L32 = dta.dit_attn_fwd_block(q, k, v, scale=scale, out_dtype=torch.float32)
+    assert_bf16_close(to_f64(O32), to_f64(L32), Oref, Lref, f"sweep {i} f32 out")
+
+    # float32 inputs (the same values), float32 kernel
+    qf, kf, vf = (t.float() for t in (q, k, v))
+    Of, Lf = dta.dit_attn_fwd_block(qf, kf, vf, scale=scale, out_dtype=torch.float32)
+    assert max_abs(to_f64(Of), Oref) <= F32_MAX_ABS and max_abs(to_f64(Lf), Lref) <= F32_MAX_ABS
+
+    # two key blocks merged (Ring)
+    if Nkv >= 2:
+        cut = Nkv // 2
+        parts = [dta.dit_attn_fwd_block(q, k[:, :, a:b].contiguous(), v[:, :, a:b].contiguous(),
+                                        scale=scale, out_dtype=torch.float32)
+                 for a, b in ((0, cut), (cut, Nkv))]
+        Om, Lm = dta.dit_attn_merge(torch.stack([p[0] for p in parts]),
+                                    torch.stack([p[1] for p in parts]), out_dtype=torch.bfloat16)
+        assert_bf16_close(to_f64(Om), to_f64(Lm), Oref, Lref, f"sweep {i} merged")
+
+    # FP8 (head dim 128): codes and descales from the oracle
+    if D == 128:
+        qc, qd = oracle.quantize_fp8(datagen.bf16_to_f32(qb))
+        kc, kd = oracle.quantize_fp8(datagen.bf16_to_f32(kb))
+        O8, L8 = dta.dit_attn_fwd_fp8(torch.from_numpy(qc).cuda(), torch.from_numpy(kc).cuda(), v,
+                                      torch.from_numpy(qd).cuda(), torch.from_numpy(kd).cuda(),
+                                      scale=scale)
+        O8r, L8r = oracle.attention_fp8(qc, kc, _f64(vb), qd, kd, scale)
+        assert_bf16_close(to_f64(O8), to_f64(L8), O8r, L8r, f"sweep {i} fp8")
+
+
+GRAD_REL_RMS, GRAD_MAX_ABS_REL = 1e-2, 3e-2  # the backward parity test's bands
+
+
+def _bwd_shapes():
+    r = np.random.default_rng(4048)
+    out = []
+    for i in range(16):
+        B, H = int(r.integers(1, 3)), int(r.integers(1, 4))
+        Nq, Nkv = (int(r.integers(1, 9)) if r.random() < 0.2 else int(r.integers(1, 701))
+                   for _ in range(2))
+        scale = None if r.random() < 0.5 else float(r.uniform(0.02, 0.3))
+        out.append((i, B, H, Nq, Nkv, scale))
+    return out
+
+
+@pytest.mark.parametrize("i,B,H,Nq,Nkv,scale", _bwd_shapes())
+def test_sweep_backward(i, B, H, Nq, Nkv, scale):
+    say(f"bwd sweep {i}: B{B} H{H} Nq{Nq} Nkv{Nkv} scale {scale}")
+    qb, kb, vb = datagen.small_bf16(B, H, Nq, 128, seed=3000 + i, Nkv=Nkv)
+    dob = datagen.small_bf16(B, H, Nq, 128, seed=5000 + i)[0]
+    q, k, v, do = (bits_to_torch_bf16(x) for x in (qb, kb, vb, dob))
+    O, L = dta.dit_attn_fwd_block(q, k, v, scale=scale, out_dtype=torch.bfloat16)
+    dq, dk, dv, delta = dta.dit_attn_bwd(q, k, v, O, do, L, scale=scale)
+    refs = oracle.attention_backward(_f64(qb), _f64(kb), _f64(vb), _f64(dob), scale)
+    for got, ref, n in zip((dq, dk, dv, delta), refs, ("dq", "dk", "dv", "delta")):
+        err = to_f64(got) - ref
+        rr = float(np.linalg.norm(err.ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300))
+        ma = float(np.abs(err).max() / max(np.abs(ref).max(), 1e-300))
+        assert rr <= GRAD_REL_RMS, f"bwd sweep {i} {n} rel-RMS {rr:.3e}"
+        if n != "delta":
+            assert ma <= GRAD_MAX_ABS_REL, f"bwd sweep {i} {n} max-abs {ma:.3e}"
