@@ -322,7 +322,36 @@ def main():
         nlv = lv[0].shape[2]
         legs.update({"long_video_ms": lv_ms,
                      "long_video_TFLOPs": attn_flops(1, 10, nlv, nlv, D) / (lv_ms * 1e-3) / 1e12})
-        del lv, lo, ll
+        # the same with the work-balanced entry point: 2960 query tiles are
+        # 11.56 waves of 256 workgroups; the last partial wave's tiles run as
+        # key chunks merged by log-sum-exp
+        nws = dta.dit_attn_fwd_balanced_workspace(1, 10, nlv, nlv, D)
+        lws = torch.empty((max(nws, 1),), device=dev, dtype=torch.uint8)
+        lvb_ms = time_it(lambda: dta.dit_attn_fwd_balanced(lv[0], lv[1], lv[2], out=lo, lse=ll,
+                                                            workspace=lws), reps=3)
+        legs.update({"long_video_balanced_ms": lvb_ms,
+                     "long_video_balanced_TFLOPs":
+                         attn_flops(1, 10, nlv, nlv, D) / (lvb_ms * 1e-3) / 1e12,
+                     "long_video_balanced_workspace_MB": nws / 1e6})
+        del lv, lo, ll, lws
+
+        # image share: FLUX 1024^2 image tokens, [1,24,4096,128] -- 384 query
+        # tiles, 1.5 waves: plain and work-balanced
+        print("[bench] image share leg", file=sys.stderr, flush=True)
+        im = [to_dev(x) for x in datagen.workload_inputs("image_share")]
+        io = torch.empty_like(im[0])
+        il = torch.empty(im[0].shape[:3], device=dev, dtype=torch.float32)
+        nim = im[0].shape[2]
+        im_ms = time_it(lambda: dta.dit_attn_fwd(im[0], im[1], im[2], out=io, lse=il), reps=20)
+        nws = dta.dit_attn_fwd_balanced_workspace(1, 24, nim, nim, D)
+        iws = torch.empty((max(nws, 1),), device=dev, dtype=torch.uint8)
+        imb_ms = time_it(lambda: dta.dit_attn_fwd_balanced(im[0], im[1], im[2], out=io, lse=il,
+                                                            workspace=iws), reps=20)
+        imf = attn_flops(1, 24, nim, nim, D)
+        legs.update({"image_share_ms": im_ms, "image_share_TFLOPs": imf / (im_ms * 1e-3) / 1e12,
+                     "image_share_balanced_ms": imb_ms,
+                     "image_share_balanced_TFLOPs": imf / (imb_ms * 1e-3) / 1e12})
+        del im, io, il, iws
 
     if not args.no_ring:
         print("[bench] ring leg", file=sys.stderr, flush=True)

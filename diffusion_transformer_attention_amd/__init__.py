@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libditattn.so")
 
 DIT_BF16, DIT_F32 = 0, 1
 DIT_OK, DIT_EINVAL, DIT_EUNSUPPORTED, DIT_EALIGN, DIT_ELAUNCH, DIT_ERANGE = 0, -1, -2, -3, -4, -5
-EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_ulysses", "dit_attn_bwd",
+EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_balanced",
+            "dit_attn_fwd_balanced_workspace", "dit_attn_fwd_ulysses", "dit_attn_bwd",
             "dit_attn_merge", "dit_rope_pack", "dit_attn_fwd_joint", "dit_quant_fp8",
             "dit_attn_fwd_fp8", "ulysses_seq2head", "ulysses_head2seq", "dit_strerror",
             "dit_abi_version")
@@ -42,6 +43,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dit_attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P]
     lib.dit_attn_fwd_block.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, P]
     lib.dit_attn_fwd_ulysses.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, P]
+    lib.dit_attn_fwd_balanced.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, P,
+                                          ctypes.c_size_t, P]
+    lib.dit_attn_fwd_balanced_workspace.argtypes = [I, I, I, I, I, I,
+                                                    ctypes.POINTER(ctypes.c_size_t)]
     lib.dit_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P]
     lib.dit_attn_merge.argtypes = [P, P, I, P, P, I, I, I, I, I, P]
     lib.dit_quant_fp8.argtypes = [P, P, P, I, I, I, I, P]
@@ -51,9 +56,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                        I, I, I, I, I, I, I, F, P]
     lib.ulysses_seq2head.argtypes = [P, P, I, I, I, I, I, I, P]
     lib.ulysses_head2seq.argtypes = [P, P, I, I, I, I, I, I, P]
-    for name in ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_ulysses", "dit_attn_bwd",
+    for name in ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_balanced",
+                 "dit_attn_fwd_balanced_workspace", "dit_attn_fwd_ulysses", "dit_attn_bwd",
                  "dit_attn_merge", "dit_rope_pack", "dit_attn_fwd_joint", "dit_quant_fp8",
-           "dit_attn_fwd_fp8", "ulysses_seq2head", "ulysses_head2seq", "dit_abi_version"):
+                 "dit_attn_fwd_fp8", "ulysses_seq2head", "ulysses_head2seq", "dit_abi_version"):
         getattr(lib, name).restype = ctypes.c_int
     lib.dit_strerror.argtypes = [ctypes.c_int]
     lib.dit_strerror.restype = ctypes.c_char_p
@@ -160,6 +166,56 @@ def dit_attn_fwd_block(q, k, v, scale=None, out_dtype=torch.float32, out=None, l
                                 ctypes.c_float(scale), _dtype_code(q.dtype),
                                 _dtype_code(o.dtype), _stream())
     _check(rc, "dit_attn_fwd_block")
+    return o, lse
+
+
+def dit_attn_fwd_balanced_workspace(B, H, Nq, Nkv, D, slots=0):
+    """Workspace bytes dit_attn_fwd_balanced needs (0: no split for these sizes)."""
+    n = ctypes.c_size_t(0)
+    _check(load_library().dit_attn_fwd_balanced_workspace(B, H, Nq, Nkv, D, int(slots),
+                                                         ctypes.byref(n)),
+           "dit_attn_fwd_balanced_workspace")
+    return int(n.value)
+
+
+def dit_attn_fwd_balanced(q, k, v, scale=None, out_dtype=torch.bfloat16, out=None, lse=None,
+                          return_lse=True, slots=0, workspace=None):
+    """Work-balanced forward of bf16 q [B,H,Nq,D] against k, v [B,H,Nkv,D].
+
+    ``workspace``: a uint8 device tensor of at least
+    dit_attn_fwd_balanced_workspace(...) bytes, allocated here when None.
+    Returns (O [B,H,Nq,D] in out_dtype, LSE float32 [B,H,Nq] or None).
+    """
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, 4)
+    B, H, Nq, D = q.shape
+    Nkv = k.shape[2]
+    if k.shape != v.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != D:
+        raise ValueError("k, v must be [B,H,Nkv,D] matching q")
+    if not (q.dtype == k.dtype == v.dtype == torch.bfloat16):
+        raise ValueError("q, k, v must be bf16")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o = torch.empty((B, H, Nq, D), device=q.device, dtype=out_dtype) if out is None else out
+    _need(o, "out", 4)
+    if tuple(o.shape) != (B, H, Nq, D):
+        raise ValueError("out must be [B,H,Nq,D]")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Nq), device=q.device, dtype=torch.float32)
+    if lse is not None:
+        _need(lse, "lse", 3)
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq):
+            raise ValueError("lse must be float32 [B,H,Nq]")
+    if workspace is None:
+        nbytes = dit_attn_fwd_balanced_workspace(B, H, Nq, Nkv, D, slots)
+        workspace = torch.empty((max(nbytes, 1),), device=q.device, dtype=torch.uint8)
+    _need(workspace, "workspace", 1)
+    rc = lib.dit_attn_fwd_balanced(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nkv,
+                                   D, ctypes.c_float(scale), _dtype_code(o.dtype), int(slots),
+                                   _ptr(workspace),
+                                   ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                   _stream())
+    _check(rc, "dit_attn_fwd_balanced")
     return o, lse
 
 

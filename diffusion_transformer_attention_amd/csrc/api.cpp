@@ -27,6 +27,36 @@ bool size_ok(int64_t a, int64_t b, int64_t c, int64_t d) {
 
 int map_launch(hipError_t e) { return e == hipSuccess ? DIT_OK : DIT_ELAUNCH; }
 
+// Sizes of a balanced forward (bf16 inputs); DIT_OK with *work false when
+// there is nothing to compute.
+int balanced_check(int B, int H, int Nq, int Nkv, int D, float scale, int o_dtype, int slots,
+                   bool* work) {
+  *work = false;
+  if (B < 0 || H < 0 || Nq < 0 || Nkv < 0 || D <= 0 || slots < 0) return DIT_EINVAL;
+  if (!(isfinite(scale) && scale > 0.0f)) return DIT_EINVAL;
+  if (o_dtype != DIT_BF16 && o_dtype != DIT_F32) return DIT_EUNSUPPORTED;
+  if (!supported_head_dim(D)) return DIT_EUNSUPPORTED;
+  if (!size_ok(B, H, Nq, D) || !size_ok(B, H, Nkv, D)) return DIT_ERANGE;
+  if (B == 0 || H == 0 || Nq == 0) return DIT_OK;
+  if (Nkv == 0) return DIT_EINVAL;
+  *work = true;
+  return DIT_OK;
+}
+
+// Concurrent workgroups of the forward kernel: one per compute unit.
+int device_slots(int slots, int* out) {
+  if (slots > 0) {
+    *out = slots;
+    return DIT_OK;
+  }
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return DIT_ELAUNCH;
+  *out = n;
+  return DIT_OK;
+}
+
 int attn_common(const void* q, const void* k, const void* v, void* o, float* lse, bool lse_required,
                 int B, int H, int Nq, int Nkv, int D, float scale, int in_dtype, int o_dtype,
                 void* stream) {
@@ -104,6 +134,38 @@ int dit_attn_fwd_block(const void* q, const void* k, const void* v, void* o, flo
                        int H, int Nq, int Nkv, int D, float scale, int in_dtype, int o_dtype,
                        void* stream) {
   return attn_common(q, k, v, o, lse, true, B, H, Nq, Nkv, D, scale, in_dtype, o_dtype, stream);
+}
+
+int dit_attn_fwd_balanced_workspace(int B, int H, int Nq, int Nkv, int D, int slots,
+                                    size_t* bytes) {
+  if (!bytes) return DIT_EINVAL;
+  *bytes = 0;
+  bool work = false;
+  int rc = balanced_check(B, H, Nq, Nkv, D, 1.0f, DIT_BF16, slots, &work);
+  if (rc != DIT_OK || !work) return rc;
+  int n = 0;
+  if ((rc = device_slots(slots, &n)) != DIT_OK) return rc;
+  *bytes = ditattn::balanced_plan(B, H, Nq, Nkv, D, n).ws_bytes;
+  return DIT_OK;
+}
+
+int dit_attn_fwd_balanced(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                          int H, int Nq, int Nkv, int D, float scale, int o_dtype, int slots,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  bool work = false;
+  int rc = balanced_check(B, H, Nq, Nkv, D, scale, o_dtype, slots, &work);
+  if (rc != DIT_OK || !work) return rc;
+  if (!q || !k || !v || !o) return DIT_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return DIT_EALIGN;
+  if (lse && !aligned(lse, 4)) return DIT_EALIGN;
+  if (workspace && !aligned(workspace, 16)) return DIT_EALIGN;
+  int n = 0;
+  if ((rc = device_slots(slots, &n)) != DIT_OK) return rc;
+  const ditattn::BalancedPlan plan = ditattn::balanced_plan(B, H, Nq, Nkv, D, n);
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return DIT_EINVAL;
+  return map_launch(ditattn::launch_attn_bf16_balanced(q, k, v, o, lse, B, H, Nq, Nkv, D, scale,
+                                                       o_dtype == DIT_F32, plan, workspace,
+                                                       static_cast<hipStream_t>(stream)));
 }
 
 int dit_attn_merge(const float* o_parts, const float* lse_parts, int nblk, void* o, float* lse,

@@ -583,16 +583,28 @@ __device__ __forceinline__ int64_t token_offset(int n, int seg, int64_t head_ele
   return head_elems + sg * sstride + (int64_t)(n - sg * seg) * D;
 }
 
+// Key-split launch (contiguous layout only): grid unit u computes key chunk
+// u % nsplit of query tile tile0 + u / nsplit.  Chunk j holds keys
+// [j*kc, min((j+1)*kc, Nkv)) with kc a multiple of the key tile, and writes
+// its float32 O and LSE over those keys alone to the workspace, chunk-major:
+// O at (j*rows + r - row0)*D, LSE at j*rows + r - row0, for the flat query
+// row r = (b*H + h)*Nq + n.  The partials are then merged by log-sum-exp.
+struct Split {
+  int tile0, nsplit, kc;
+  int64_t row0, rows;
+};
+
 // The kernel body.  F8: q and k are E4M3 codes (1 byte per element) whose
 // scores are rescaled by the per-(b, h) factors qds[bh] * kds[bh]; else q
-// and k are bf16 and qds, kds are unused.
-template <int D, bool OUT_F32, bool F8>
+// and k are bf16 and qds, kds are unused.  SPLIT: a key-split launch (above),
+// total_tiles is then the number of units.
+template <int D, bool OUT_F32, bool F8, bool SPLIT = false>
 __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const void* __restrict__ K,
                                               const __bf16* __restrict__ V, void* __restrict__ Oout,
                                               float* __restrict__ LSE, int Nq, int Nkv,
                                               int n_qtiles, int total_tiles, float c, Layout lay,
                                               const float* __restrict__ qds,
-                                              const float* __restrict__ kds) {
+                                              const float* __restrict__ kds, Split sp = {}) {
   using Gm = Geo<D>;
   using QK = QKOps<D, F8>;
   constexpr int QKB = F8 ? 1 : 2;  // bytes per q / k element
@@ -603,7 +615,14 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
   __shared__ __attribute__((aligned(1024))) char v1s[Gm::TILE];
   __shared__ __attribute__((aligned(1024))) char v2s[Gm::TILE];
 
-  const int tile = remap_xcd(blockIdx.x, total_tiles);
+  int tile = remap_xcd(blockIdx.x, total_tiles), chunk = 0;
+  if (SPLIT) {
+    const int u = tile;
+    tile = sp.tile0 + u / sp.nsplit;
+    chunk = u - (u / sp.nsplit) * sp.nsplit;
+  }
+  const int kbeg = SPLIT ? chunk * sp.kc : 0;  // first key of the chunk
+  if (SPLIT) Nkv = min(sp.kc, Nkv - kbeg);
   const int bh = tile / n_qtiles;
   const int qt = tile - bh * n_qtiles;
   const int lane = threadIdx.x & 63;
@@ -617,9 +636,9 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
   const int64_t qsstride = (int64_t)lay.B * lay.htot * lay.qseg * D;
   if (F8) c *= qds[bh] * kds[bh];
   PassCtx<D, F8> x;
-  x.Kb = static_cast<const char*>(K) + ((int64_t)bb * lay.htot + hh) * lay.kseg * D * QKB;
-  x.Vb = reinterpret_cast<const char*>(V + ((int64_t)bb * lay.htot + hh) * lay.kseg * D);
-  x.kseg = lay.kseg;
+  x.Kb = static_cast<const char*>(K) + (((int64_t)bb * lay.htot + hh) * lay.kseg + kbeg) * D * QKB;
+  x.Vb = reinterpret_cast<const char*>(V + (((int64_t)bb * lay.htot + hh) * lay.kseg + kbeg) * D);
+  x.kseg = lay.kseg - kbeg;
   x.kstride = (int64_t)lay.B * lay.htot * lay.kseg * D * QKB;
   x.vstride = (int64_t)lay.B * lay.htot * lay.kseg * D * 2;
   x.k0 = (lds_t*)k0s; x.k1 = (lds_t*)k1s; x.k2 = (lds_t*)k2s;
@@ -695,7 +714,9 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
     const float inv = 1.0f / f.lb[qb][0];
     const int qrow = qrow0 + 16 * qb;
     if (qrow < Nq) {
-      const int64_t obase = token_offset(qrow, lay.qseg, qhead, qsstride, D);
+      const int64_t wrow = (int64_t)chunk * sp.rows + (int64_t)bh * Nq + qrow - sp.row0;
+      const int64_t obase =
+          SPLIT ? wrow * D : token_offset(qrow, lay.qseg, qhead, qsstride, D);
 #pragma unroll
       for (int db = 0; db < Gm::DB; ++db) {
         const int d0 = db * 16 + 4 * g;
@@ -708,7 +729,7 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
         }
       }
       if (LSE && g == 0)
-        LSE[(int64_t)bh * Nq + qrow] =
+        LSE[SPLIT ? wrow : (int64_t)bh * Nq + qrow] =
             (f.m[qb] * c + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
     }
   }
@@ -722,6 +743,17 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
                           float c, Layout lay) {
   attn_fwd_body<D, OUT_F32, false>(Q, K, V, Oout, LSE, Nq, Nkv, n_qtiles, total_tiles, c, lay,
                                    nullptr, nullptr);
+}
+
+// Key-split partials (float32 O and LSE into the workspace).
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
+void attn_fwd_bf16_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                                const __bf16* __restrict__ V, float* __restrict__ Opart,
+                                float* __restrict__ Lpart, int Nq, int Nkv, int n_qtiles,
+                                int units, float c, Layout lay, Split sp) {
+  attn_fwd_body<D, true, false, true>(Q, K, V, Opart, Lpart, Nq, Nkv, n_qtiles, units, c, lay,
+                                      nullptr, nullptr, sp);
 }
 
 template <bool OUT_F32>
@@ -780,6 +812,98 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
   const Layout lay{Nq, Nkv, H, H, 0, B};
   return o_f32 ? launch_layout<true>(q, k, v, o, lse, Nq, Nkv, D, scale, lay, stream)
                : launch_layout<false>(q, k, v, o, lse, Nq, Nkv, D, scale, lay, stream);
+}
+
+BalancedPlan balanced_plan(int B, int H, int Nq, int Nkv, int D, int slots) {
+  // Costs in key-tile steps of one workgroup (64 keys x 256 rows): a
+  // workgroup's fixed cost (query load, epilogue, the gap before the next) is
+  // about 6 steps; an extra launch about 6; HBM moves ~8 MB per step at
+  // D = 128 (the step shrinks with D).
+  constexpr double kFixed = 6.0, kLaunch = 6.0, kStepBytes = 8.0e6;
+  BalancedPlan pl{};
+  const int n_qtiles = (Nq + kBM - 1) / kBM;
+  const int64_t total = (int64_t)B * H * n_qtiles;
+  const int nt = (Nkv + kBN - 1) / kBN;
+  pl.whole = (int)total;
+  pl.nsplit = 1;
+  if (slots < 1 || total < 1 || nt < 2) return pl;
+  const int64_t whole = total / slots * slots, R = total - whole;
+  if (R == 0) return pl;
+  const double step_bytes = kStepBytes * D / 128.0;
+  auto cost = [&](int per, int s) {  // per key tiles per chunk, s chunks
+    const double waves = (double)((R * s + slots - 1) / slots);
+    double t = waves * (kFixed + per);
+    if (s > 1) t += 2 * kLaunch + (double)R * kBM * s * (D + 1) * 4.0 * 2.0 / step_bytes;
+    return t;
+  };
+  const double c1 = cost(nt, 1);
+  double best = c1;
+  for (int s0 = 2; s0 <= 32 && s0 <= nt; ++s0) {
+    const int per = (nt + s0 - 1) / s0, s = (nt + per - 1) / per;
+    const double t = cost(per, s);
+    if (t < best - 1e-9) {
+      best = t;
+      pl.nsplit = s;
+      pl.kc = per * kBN;
+    }
+  }
+  if (pl.nsplit == 1 || best > 0.97 * c1) {
+    pl.nsplit = 1;
+    pl.kc = 0;
+    return pl;
+  }
+  pl.whole = (int)whole;
+  pl.row0 = (whole / n_qtiles) * (int64_t)Nq + (whole % n_qtiles) * (int64_t)kBM;
+  pl.rows = (int64_t)B * H * Nq - pl.row0;
+  pl.units = (int)(R * pl.nsplit);
+  pl.ws_bytes = (size_t)pl.nsplit * pl.rows * (D + 1) * sizeof(float);
+  return pl;
+}
+
+hipError_t launch_attn_bf16_balanced(const void* q, const void* k, const void* v, void* o,
+                                     float* lse, int B, int H, int Nq, int Nkv, int D, float scale,
+                                     bool o_f32, const BalancedPlan& pl, void* workspace,
+                                     hipStream_t stream) {
+  if (pl.nsplit <= 1)
+    return launch_attn_bf16(q, k, v, o, lse, B, H, Nq, Nkv, D, scale, o_f32, stream);
+  const Layout lay{Nq, Nkv, H, H, 0, B};
+  const float c = scale * 1.4426950408889634f;
+  const int n_qtiles = (Nq + kBM - 1) / kBM;
+  hipError_t e = hipSuccess;
+  if (pl.whole > 0) {  // whole tiles: exact waves of the plain kernel
+    auto run = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3((unsigned)pl.whole), dim3(kThreads), 0, stream,
+                         static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                         static_cast<const __bf16*>(v), o, lse, Nq, Nkv, n_qtiles, pl.whole, c,
+                         lay);
+    };
+    if (o_f32) {
+      if (D == 32) run(attn_fwd_bf16_kernel<32, true>);
+      else if (D == 64) run(attn_fwd_bf16_kernel<64, true>);
+      else run(attn_fwd_bf16_kernel<128, true>);
+    } else {
+      if (D == 32) run(attn_fwd_bf16_kernel<32, false>);
+      else if (D == 64) run(attn_fwd_bf16_kernel<64, false>);
+      else run(attn_fwd_bf16_kernel<128, false>);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  float* opart = static_cast<float*>(workspace);
+  float* lpart = opart + (size_t)pl.nsplit * pl.rows * D;
+  const Split sp{pl.whole, pl.nsplit, pl.kc, pl.row0, pl.rows};
+  auto split = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)pl.units), dim3(kThreads), 0, stream,
+                       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                       static_cast<const __bf16*>(v), opart, lpart, Nq, Nkv, n_qtiles, pl.units,
+                       c, lay, sp);
+  };
+  if (D == 32) split(attn_fwd_bf16_split_kernel<32>);
+  else if (D == 64) split(attn_fwd_bf16_split_kernel<64>);
+  else split(attn_fwd_bf16_split_kernel<128>);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  char* otail = static_cast<char*>(o) + pl.row0 * D * (o_f32 ? 4 : 2);
+  return launch_merge(opart, lpart, pl.nsplit, otail, lse ? lse + pl.row0 : nullptr, pl.rows, D,
+                      o_f32, stream);
 }
 
 hipError_t launch_attn_fp8(const void* q, const void* k, const void* v, const float* q_descale,

@@ -11,6 +11,24 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
                             int B, int H, int Nq, int Nkv, int D, float scale, bool o_f32,
                             hipStream_t stream);
 
+// Work balance of one bf16 forward over `slots` concurrent workgroups: the
+// first `whole` query tiles (a multiple of slots) run whole; the remaining
+// tiles are cut into nsplit key chunks of kc keys (units = tiles * nsplit
+// workgroups) whose float32 partials fill ws_bytes of workspace and are
+// merged into flat query rows [row0, row0 + rows).  nsplit == 1: one plain
+// launch, no workspace.
+struct BalancedPlan {
+  int whole, nsplit, kc, units;
+  int64_t row0, rows;
+  size_t ws_bytes;
+};
+BalancedPlan balanced_plan(int B, int H, int Nq, int Nkv, int D, int slots);
+
+hipError_t launch_attn_bf16_balanced(const void* q, const void* k, const void* v, void* o,
+                                     float* lse, int B, int H, int Nq, int Nkv, int D, float scale,
+                                     bool o_f32, const BalancedPlan& plan, void* workspace,
+                                     hipStream_t stream);
+
 // bf16 q/k/v/o in Ulysses token-shard layout [P][B,H,N/P,D]: attention of
 // head group r (heads [r*H/P, (r+1)*H/P)) over all N tokens.  lse is
 // [B,H/P,N] or null.  Requires (N/P) % 64 == 0.

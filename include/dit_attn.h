@@ -44,6 +44,8 @@
 #ifndef DIT_ATTN_H
 #define DIT_ATTN_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -101,6 +103,44 @@ int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 int dit_attn_fwd_block(const void* q, const void* k, const void* v, void* o, float* lse,
                        int B, int H, int Nq, int Nkv, int D, float scale,
                        int in_dtype, int o_dtype, void* stream);
+
+/*
+ * Work-balanced forward: the same attention as dit_attn_fwd_block (bf16
+ * inputs), computed so that the last, partly filled wave of query tiles does
+ * not leave compute units idle.  The query tiles (256 rows of one head) that
+ * fill whole waves of `slots` concurrent workgroups run as in
+ * dit_attn_fwd_block and give bit-identical rows; each remaining tile is cut
+ * into key chunks whose float32 (O_j, LSE_j) are merged exactly as Ring
+ * blocks are ([HB] Ring paragraph: attention of disjoint key blocks merged
+ * by log-sum-exp), so those rows differ from dit_attn_fwd_block only in
+ * rounding.  The cut depends on B*H, Nq, Nkv, D and slots, never on the data;
+ * two calls with the same arguments give bit-identical results.
+ *
+ *   q        : bf16 [B,H,Nq,D];  k, v : bf16 [B,H,Nkv,D];  D in {32, 64, 128}
+ *   o        : [B,H,Nq,D] in o_dtype (DIT_BF16 or DIT_F32), written
+ *   lse      : float32 [B,H,Nq], written, or NULL to skip
+ *   slots    : concurrent workgroups to plan for; 0 = the current device's
+ *              compute-unit count (one workgroup per compute unit)
+ *   workspace: device memory of at least the size that
+ *              dit_attn_fwd_balanced_workspace reports for the same sizes and
+ *              slots (16-byte aligned; may be NULL when that size is 0);
+ *              caller-owned, overwritten, must not overlap any other argument
+ * Returns DIT_EINVAL when the workspace is missing or too small.  Calls that
+ * share one workspace must be ordered on one stream.
+ */
+int dit_attn_fwd_balanced(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int Nq, int Nkv, int D, float scale, int o_dtype,
+                          int slots, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes dit_attn_fwd_balanced needs for these sizes and slots
+ * (0 when the tiles already fill whole waves or a split would not pay).
+ * Writes *bytes; returns DIT_OK or the error dit_attn_fwd_balanced would give
+ * for the sizes.  slots = 0 queries the current device (a host-side HIP
+ * attribute query; DIT_ELAUNCH if it fails).
+ */
+int dit_attn_fwd_balanced_workspace(int B, int H, int Nq, int Nkv, int D, int slots,
+                                    size_t* bytes);
 
 /*
  * Attention backward: the gradients of sum(dout * O) for O = attention(q, k, v)

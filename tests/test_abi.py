@@ -78,6 +78,33 @@ def test_block_validation(lib):
     assert blk(lib, Nq=0) == dta.DIT_OK                  # nothing to compute
 
 
+def test_balanced_workspace_and_validation(lib):
+    n = ctypes.c_size_t(7)
+    size = lambda B=1, H=10, Nq=75600, Nkv=75600, D=128, slots=256: (
+        lib.dit_attn_fwd_balanced_workspace(B, H, Nq, Nkv, D, slots, ctypes.byref(n)), n.value)
+    assert size(Nq=32768, Nkv=32768) == (dta.DIT_OK, 0)   # 1280 tiles: five whole waves of 256
+    rc, need = size()                                      # 2960 tiles: 11.56 waves, tail split
+    assert rc == dta.DIT_OK and need > 0 and need % (4 * 129) == 0
+    assert size(Nkv=64) == (dta.DIT_OK, 0)                 # one key tile: nothing to split
+    assert size(Nq=0) == (dta.DIT_OK, 0)
+    assert size(D=96)[0] == dta.DIT_EUNSUPPORTED
+    assert size(slots=-1)[0] == dta.DIT_EINVAL
+    assert size(Nkv=0)[0] == dta.DIT_EINVAL
+    assert lib.dit_attn_fwd_balanced_workspace(1, 1, 64, 64, 128, 256, None) == dta.DIT_EINVAL
+    bal = lambda ws=A, nb=need, o=A, od=0, Nq=75600, Nkv=75600, scale=0.125, slots=256: \
+        lib.dit_attn_fwd_balanced(A, A, A, o, A, 1, 10, Nq, Nkv, 128, ctypes.c_float(scale), od,
+                                  slots, ws, nb, S)
+    assert bal(nb=need - 1) == dta.DIT_EINVAL              # workspace too small
+    assert bal(ws=NULL) == dta.DIT_EINVAL
+    assert bal(ws=MIS) == dta.DIT_EALIGN
+    assert bal(o=NULL) == dta.DIT_EINVAL
+    assert bal(od=5) == dta.DIT_EUNSUPPORTED
+    assert bal(scale=0.0) == dta.DIT_EINVAL
+    assert bal(Nkv=0) == dta.DIT_EINVAL
+    assert bal(slots=-2) == dta.DIT_EINVAL
+    assert bal(Nq=0, ws=NULL) == dta.DIT_OK                # nothing to compute
+
+
 def test_merge_validation(lib):
     m = lambda nblk=4, o=A, op=A, lp=A, D=128, od=0, N=64: lib.dit_attn_merge(
         op, lp, nblk, o, A, 1, 2, N, D, od, S)

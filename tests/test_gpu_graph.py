@@ -4,7 +4,9 @@ The entry points enqueue kernels only (no allocation, copy or memset) on the
 caller's stream, so a caller can capture a whole step once and replay it.
 The step captured here: the Ulysses round trip (seq2head, attention of each
 head group with LSE, head2seq), the backward of head group 0, per-head FP8
-quantization followed by FP8 attention, and a joint text + image call.  It is
+quantization followed by FP8 attention, a joint text + image call and a
+work-balanced call that takes its key-split path (its device query runs
+under capture too).  It is
 replayed three times, with unrelated eager launches and synchronizations in
 between, and every replay must reproduce the eager outputs bit for bit (the
 kernels are deterministic, so any difference would come from the capture).
@@ -40,7 +42,8 @@ def _inputs():
     ct, st = datagen.rope_tables_text(77, 5, 64, D)
     tabs = [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (ct, st)] + tabs
     joint = [bits_to_torch_bf16(x) for x in txt + img]
-    return shards, dout, joint, tabs
+    bal = [torch.randn(1, 2, n, D, generator=g).to(torch.bfloat16).cuda() for n in (256, 4096, 4096)]
+    return shards, dout, joint + [bal], tabs
 
 
 def _buffers(shards):
@@ -63,6 +66,10 @@ def _buffers(shards):
         "oj": torch.empty((B, H, 377, D), device="cuda", dtype=torch.bfloat16),
         "lj": torch.empty((B, H, 377), device="cuda", dtype=torch.float32),
         "ws": torch.empty((3, B, H, 377, D), device="cuda", dtype=torch.bfloat16),
+        "ob": torch.empty((1, 2, 256, D), device="cuda", dtype=torch.bfloat16),
+        "lb": torch.empty((1, 2, 256), device="cuda", dtype=torch.float32),
+        "wb": torch.empty((dta.dit_attn_fwd_balanced_workspace(1, 2, 256, 4096, D),),
+                          device="cuda", dtype=torch.uint8),
     }
 
 
@@ -79,11 +86,13 @@ def _step(shards, dout, joint, tabs, b):
     dta.dit_quant_fp8(q0, codes=b["qc"], descale=b["qd"])
     dta.dit_quant_fp8(k0, codes=b["kc"], descale=b["kd"])
     dta.dit_attn_fwd_fp8(b["qc"], b["kc"], v0, b["qd"], b["kd"], out=b["o8"], lse=b["l8"])
-    dta.dit_attn_fwd_joint(*joint, *tabs, out=b["oj"], lse=b["lj"], workspace=b["ws"])
+    dta.dit_attn_fwd_joint(*joint[:6], *tabs, out=b["oj"], lse=b["lj"], workspace=b["ws"])
+    dta.dit_attn_fwd_balanced(*joint[6], out=b["ob"], lse=b["lb"], workspace=b["wb"])
 
 
 def _snapshot(b):
-    keys = ("back", "lse", "dq", "dk", "dv", "delta", "qc", "kc", "qd", "kd", "o8", "l8", "oj", "lj")
+    keys = ("back", "lse", "dq", "dk", "dv", "delta", "qc", "kc", "qd", "kd", "o8", "l8", "oj", "lj",
+            "ob", "lb")
     return {k: b[k].clone() for k in keys}
 
 
