@@ -101,6 +101,15 @@ def small_bf16(B, H, N, D, seed, Nkv=None):
     return bf16_bits(q), bf16_bits(k), bf16_bits(v)
 
 
+def device_normal_bf16(shape, seed, device="cuda"):
+    """N(0,1) bf16 tensor drawn on the device by torch's seeded generator
+    (for tensors too large to draw on the host; the oracle gets the slices it
+    needs copied back)."""
+    import torch
+    g = torch.Generator(device=device).manual_seed(seed)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.bfloat16)
+
+
 def small_f32(B, H, N, D, seed, Nkv=None):
     """Plain N(0,1) float32 q [B,H,N,D] and k, v [B,H,Nkv,D]."""
     Nkv = N if Nkv is None else Nkv

@@ -213,7 +213,7 @@ __device__ __forceinline__ void tile_barrier() {
 // rows, sstride bytes apart (a single segment unless the keys come from
 // Ulysses token shards, whose length is then a multiple of the tile).  The
 // descriptor covers the tile's rows up to the end of its segment, so rows
-// past the end read as zero.
+// past the end read as zero (its 32-bit size is at most one tile).
 template <int ROWB, int PIECES>
 __device__ __forceinline__ void stage_tile(const char* __restrict__ G, int k0, int kseg,
                                            int64_t sstride, lds_t* buf, int wave, const int* voff) {
@@ -224,7 +224,7 @@ __device__ __forceinline__ void stage_tile(const char* __restrict__ G, int k0, i
     G += sg * sstride;
   }
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(G + (int64_t)local * ROWB), (short)0, (kseg - local) * ROWB, 0x00020000);
+      (void*)(G + (int64_t)local * ROWB), (short)0, min(kseg - local, kBN) * ROWB, 0x00020000);
 #pragma unroll
   for (int n = 0; n < (PIECES + kWaves - 1) / kWaves; ++n) {
     const int inst = n * kWaves + wave;

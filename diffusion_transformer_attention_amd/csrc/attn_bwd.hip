@@ -102,11 +102,12 @@ __device__ __forceinline__ void tile_barrier() {
 
 // Stage rows [r0, r0 + 64) of a [rows, D] bf16 matrix into a swizzled LDS
 // tile: LDS slot pc of row r holds chunk pc ^ swz(r).  The descriptor ends at
-// row nrows, so rows past the end arrive as zeros.
+// row min(nrows, r0 + TR), so rows past the end arrive as zeros (and its
+// 32-bit size stays within one tile).
 __device__ __forceinline__ void stage_rows(const __bf16* G, int r0, int nrows, lds_t* buf,
                                            int wave, const int* voff) {
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(G + (int64_t)r0 * D), (short)0, (nrows - r0) * ROWB, 0x00020000);
+      (void*)(G + (int64_t)r0 * D), (short)0, min(nrows - r0, TR) * ROWB, 0x00020000);
 #pragma unroll
   for (int n = 0; n < PIECES / kWaves; ++n)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -117,7 +118,7 @@ __device__ __forceinline__ void stage_rows(const __bf16* G, int r0, int nrows, l
 // Stage 64 floats (rows [r0, r0 + 64) of a row vector) into LDS, lane l -> row r0 + l.
 __device__ __forceinline__ void stage_vec(const float* G, int r0, int nrows, lds_f32* buf, int lane) {
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(G + r0), (short)0, (nrows - r0) * 4, 0x00020000);
+      (void*)(G + r0), (short)0, min(nrows - r0, TR) * 4, 0x00020000);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)buf, 4,
                                            4 * lane, 0, 0, 0);
 }
