@@ -82,6 +82,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kQB = 2;                  // 16-row query blocks per wave
 constexpr int kBM = 16 * kQB * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;                 // keys per LDS tile (two 32-key slots)
+static_assert(kBM == kFwdQueryTile && kBN == kFwdKeyTile, "launch.h tile sizes");
 constexpr int kStages = 3;              // LDS stages for K and for V (tile t uses stage t % 3)
 constexpr float kMaxSum = 1099511627776.0f;  // 2^40: a larger row sum means the pass must be redone
 
@@ -812,52 +813,6 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
   const Layout lay{Nq, Nkv, H, H, 0, B};
   return o_f32 ? launch_layout<true>(q, k, v, o, lse, Nq, Nkv, D, scale, lay, stream)
                : launch_layout<false>(q, k, v, o, lse, Nq, Nkv, D, scale, lay, stream);
-}
-
-BalancedPlan balanced_plan(int B, int H, int Nq, int Nkv, int D, int slots) {
-  // Costs in key-tile steps of one workgroup (64 keys x 256 rows): a
-  // workgroup's fixed cost (query load, epilogue, the gap before the next) is
-  // about 6 steps; an extra launch about 6; HBM moves ~8 MB per step at
-  // D = 128 (the step shrinks with D).
-  constexpr double kFixed = 6.0, kLaunch = 6.0, kStepBytes = 8.0e6;
-  BalancedPlan pl{};
-  const int n_qtiles = (Nq + kBM - 1) / kBM;
-  const int64_t total = (int64_t)B * H * n_qtiles;
-  const int nt = (Nkv + kBN - 1) / kBN;
-  pl.whole = (int)total;
-  pl.nsplit = 1;
-  if (slots < 1 || total < 1 || nt < 2) return pl;
-  const int64_t whole = total / slots * slots, R = total - whole;
-  if (R == 0) return pl;
-  const double step_bytes = kStepBytes * D / 128.0;
-  auto cost = [&](int per, int s) {  // per key tiles per chunk, s chunks
-    const double waves = (double)((R * s + slots - 1) / slots);
-    double t = waves * (kFixed + per);
-    if (s > 1) t += 2 * kLaunch + (double)R * kBM * s * (D + 1) * 4.0 * 2.0 / step_bytes;
-    return t;
-  };
-  const double c1 = cost(nt, 1);
-  double best = c1;
-  for (int s0 = 2; s0 <= 32 && s0 <= nt; ++s0) {
-    const int per = (nt + s0 - 1) / s0, s = (nt + per - 1) / per;
-    const double t = cost(per, s);
-    if (t < best - 1e-9) {
-      best = t;
-      pl.nsplit = s;
-      pl.kc = per * kBN;
-    }
-  }
-  if (pl.nsplit == 1 || best > 0.97 * c1) {
-    pl.nsplit = 1;
-    pl.kc = 0;
-    return pl;
-  }
-  pl.whole = (int)whole;
-  pl.row0 = (whole / n_qtiles) * (int64_t)Nq + (whole % n_qtiles) * (int64_t)kBM;
-  pl.rows = (int64_t)B * H * Nq - pl.row0;
-  pl.units = (int)(R * pl.nsplit);
-  pl.ws_bytes = (size_t)pl.nsplit * pl.rows * (D + 1) * sizeof(float);
-  return pl;
 }
 
 hipError_t launch_attn_bf16_balanced(const void* q, const void* k, const void* v, void* o,

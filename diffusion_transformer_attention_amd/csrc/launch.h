@@ -11,6 +11,10 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
                             int B, int H, int Nq, int Nkv, int D, float scale, bool o_f32,
                             hipStream_t stream);
 
+// Tile sizes of the bf16 / fp8 forward kernels (checked in attn_bf16.hip).
+constexpr int kFwdQueryTile = 256;  // query rows per workgroup
+constexpr int kFwdKeyTile = 64;     // keys per LDS stage
+
 // Work balance of one bf16 forward over `slots` concurrent workgroups: the
 // first `whole` query tiles (a multiple of slots) run whole; the remaining
 // tiles are cut into nsplit key chunks of kc keys (units = tiles * nsplit

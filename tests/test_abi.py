@@ -87,6 +87,7 @@ def test_balanced_workspace_and_validation(lib):
     assert rc == dta.DIT_OK and need > 0 and need % (4 * 129) == 0
     assert size(Nkv=64) == (dta.DIT_OK, 0)                 # one key tile: nothing to split
     assert size(Nq=0) == (dta.DIT_OK, 0)
+    assert size(H=1 << 20, Nq=1 << 20, Nkv=128, D=32) == (dta.DIT_OK, 0)  # 2^32 tiles: no plan
     assert size(D=96)[0] == dta.DIT_EUNSUPPORTED
     assert size(slots=-1)[0] == dta.DIT_EINVAL
     assert size(Nkv=0)[0] == dta.DIT_EINVAL
