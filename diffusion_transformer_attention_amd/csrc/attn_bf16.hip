@@ -598,16 +598,14 @@ struct Split {
 // The kernel body.  F8: q and k are E4M3 codes (1 byte per element) whose
 // scores are rescaled by the per-(b, h) factors qds[bh] * kds[bh]; else q
 // and k are bf16 and qds, kds are unused.  SPLIT: a key-split launch (above),
-// total_tiles is then the number of units.  index: the workgroup's work item
-// in launch order (blockIdx.x, or a persistent workgroup's current item).
+// total_tiles is then the number of units.
 template <int D, bool OUT_F32, bool F8, bool SPLIT = false>
 __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const void* __restrict__ K,
                                               const __bf16* __restrict__ V, void* __restrict__ Oout,
                                               float* __restrict__ LSE, int Nq, int Nkv,
                                               int n_qtiles, int total_tiles, float c, Layout lay,
                                               const float* __restrict__ qds,
-                                              const float* __restrict__ kds, int index,
-                                              Split sp = {}) {
+                                              const float* __restrict__ kds, Split sp = {}) {
   using Gm = Geo<D>;
   using QK = QKOps<D, F8>;
   constexpr int QKB = F8 ? 1 : 2;  // bytes per q / k element
@@ -618,7 +616,7 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
   __shared__ __attribute__((aligned(1024))) char v1s[Gm::TILE];
   __shared__ __attribute__((aligned(1024))) char v2s[Gm::TILE];
 
-  int tile = remap_xcd(index, total_tiles), chunk = 0;
+  int tile = remap_xcd(blockIdx.x, total_tiles), chunk = 0;
   if (SPLIT) {
     const int u = tile;
     tile = sp.tile0 + u / sp.nsplit;
@@ -745,7 +743,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
                           float* __restrict__ LSE, int Nq, int Nkv, int n_qtiles, int total_tiles,
                           float c, Layout lay) {
   attn_fwd_body<D, OUT_F32, false>(Q, K, V, Oout, LSE, Nq, Nkv, n_qtiles, total_tiles, c, lay,
-                                   nullptr, nullptr, blockIdx.x);
+                                   nullptr, nullptr);
 }
 
 // Key-split partials (float32 O and LSE into the workspace).
@@ -756,7 +754,7 @@ void attn_fwd_bf16_split_kernel(const __bf16* __restrict__ Q, const __bf16* __re
                                 float* __restrict__ Lpart, int Nq, int Nkv, int n_qtiles,
                                 int units, float c, Layout lay, Split sp) {
   attn_fwd_body<D, true, false, true>(Q, K, V, Opart, Lpart, Nq, Nkv, n_qtiles, units, c, lay,
-                                      nullptr, nullptr, blockIdx.x, sp);
+                                      nullptr, nullptr, sp);
 }
 
 template <bool OUT_F32>
@@ -767,7 +765,7 @@ void attn_fwd_fp8_kernel(const unsigned char* __restrict__ Q, const unsigned cha
                          float c, Layout lay, const float* __restrict__ qds,
                          const float* __restrict__ kds) {
   attn_fwd_body<128, OUT_F32, true>(Q, K, V, Oout, LSE, Nq, Nkv, n_qtiles, total_tiles, c, lay,
-                                    qds, kds, blockIdx.x);
+                                    qds, kds);
 }
 
 template <int D, bool OUT_F32>
