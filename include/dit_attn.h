@@ -58,7 +58,8 @@ enum {
   DIT_OK = 0,
   DIT_EINVAL = -1,       /* null pointer, negative size, Nkv == 0, scale not finite or <= 0,
                             H % P != 0, N % P != 0, nblk < 1, P < 1, r outside [0, P),
-                            text head range outside [0, Ht), cos without sin */
+                            text head range outside [0, Ht), cos without sin, slots < 0,
+                            balanced-forward workspace missing or too small */
   DIT_EUNSUPPORTED = -2, /* D not in {32, 64, 128}, a dtype combination not built, elem_bytes
                             not in {1, 2, 4, 8}, fused Ulysses shard length not a multiple
                             of 64 */
