@@ -124,3 +124,22 @@ def test_balanced_long_video():
     ri = torch.from_numpy(rows).cuda()
     assert_bf16_close(to_f64(O[:, h:h + 1, ri]), to_f64(L[:, h:h + 1, ri]), Oref, Lref,
                       "balanced long video tail")
+
+
+def test_balanced_score_jump_in_a_split_chunk():
+    """A late key scoring ~100 (base 2) above the first step's max of its
+    chunk: the chunk's pass must take the exact-max path, and the merge must
+    still give the oracle's row (dominated by that key's value)."""
+    say("balanced score jump: 4 tiles on 3 slots, the last tile split in key chunks")
+    rng = np.random.default_rng(92)
+    q = rng.standard_normal((1, 2, 300, 128)).astype(np.float32)
+    k = rng.standard_normal((1, 2, 4100, 128)).astype(np.float32)
+    v = rng.standard_normal((1, 2, 4100, 128)).astype(np.float32)
+    k[0, 0, 700] = 6.0 * q[0, 0, 5]          # head 0, a whole tile
+    k[0, 1, 4097] = 6.0 * q[0, 1, 260]       # head 1, tail tile, last chunk's partial key tile
+    qb, kb, vb = (datagen.bf16_bits(x) for x in (q, k, v))
+    O, L = _run(*(bits_to_torch_bf16(x) for x in (qb, kb, vb)), torch.float32, 3)
+    Oref, Lref = oracle.attention(f64(qb), f64(kb), f64(vb))
+    assert_bf16_close(to_f64(O), to_f64(L), Oref, Lref, "balanced score jump")
+    assert abs(to_f64(O)[0, 1, 260] - f64(vb)[0, 1, 4097]).max() < 2e-2
+    assert abs(to_f64(O)[0, 0, 5] - f64(vb)[0, 0, 700]).max() < 2e-2
