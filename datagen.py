@@ -10,8 +10,8 @@ parallelism: spreading one step over several cards", sections "Sequence
 parallelism: Ulysses and Ring" and "Guidance parallelism"; the miles_diffusion
 USP pull request, "Ring kernel selection"):
 
-* tiny_f32      B1 H8 N256 D32 fp32, the handbook's four-card Ulysses
-                simulation recipe (torch.manual_seed(0), three torch.randn).
+* tiny_f32      B1 H8 N256 D32 fp32 from seed 0 (torch's CPU generator), the
+                numbers of the handbook's four-card Ulysses simulation.
 * image_share   B1 H24 N4096 D128 bf16, FLUX 1024^2 image tokens (64x64 patch
                 grid, 24 heads, head dim 128); each (tensor, b, h, token) row
                 is scaled by a factor drawn from U(0.5, 2).
@@ -26,9 +26,9 @@ USP pull request, "Ring kernel selection"):
                 shared by every head and channel.
 
 Random draws use numpy's PCG64 ``default_rng(seed)`` in the order q, k, v,
-then the structure draws in the order q, k, v.  The tiny workload instead uses
-the handbook's own torch recipe so the simulation's printed outcome can be
-reproduced on identical data.
+then the structure draws in the order q, k, v.  The tiny workload instead
+draws from torch's CPU generator, which gives the handbook simulation's own
+numbers, so its printed outcome can be checked on identical data.
 """
 from __future__ import annotations
 
@@ -63,11 +63,17 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 def tiny_f32():
-    """The handbook simulation's q, k, v: torch.manual_seed(0), three randn(1,8,256,32)."""
+    """The tiny float32 workload: q, k, v [1,8,256,32] ~ N(0,1) from seed 0.
+
+    One [3,1,8,256,32] standard-normal draw of a torch CPU generator seeded
+    with 0, split into q, k, v.  These are the same numbers as the
+    handbook's four-card simulation draws, so its printed outcome can be
+    checked on identical data.
+    """
     import torch
-    torch.manual_seed(0)
-    q, k, v = (torch.randn(1, 8, 256, 32) for _ in range(3))
-    return q.numpy().copy(), k.numpy().copy(), v.numpy().copy()
+    gen = torch.Generator(device="cpu").manual_seed(0)
+    qkv = torch.randn((3, 1, 8, 256, 32), generator=gen, dtype=torch.float32).numpy()
+    return tuple(np.ascontiguousarray(qkv[i]) for i in range(3))
 
 
 def normal_bf16(shape, seed, row_scale=None, token_offset_std=None):

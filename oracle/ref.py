@@ -12,10 +12,10 @@ computes, with no fusion or reordering beyond what that definition states.
 
 Sources (web pages; sections named, not quoted):
 * "Multi-GPU parallelism: spreading one step over several cards" (AI infra
-  handbook), section "Sequence parallelism: Ulysses and Ring": the four-card
-  Ulysses simulation listing (token partition, ``all_to_all_heads``,
-  per-card attention, ``all_to_all_tokens``, concatenation), and the Ring
-  paragraph (local attention per K/V block, merged with a log-sum-exp).
+  handbook), section "Sequence parallelism: Ulysses and Ring": Ulysses cuts
+  the tokens into one slice per card and trades slices for head groups
+  before attention and back after it; Ring runs local attention on each
+  K/V block and merges the blocks with a log-sum-exp.
 * "Feat: USP sequence parallelism (Ulysses x Ring) via SequenceParallelPlan"
   (miles_diffusion pull request), Design / "Ring kernel selection": ring
   kernels must return the LSE; "Limitations": no mask, dropout, causal flag
@@ -217,61 +217,84 @@ def ring_attention(q, k, v, nblk, scale=None):
 
 
 # --------------------------------------------------------------------------
-# Ulysses layout exchange on one device (handbook simulation listing:
-# ``all_to_all_heads`` / ``all_to_all_tokens``).  Buffers are rank-stacked:
-# index 0 is the rank.  Pure data movement, exact in any dtype.
+# Ulysses layout exchange on one device (handbook, "Sequence parallelism:
+# Ulysses and Ring": before attention every card trades its token slice of
+# all heads for all tokens of its head group, and trades back afterwards).
+# Buffers are rank-stacked: axis 0 is the rank.  With n = N/P tokens per
+# slice and g = H/P heads per group, the two exchanges are the index maps
+#   seq->head:  out[r, b, h', s*n + i, d] = in[s, b, r*g + h', i, d]
+#   head->seq:  out[s, b, r*g + h', i, d] = in[r, b, h', s*n + i, d]
+# for ranks r, s < P, h' < g, i < n.  Each function below writes its map as
+# a split of one axis into (rank, index) plus an axis permutation, so a
+# reader can check it against the map letter by letter.  Pure data
+# movement, exact in any dtype.
 # --------------------------------------------------------------------------
 def shard_tokens(x, P):
-    """[B,H,N,D] -> [P,B,H,N/P,D]: rank r holds every head of tokens
-    [r*N/P, (r+1)*N/P)."""
+    """[B,H,N,D] -> [P,B,H,N/P,D]:  out[r, b, h, i, d] = x[b, h, r*n + i, d].
+
+    Rank r holds every head of tokens [r*n, (r+1)*n), n = N/P.
+    """
     x = np.asarray(x)
-    N = x.shape[2]
+    B, H, N, D = x.shape
     if N % P:
         raise ValueError("N must be divisible by P")
-    s = N // P
-    return np.stack([x[:, :, r * s:(r + 1) * s] for r in range(P)])
-
-
-def seq2head(shards):
-    """[P,B,H,N/P,D] token shards -> [P,B,H/P,N,D] head groups.
-
-    Rank r gathers head group r (heads [r*H/P, (r+1)*H/P)) from every rank s
-    and concatenates them along tokens in rank order s = 0..P-1.
-    """
-    shards = np.asarray(shards)
-    P, B, H = shards.shape[:3]
-    if H % P:
-        raise ValueError("H must be divisible by P")
-    g = H // P
-    return np.stack([np.concatenate([shards[s][:, r * g:(r + 1) * g] for s in range(P)], axis=2)
-                     for r in range(P)])
-
-
-def head2seq(groups):
-    """[P,B,H/P,N,D] head groups -> [P,B,H,N/P,D] token shards (inverse of seq2head).
-
-    Rank s gathers token slice s ([s*N/P, (s+1)*N/P)) from every rank r and
-    concatenates them along heads in rank order r = 0..P-1.
-    """
-    groups = np.asarray(groups)
-    P, B, g, N = groups.shape[:4]
-    if N % P:
-        raise ValueError("N must be divisible by P")
-    s_len = N // P
-    return np.stack([np.concatenate([groups[r][:, :, s * s_len:(s + 1) * s_len] for r in range(P)], axis=1)
-                     for s in range(P)])
+    # token axis N -> (r, i); then move r to the front
+    return np.ascontiguousarray(x.reshape(B, H, P, N // P, D).transpose(2, 0, 1, 3, 4))
 
 
 def unshard_tokens(shards):
-    """[P,B,H,N/P,D] -> [B,H,N,D]: concatenate the token shards in rank order."""
-    return np.concatenate(list(np.asarray(shards)), axis=2)
+    """[P,B,H,N/P,D] -> [B,H,N,D]:  out[b, h, r*n + i, d] = shards[r, b, h, i, d]."""
+    shards = np.asarray(shards)
+    P, B, H, n, D = shards.shape
+    return np.ascontiguousarray(shards.transpose(1, 2, 0, 3, 4)).reshape(B, H, P * n, D)
+
+
+def seq2head(shards):
+    """[P,B,H,N/P,D] token slices -> [P,B,H/P,N,D] head groups.
+
+    out[r, b, h', s*n + i, d] = in[s, b, r*g + h', i, d]: rank r ends up with
+    head group r (heads [r*g, (r+1)*g)) over all N tokens, the slice that
+    came from rank s landing at tokens [s*n, (s+1)*n).
+    """
+    x = np.asarray(shards)
+    P, B, H, n, D = x.shape
+    if H % P:
+        raise ValueError("H must be divisible by P")
+    g = H // P
+    # in axes (s, b, r, h', i, d) with the head axis split as r*g + h'
+    t = x.reshape(P, B, P, g, n, D)
+    # out axes (r, b, h', s, i, d); (s, i) then merge into the token s*n + i
+    t = t.transpose(2, 1, 3, 0, 4, 5)
+    return np.ascontiguousarray(t).reshape(P, B, g, P * n, D)
+
+
+def head2seq(groups):
+    """[P,B,H/P,N,D] head groups -> [P,B,H,N/P,D] token slices (inverse of seq2head).
+
+    out[s, b, r*g + h', i, d] = in[r, b, h', s*n + i, d]: rank s gets back
+    token slice s of every head, the group from rank r landing at heads
+    [r*g, (r+1)*g).
+    """
+    x = np.asarray(groups)
+    P, B, g, N, D = x.shape
+    if N % P:
+        raise ValueError("N must be divisible by P")
+    n = N // P
+    # in axes (r, b, h', s, i, d) with the token axis split as s*n + i
+    t = x.reshape(P, B, g, P, n, D)
+    # out axes (s, b, r, h', i, d); (r, h') then merge into the head r*g + h'
+    t = t.transpose(3, 1, 0, 2, 4, 5)
+    return np.ascontiguousarray(t).reshape(P, B, P * g, n, D)
 
 
 def ulysses_attention(q, k, v, P, scale=None):
-    """The whole simulated Ulysses round trip: shard by tokens, exchange to
-    head groups, attention per rank, exchange back, concatenate tokens."""
-    qh, kh, vh = (seq2head(shard_tokens(t, P)) for t in (q, k, v))
-    outs = np.stack([attention(qh[r], kh[r], vh[r], scale)[0] for r in range(P)])
+    """Attention as the P Ulysses ranks compute it together: every tensor is
+    cut into token slices and exchanged to head groups, each rank runs
+    ``attention`` on its group, and the outputs are exchanged back and the
+    token slices joined."""
+    grouped = [seq2head(shard_tokens(t, P)) for t in (q, k, v)]
+    outs = np.stack([attention(grouped[0][r], grouped[1][r], grouped[2][r], scale)[0]
+                     for r in range(P)])
     return unshard_tokens(head2seq(outs))
 
 

@@ -260,15 +260,66 @@ def _seq2head_by_index(shards):
     return out
 
 
-@pytest.mark.parametrize("P,B,H,N,D", [(4, 1, 8, 16, 3), (2, 2, 6, 10, 4), (3, 1, 3, 9, 2), (1, 1, 2, 4, 2)])
+def _shard_by_index(x, P):
+    """out[r][b,h,i,d] = x[b,h,r*N/P+i,d], element by element."""
+    B, H, N, D = x.shape
+    n = N // P
+    out = np.empty((P, B, H, n, D), dtype=x.dtype)
+    for r, b, h, i in itertools.product(range(P), range(B), range(H), range(n)):
+        out[r, b, h, i] = x[b, h, r * n + i]
+    return out
+
+
+def _head2seq_by_index(groups):
+    """out[s][b,r*H/P+h',i,d] = in[r][b,h',s*N/P+i,d], element by element."""
+    P, B, g, N, D = groups.shape
+    n = N // P
+    out = np.empty((P, B, g * P, n, D), dtype=groups.dtype)
+    for s, r, b, hh, i in itertools.product(range(P), range(P), range(B), range(g), range(n)):
+        out[s, b, r * g + hh, i] = groups[r, b, hh, s * n + i]
+    return out
+
+
+@pytest.mark.parametrize("P,B,H,N,D", [(4, 1, 8, 16, 3), (2, 2, 6, 10, 4), (3, 1, 3, 9, 2), (1, 1, 2, 4, 2),
+                                       (3, 2, 6, 12, 1)])
 def test_seq2head_index_map(P, B, H, N, D):
     x = np.arange(B * H * N * D, dtype=np.int64).reshape(B, H, N, D)
     shards = oracle.shard_tokens(x, P)
+    assert np.array_equal(shards, _shard_by_index(x, P))
     out = oracle.seq2head(shards)
     assert np.array_equal(out, _seq2head_by_index(shards))
+    # head2seq checked on its own map (distinct values everywhere), not only
+    # as the inverse of seq2head
+    y = (np.arange(P * B * (H // P) * N * D, dtype=np.int64) * 7 + 3).reshape(P, B, H // P, N, D)
+    assert np.array_equal(oracle.head2seq(y), _head2seq_by_index(y))
     back = oracle.head2seq(out)
     assert np.array_equal(back, shards)
     assert np.array_equal(oracle.unshard_tokens(back), x)
+
+
+def test_permute_pins_reject_planted_mistakes():
+    """Plausible slips in the exchanges (rank axes swapped, group and rank
+    swapped in the head index, token slices joined in reverse) each fail the
+    element-by-element maps."""
+    P, B, H, N, D = 3, 2, 6, 12, 2
+    x = np.arange(B * H * N * D, dtype=np.int64).reshape(B, H, N, D)
+    shards = oracle.shard_tokens(x, P)
+    g, n = H // P, N // P
+
+    def rank_axes_swapped(sh):        # out[s] gets group s of rank r's slice at r*n
+        t = sh.reshape(P, B, P, g, n, D).transpose(0, 1, 3, 2, 4, 5)
+        return np.ascontiguousarray(t).reshape(P, B, g, P * n, D)
+
+    def head_index_swapped(sh):       # head split as h'*P + r instead of r*g + h'
+        t = sh.reshape(P, B, g, P, n, D).transpose(3, 1, 2, 0, 4, 5)
+        return np.ascontiguousarray(t).reshape(P, B, g, P * n, D)
+
+    def slices_reversed(sh):
+        return oracle.seq2head(sh[::-1])
+
+    want = _seq2head_by_index(shards)
+    for bad in (rank_axes_swapped, head_index_swapped, slices_reversed):
+        assert not np.array_equal(bad(shards), want), bad.__name__
 
 
 def test_permute_divisibility_errors():
