@@ -101,6 +101,31 @@ def parse():
     return ap.parse_args()
 
 
+def host_cpus():
+    """(CPUs this process may use, CPUs in its affinity set, CPU model name).
+
+    The usable count is the affinity set capped by the cgroup CPU quota, when
+    one is set: a container given a share of a larger host sees every host
+    CPU in its affinity set but may run only its quota at once."""
+    affinity = len(os.sched_getaffinity(0))
+    usable = affinity
+    try:
+        quota, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if quota != "max":
+            usable = min(affinity, max(1, int(quota) // int(period)))
+    except (OSError, ValueError):
+        pass
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return usable, affinity, model
+
+
 def cpu_baseline(qb, kb, vb, target_s):
     """Time the fp64 oracle on query rows of the 10-head share (all 32768 keys)."""
     import concurrent.futures as cf
@@ -108,7 +133,7 @@ def cpu_baseline(qb, kb, vb, target_s):
     import oracle
     import datagen
     from threadpoolctl import threadpool_limits
-    cores = min(16, len(os.sched_getaffinity(0)))
+    cores, affinity, model = host_cpus()
     f64 = lambda b: datagen.bf16_to_f32(b).astype(np.float64)
     k64 = [f64(kb[:, h:h + 1]) for h in range(H)]
     v64 = [f64(vb[:, h:h + 1]) for h in range(H)]
@@ -138,7 +163,8 @@ def cpu_baseline(qb, kb, vb, target_s):
             "sample": f"{rows_per_head} query rows x {H} heads against all {N} keys "
                       f"(fp64 numpy, {len(range(0, rows_per_head, 64)) * H} tasks of 64 rows "
                       f"on {cores} threads, BLAS 1 thread each), {dt:.1f} s",
-            "seconds": dt, "flops": flops}
+            "seconds": dt, "flops": flops, "cpu_model": model, "affinity_cpus": affinity,
+            "workers": cores}
 
 
 def main():

@@ -16,7 +16,7 @@ import torch
 import datagen
 import oracle
 import diffusion_transformer_attention_amd as dta
-from _helpers import bits_to_torch_bf16, to_f64
+from _helpers import bits_to_torch_bf16, run_threaded, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -125,13 +125,34 @@ def test_backward_image_share_full():
 
 
 def test_backward_ulysses_share_sampled_rows():
-    say("bwd Ulysses share B1 H10 N32768 D128, sampled dq rows")
+    say("bwd Ulysses share B1 H10 N32768 D128: sampled dq rows and dk, dv keys")
     qb, kb, vb = (x[:, :10] for x in datagen.workload_inputs("ulysses_share"))
     dob = datagen.small_bf16(1, 10, 32768, 128, seed=1002)[0]
     _, (dq, dk, dv, delta) = _gpu_fwd_bwd(qb, kb, vb, dob)
-    rows = datagen.sample_rows(32768, 32, 1003)
-    rq, rd = oracle.attention_backward_rows(f64(qb), f64(kb), f64(vb), f64(dob), rows)
+    q64, k64, v64, do64 = f64(qb), f64(kb), f64(vb), f64(dob)
+    rows = datagen.sample_rows(32768, 64, 1003)
     ri = torch.from_numpy(rows).cuda()
-    _check_grad(to_f64(dq[:, :, ri]), rq, "dq", "ulysses share sampled")
+
+    def rows_task(h):
+        return oracle.attention_backward_rows(q64[:, h:h + 1], k64[:, h:h + 1], v64[:, h:h + 1],
+                                              do64[:, h:h + 1], rows)
+
+    res = run_threaded(rows_task, range(10))
+    rq = np.concatenate([r[0] for r in res], axis=1)
+    rd = np.concatenate([r[1] for r in res], axis=1)
+    _check_grad(to_f64(dq[:, :, ri]), rq, "dq", "ulysses share sampled rows")
     assert np.abs(to_f64(delta[:, :, ri]) - rd).max() <= 1e-2 * np.abs(rd).max()
+    # dk, dv of 64 keys per head: each sums over all 32768 query rows
+    keys = datagen.sample_rows(32768, 64, 1005)
+    ki = torch.from_numpy(keys).cuda()
+
+    def keys_task(h):
+        return oracle.attention_backward_keys(q64[:, h:h + 1], k64[:, h:h + 1], v64[:, h:h + 1],
+                                              do64[:, h:h + 1], keys)
+
+    res = run_threaded(keys_task, range(10))
+    rk = np.concatenate([r[0] for r in res], axis=1)
+    rv = np.concatenate([r[1] for r in res], axis=1)
+    _check_grad(to_f64(dk[:, :, ki]), rk, "dk", "ulysses share sampled keys")
+    _check_grad(to_f64(dv[:, :, ki]), rv, "dv", "ulysses share sampled keys")
     assert torch.isfinite(dk).all() and torch.isfinite(dv).all()

@@ -1,9 +1,12 @@
 """GPU parity: the HIP library against the fp64 oracle, through the C ABI.
 
-Small cases compare every output element; the full-size workloads compare
-sampled rows the oracle computes one by one, plus properties that hold at
-any size (bit-exact permutes, Ulysses output equal to single-pass output bit
-for bit, ring-merged output equal to single-pass output within tolerance,
+Small cases compare every output element.  At full size the Ulysses share
+(B1 H10 N32768 D128) is compared on every row, the ring merge on 512 rows
+per head for the merged output and each of its four partials, and the long
+video on 512 rows per head (its stated 64, widened); the oracle runs on worker
+threads over row blocks.  Properties that hold at any size are checked too
+(bit-exact permutes, Ulysses output equal to single-pass output bit for bit,
+ring-merged output equal to single-pass output within tolerance,
 determinism, untouched guard bands).
 """
 import sys
@@ -15,8 +18,8 @@ import torch
 import datagen
 import oracle
 import diffusion_transformer_attention_amd as dta
-from _helpers import (F32_MAX_ABS, assert_bf16_close, bits_to_torch_bf16, max_abs, rel_rms,
-                      to_f64)
+from _helpers import (BF16_LSE_MAX_ABS, F32_MAX_ABS, assert_bf16_close, bits_to_torch_bf16,
+                      max_abs, oracle_attention_threaded, rel_rms, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -144,8 +147,9 @@ def test_bf16_large_scores_and_explicit_scale():
         assert np.isfinite(to_f64(O)).all()
         ma, rr = max_abs(to_f64(O), Oref), rel_rms(to_f64(O), Oref)
         assert ma <= 2e-2 and rr <= 1e-2, (scale, ma, rr)
-        # LSE grows with the score range; its absolute bound scales with |LSE|
-        assert max_abs(to_f64(L), Lref) <= 1e-3 * max(1.0, np.abs(Lref).max() / 10)
+        la = max_abs(to_f64(L), Lref)
+        say(f"scale {scale:.4f}: |LSE| up to {np.abs(Lref).max():.1f}, LSE max-abs {la:.2e}")
+        assert la <= BF16_LSE_MAX_ABS, (scale, la)
 
 
 @pytest.mark.parametrize("Nkv", [1000, 4100])
@@ -262,21 +266,25 @@ def test_image_share_full():
 
 
 def test_ulysses_share(wan_draw):
-    say("ulysses share: permutes of [4][1,40,8192,128] + attention B1 H10 N32768 D128")
+    say("ulysses share: permutes of [4][1,40,8192,128] + attention B1 H10 N32768 D128, every row")
     qb, kb, vb = wan_draw
-    P, rows = 4, datagen.sample_rows(32768, 64, 1002)
+    P = 4
     full = [bits_to_torch_bf16(x) for x in (qb, kb, vb)]
     shard = lambda t: torch.stack(t.chunk(P, dim=2)).contiguous()   # rank s's token slice
     groups = [dta.ulysses_seq2head(shard(t)) for t in full]
     torch.cuda.synchronize()
-    want_q = oracle.seq2head(oracle.shard_tokens(qb, P))
-    assert np.array_equal(groups[0].cpu().view(torch.int16).numpy().view(np.uint16), want_q)
-    del want_q
-    # rank 0's share: heads 0..9 over all tokens
+    # q, k and v exchanges against the oracle's index map, bit for bit
+    for name, bits, got in zip("qkv", (qb, kb, vb), groups):
+        want = oracle.seq2head(oracle.shard_tokens(bits, P))
+        assert np.array_equal(got.cpu().view(torch.int16).numpy().view(np.uint16), want), name
+        del want
+    # rank 0's share (heads 0..9 over all tokens) against the oracle, every row
     O0, L0 = dta.dit_attn_fwd(groups[0][0], groups[1][0], groups[2][0])
-    Oref, Lref = oracle.attention_rows(f64(qb[:, :10]), f64(kb[:, :10]), f64(vb[:, :10]), rows)
-    ri = torch.from_numpy(rows).cuda()
-    assert_bf16_close(to_f64(O0[:, :, ri]), to_f64(L0[:, :, ri]), Oref, Lref, "ulysses share r0")
+    Oref, Lref = oracle_attention_threaded(f64(qb[:, :10]), f64(kb[:, :10]), f64(vb[:, :10]))
+    ma, rr = assert_bf16_close(to_f64(O0), to_f64(L0), Oref, Lref, "ulysses share r0, all rows")
+    say(f"ulysses share r0, all {Oref.shape[2]} rows x 10 heads: O max-abs {ma:.2e} rel-RMS {rr:.2e}, "
+        f"LSE max-abs {max_abs(to_f64(L0), Lref):.2e}")
+    del Oref, Lref
     # every rank, exchanged back, equals one pass over all 40 heads bit for bit
     outs = torch.stack([O0] + [dta.dit_attn_fwd(groups[0][r], groups[1][r], groups[2][r],
                                                 return_lse=False)[0] for r in range(1, P)])
@@ -284,6 +292,10 @@ def test_ulysses_share(wan_draw):
     O_ul = torch.cat(list(back), dim=2)
     O_single, _ = dta.dit_attn_fwd(*full, return_lse=False)
     assert torch.equal(O_ul, O_single)
+    # the output exchange against the oracle's inverse map, bit for bit
+    want = oracle.head2seq(outs.cpu().view(torch.int16).numpy().view(np.uint16))
+    assert np.array_equal(back.cpu().view(torch.int16).numpy().view(np.uint16), want)
+    del want
     # the fused entry point reads the shards directly: same bits, no exchange buffers
     sh = [shard(t) for t in full]
     out = torch.zeros_like(sh[0])
@@ -295,7 +307,7 @@ def test_ulysses_share(wan_draw):
 
 
 def test_ring_merge(wan_draw):
-    say("ring merge B1 H40 N32768 D128, 4 K/V blocks of 8192")
+    say("ring merge B1 H40 N32768 D128, 4 K/V blocks of 8192; 512 rows per head vs the oracle")
     qb, kb, vb = wan_draw
     tq, tk, tv = (bits_to_torch_bf16(x) for x in (qb, kb, vb))
     nblk, s = 4, 8192
@@ -311,20 +323,23 @@ def test_ring_merge(wan_draw):
     ma = (Om.float() - Os.float()).abs().max().item()
     assert ma <= 2e-2, ma
     assert (Lm - Ls).abs().max().item() <= 1e-3
-    # merged and per-block partials vs the oracle on sampled rows of every head
-    rows = datagen.sample_rows(32768, 32, 1003)
+    # merged output and every per-block partial vs the oracle on 512 rows of each head
+    rows = datagen.sample_rows(32768, 512, 1003)
     ri = torch.from_numpy(rows).cuda()
-    q64, k64, v64 = f64(qb[:, :, rows]), f64(kb), f64(vb)
-    Oref, Lref = oracle.attention(q64, k64, v64)
-    assert_bf16_close(to_f64(Om[:, :, ri]), to_f64(Lm[:, :, ri]), Oref, Lref, "ring merged")
-    for i in (0, 3):
-        Opr, Lpr = oracle.attention(q64, k64[:, :, i * s:(i + 1) * s], v64[:, :, i * s:(i + 1) * s])
+    q64 = f64(qb[:, :, rows])
+    k64, v64 = f64(kb), f64(vb)
+    Oref, Lref = oracle_attention_threaded(q64, k64, v64)
+    ma, rr = assert_bf16_close(to_f64(Om[:, :, ri]), to_f64(Lm[:, :, ri]), Oref, Lref, "ring merged")
+    say(f"ring merged, 512 rows x 40 heads: O max-abs {ma:.2e} rel-RMS {rr:.2e}")
+    del Oref, Lref
+    for i in range(nblk):
+        Opr, Lpr = oracle_attention_threaded(q64, k64[:, :, i * s:(i + 1) * s], v64[:, :, i * s:(i + 1) * s])
         assert_bf16_close(to_f64(o_parts[i][:, :, ri]), to_f64(l_parts[i][:, :, ri]), Opr, Lpr,
                           f"ring partial {i}")
 
 
 def test_long_video_tail():
-    say("long video B1 H10 N75600 D128 (tail), 64 sampled rows per head, guard bands")
+    say("long video B1 H10 N75600 D128 (tail), 512 sampled rows per head, guard bands")
     qb, kb, vb = datagen.workload_inputs("long_video")
     tq, tk, tv = (bits_to_torch_bf16(x) for x in (qb, kb, vb))
     obuf, O = guarded((1, 10, 75600, 128), torch.bfloat16)
@@ -332,7 +347,11 @@ def test_long_video_tail():
     dta.dit_attn_fwd(tq, tk, tv, out=O, lse=L)
     torch.cuda.synchronize()
     assert margins_intact(obuf) and margins_intact(lbuf)
-    rows = datagen.sample_rows(75600, 64, 1004)
-    Oref, Lref = oracle.attention_rows(f64(qb), f64(kb), f64(vb), rows)
+    # the workload's stated 64 rows per head, widened to 512 (the oracle runs
+    # on worker threads); the sample holds rows 0, N-1 and a row of the last
+    # partial tile
+    rows = datagen.sample_rows(75600, 512, 1004)
+    Oref, Lref = oracle_attention_threaded(f64(qb), f64(kb), f64(vb), rows=rows)
     ri = torch.from_numpy(rows).cuda()
-    assert_bf16_close(to_f64(O[:, :, ri]), to_f64(L[:, :, ri]), Oref, Lref, "long video")
+    ma, rr = assert_bf16_close(to_f64(O[:, :, ri]), to_f64(L[:, :, ri]), Oref, Lref, "long video")
+    say(f"long video, 512 rows x 10 heads: O max-abs {ma:.2e} rel-RMS {rr:.2e}")

@@ -481,3 +481,21 @@ def test_sample_rows_forced_members():
     assert len(rows) == 64 and len(set(rows.tolist())) == 64
     assert rows[0] == 0 and rows[-1] == 75599
     assert any(r >= 75600 - 75600 % 128 and r < 75599 for r in rows)
+
+
+def test_threaded_runner_is_the_oracle_row_by_row():
+    """The worker-thread runner the full-size GPU tests use returns the
+    oracle's rows (all rows, and a row sample).  Rows are independent; only
+    the BLAS blocking of a different row count can move the last bits."""
+    from _helpers import oracle_attention_threaded
+    r = _rng(19)
+    q, k, v = r.standard_normal((2, 3, 70, 8)), r.standard_normal((2, 3, 50, 8)), r.standard_normal((2, 3, 50, 8))
+    O, L = oracle.attention(q, k, v, 0.4)
+    O2, L2 = oracle_attention_threaded(q, k, v, 0.4, block=16)
+    assert np.abs(O - O2).max() <= 1e-13 and np.abs(L - L2).max() <= 1e-13
+    rows = np.array([0, 5, 33, 69])
+    O3, L3 = oracle_attention_threaded(q, k, v, 0.4, rows=rows, block=3)
+    assert np.abs(O3 - O[:, :, rows]).max() <= 1e-13 and np.abs(L3 - L[:, :, rows]).max() <= 1e-13
+    # a wrong row mapping (rows taken in block order from the start) is caught
+    O4, _ = oracle_attention_threaded(q, k, v, 0.4, rows=np.arange(4), block=3)
+    assert np.abs(O4 - O[:, :, rows]).max() > 1e-3
