@@ -21,8 +21,11 @@ LIB_PATH = os.path.join(_HERE, "libditattn.so")
 
 DIT_BF16, DIT_F32 = 0, 1
 DIT_OK, DIT_EINVAL, DIT_EUNSUPPORTED, DIT_EALIGN, DIT_ELAUNCH, DIT_ERANGE = 0, -1, -2, -3, -4, -5
+DIT_ESCRATCH = -6
+DIT_SCRATCH_BYTES = 160 << 20   # static device scratch behind dit_attn_fwd_balanced_noalloc
 EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_balanced",
-            "dit_attn_fwd_balanced_workspace", "dit_attn_fwd_ulysses", "dit_attn_bwd",
+            "dit_attn_fwd_balanced_workspace", "dit_attn_fwd_balanced_noalloc",
+            "dit_attn_fwd_ulysses", "dit_attn_bwd",
             "dit_attn_merge", "dit_rope_pack", "dit_attn_fwd_joint", "dit_quant_fp8",
             "dit_attn_fwd_fp8", "ulysses_seq2head", "ulysses_head2seq", "dit_strerror",
             "dit_abi_version")
@@ -47,6 +50,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                           ctypes.c_size_t, P]
     lib.dit_attn_fwd_balanced_workspace.argtypes = [I, I, I, I, I, I,
                                                     ctypes.POINTER(ctypes.c_size_t)]
+    lib.dit_attn_fwd_balanced_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, P]
     lib.dit_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P]
     lib.dit_attn_merge.argtypes = [P, P, I, P, P, I, I, I, I, I, P]
     lib.dit_quant_fp8.argtypes = [P, P, P, I, I, I, I, P]
@@ -57,7 +61,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ulysses_seq2head.argtypes = [P, P, I, I, I, I, I, I, P]
     lib.ulysses_head2seq.argtypes = [P, P, I, I, I, I, I, I, P]
     for name in ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_balanced",
-                 "dit_attn_fwd_balanced_workspace", "dit_attn_fwd_ulysses", "dit_attn_bwd",
+                 "dit_attn_fwd_balanced_workspace", "dit_attn_fwd_balanced_noalloc",
+                 "dit_attn_fwd_ulysses", "dit_attn_bwd",
                  "dit_attn_merge", "dit_rope_pack", "dit_attn_fwd_joint", "dit_quant_fp8",
                  "dit_attn_fwd_fp8", "ulysses_seq2head", "ulysses_head2seq", "dit_abi_version"):
         getattr(lib, name).restype = ctypes.c_int
@@ -217,6 +222,35 @@ def dit_attn_fwd_balanced(q, k, v, scale=None, out_dtype=torch.bfloat16, out=Non
                                    _stream())
     _check(rc, "dit_attn_fwd_balanced")
     return o, lse
+
+
+def dit_attn_fwd_balanced_noalloc(q, k, v, out, lse=None, scale=None, slots=0):
+    """dit_attn_fwd_balanced with the library's static device scratch instead
+    of a workspace: the caller passes the outputs ``out`` ([B,H,Nq,D], bf16 or
+    float32) and ``lse`` (float32 [B,H,Nq] or None) and nothing is allocated.
+    Raises DitError (DIT_ESCRATCH) when the plan needs more than
+    DIT_SCRATCH_BYTES.  Returns (out, lse)."""
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, n, 4)
+    B, H, Nq, D = q.shape
+    Nkv = k.shape[2]
+    if k.shape != v.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != D:
+        raise ValueError("k, v must be [B,H,Nkv,D] matching q")
+    if not (q.dtype == k.dtype == v.dtype == torch.bfloat16):
+        raise ValueError("q, k, v must be bf16")
+    if tuple(out.shape) != (B, H, Nq, D):
+        raise ValueError("out must be [B,H,Nq,D]")
+    if lse is not None:
+        _need(lse, "lse", 3)
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq):
+            raise ValueError("lse must be float32 [B,H,Nq]")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = lib.dit_attn_fwd_balanced_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq,
+                                           Nkv, D, ctypes.c_float(scale), _dtype_code(out.dtype),
+                                           int(slots), _stream())
+    _check(rc, "dit_attn_fwd_balanced_noalloc")
+    return out, lse
 
 
 def dit_attn_fwd_ulysses(q, k, v, r, scale=None, out=None, lse=None, return_lse=True):

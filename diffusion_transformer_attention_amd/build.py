@@ -25,7 +25,7 @@ HIPFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I" + os.path.join(ROOT, "include")]
 SOURCES = ["api.cpp", "plan.cpp", "attn_bf16.hip", "attn_bwd.hip", "attn_f32.hip", "merge.hip", "permute.hip",
-           "rope_pack.hip", "quant_fp8.hip"]
+           "rope_pack.hip", "quant_fp8.hip", "scratch.hip"]
 
 
 def _compile(src: str, verbose: bool) -> str:

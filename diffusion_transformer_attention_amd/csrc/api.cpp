@@ -168,6 +168,30 @@ int dit_attn_fwd_balanced(const void* q, const void* k, const void* v, void* o, 
                                                        static_cast<hipStream_t>(stream)));
 }
 
+int dit_attn_fwd_balanced_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  int B, int H, int Nq, int Nkv, int D, float scale, int o_dtype,
+                                  int slots, void* stream) {
+  bool work = false;
+  int rc = balanced_check(B, H, Nq, Nkv, D, scale, o_dtype, slots, &work);
+  if (rc != DIT_OK || !work) return rc;
+  if (!q || !k || !v || !o) return DIT_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return DIT_EALIGN;
+  if (lse && !aligned(lse, 4)) return DIT_EALIGN;
+  int n = 0;
+  if ((rc = device_slots(slots, &n)) != DIT_OK) return rc;
+  const ditattn::BalancedPlan plan = ditattn::balanced_plan(B, H, Nq, Nkv, D, n);
+  if (plan.ws_bytes > DIT_SCRATCH_BYTES) return DIT_ESCRATCH;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (plan.ws_bytes > 0) {
+    if (ditattn::scratch_buffer(&ws, &ws_bytes) != hipSuccess) return DIT_ELAUNCH;
+    if (ws_bytes < plan.ws_bytes) return DIT_ESCRATCH;
+  }
+  return map_launch(ditattn::launch_attn_bf16_balanced(q, k, v, o, lse, B, H, Nq, Nkv, D, scale,
+                                                       o_dtype == DIT_F32, plan, ws,
+                                                       static_cast<hipStream_t>(stream)));
+}
+
 int dit_attn_merge(const float* o_parts, const float* lse_parts, int nblk, void* o, float* lse,
                    int B, int H, int N, int D, int o_dtype, void* stream) {
   if (nblk < 1 || B < 0 || H < 0 || N < 0 || D <= 0) return DIT_EINVAL;
@@ -316,6 +340,8 @@ const char* dit_strerror(int code) {
     case DIT_EALIGN: return "misaligned pointer";
     case DIT_ELAUNCH: return "HIP launch failed";
     case DIT_ERANGE: return "tensor size out of range";
+    case DIT_ESCRATCH:
+      return "the work needs more scratch than the static buffer holds (DIT_SCRATCH_BYTES)";
     default: return "unknown error code";
   }
 }

@@ -33,6 +33,10 @@ hipError_t launch_attn_bf16_balanced(const void* q, const void* k, const void* v
                                      bool o_f32, const BalancedPlan& plan, void* workspace,
                                      hipStream_t stream);
 
+// Device address of this device's static scratch array (DIT_SCRATCH_BYTES
+// bytes, scratch.hip), looked up on the first call per device.
+hipError_t scratch_buffer(void** out, size_t* bytes);
+
 // bf16 q/k/v/o in Ulysses token-shard layout [P][B,H,N/P,D]: attention of
 // head group r (heads [r*H/P, (r+1)*H/P)) over all N tokens.  lse is
 // [B,H/P,N] or null.  Requires (N/P) % 64 == 0.

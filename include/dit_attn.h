@@ -67,8 +67,14 @@ enum {
                             4-byte aligned,
                             permute buffers not aligned to elem_bytes */
   DIT_ELAUNCH = -4,      /* the HIP runtime reported an error at launch */
-  DIT_ERANGE = -5        /* a size product does not fit the 64-bit index space */
+  DIT_ERANGE = -5,       /* a size product does not fit the 64-bit index space */
+  DIT_ESCRATCH = -6      /* dit_attn_fwd_balanced_noalloc: the plan needs more scratch than
+                            the library's static buffer holds (DIT_SCRATCH_BYTES) */
 };
+
+/* Bytes of the static device scratch behind dit_attn_fwd_balanced_noalloc:
+   one copy per GPU the library runs on, held until the process ends. */
+#define DIT_SCRATCH_BYTES ((size_t)160 << 20)
 
 /*
  * Non-causal full-sequence attention with log-sum-exp  ([HB] Ulysses
@@ -142,6 +148,28 @@ int dit_attn_fwd_balanced(const void* q, const void* k, const void* v, void* o, 
  */
 int dit_attn_fwd_balanced_workspace(int B, int H, int Nq, int Nkv, int D, int slots,
                                     size_t* bytes);
+
+/*
+ * dit_attn_fwd_balanced without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, plan, kernels and results
+ * (bit for bit) as dit_attn_fwd_balanced; the key-chunk partials go to a
+ * static device array of DIT_SCRATCH_BYTES (160 MiB) per GPU instead of a
+ * caller workspace.  The call allocates nothing (no hipMalloc / hipFree, no
+ * allocating library routine); its first call on a device looks up that
+ * device's copy of the array once.
+ *
+ * Returns DIT_ESCRATCH, before any launch, when the plan's partials need more
+ * than DIT_SCRATCH_BYTES (dit_attn_fwd_balanced_workspace reports the size;
+ * the long-video shape B1 H10 N75600 D128 on 256 compute units needs 133 MB).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (on different streams, or from different threads) race; order
+ * them on one stream.  Nothing in the array has to start at zero (each call
+ * writes every partial it reads), and it keeps the last call's contents.
+ */
+int dit_attn_fwd_balanced_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  int B, int H, int Nq, int Nkv, int D, float scale, int o_dtype,
+                                  int slots, void* stream);
 
 /*
  * Attention backward: the gradients of sum(dout * O) for O = attention(q, k, v)

@@ -37,8 +37,9 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_strerror(lib):
     assert lib.dit_abi_version() == 1
-    for code in (0, -1, -2, -3, -4, -5, 7):
+    for code in (0, -1, -2, -3, -4, -5, -6, 7):
         assert lib.dit_strerror(code)
+    assert b"scratch" in lib.dit_strerror(dta.DIT_ESCRATCH)
 
 
 V = ctypes.c_void_p
@@ -104,6 +105,31 @@ def test_balanced_workspace_and_validation(lib):
     assert bal(Nkv=0) == dta.DIT_EINVAL
     assert bal(slots=-2) == dta.DIT_EINVAL
     assert bal(Nq=0, ws=NULL) == dta.DIT_OK                # nothing to compute
+
+
+def test_balanced_noalloc_validation(lib):
+    """The no-allocation balanced forward: argument errors as the workspace
+    form, and a plan whose partials exceed the static scratch is refused on
+    the host before any HIP call."""
+    nb = lambda o=A, od=0, B=1, H=10, Nq=75600, Nkv=75600, scale=0.125, slots=256, lse=A: \
+        lib.dit_attn_fwd_balanced_noalloc(A, A, A, o, lse, B, H, Nq, Nkv, 128, ctypes.c_float(scale),
+                                          od, slots, S)
+    assert nb(o=NULL) == dta.DIT_EINVAL
+    assert nb(o=MIS) == dta.DIT_EALIGN
+    assert nb(lse=V(0x10002)) == dta.DIT_EALIGN
+    assert nb(od=5) == dta.DIT_EUNSUPPORTED
+    assert nb(scale=float("nan")) == dta.DIT_EINVAL
+    assert nb(Nkv=0) == dta.DIT_EINVAL
+    assert nb(slots=-1) == dta.DIT_EINVAL
+    assert nb(Nq=0, o=NULL) == dta.DIT_OK
+    # 5120 tiles on 2048 slots: 1024 tail tiles in two key chunks, 270 MB of partials
+    n = ctypes.c_size_t(0)
+    assert lib.dit_attn_fwd_balanced_workspace(1, 40, 32768, 32768, 128, 2048, ctypes.byref(n)) == 0
+    assert n.value > dta.DIT_SCRATCH_BYTES
+    assert nb(H=40, Nq=32768, Nkv=32768, slots=2048) == dta.DIT_ESCRATCH
+    # the long-video plan on 256 compute units fits the scratch
+    assert lib.dit_attn_fwd_balanced_workspace(1, 10, 75600, 75600, 128, 256, ctypes.byref(n)) == 0
+    assert 0 < n.value <= dta.DIT_SCRATCH_BYTES
 
 
 def test_merge_validation(lib):
