@@ -13,7 +13,9 @@ attention FLOPs of the step (4 * 4*B*H*N^2*D) over the step's wall time.
 
 The fused leg runs the same step as four dit_attn_fwd_ulysses calls that
 read the token shards and write the token-shard output directly, with no
-exchange buffers; it is reported under "legs" beside the unfused step time.
+exchange buffers; it is reported under "legs" beside the unfused step, both
+timed with events on the launch stream, three repetitions each, interleaved
+three times (medians).
 
 The backward leg times dit_attn_bwd (dQ, dK, dV from the forward's O and
 LSE) on one head group; its TFLOP/s counts the five products of the
@@ -262,10 +264,16 @@ def main():
             for r in range(P):
                 dta.dit_attn_fwd_ulysses(*shards, r, out=fused_out, lse=lses[r])
 
-        fused_ms = time_it(fused_step, reps=3)
+        # the same timer and repetition count for both forms, interleaved
+        fused_v, unfused_v = [], []
+        for _ in range(3):
+            fused_v.append(time_it(fused_step, reps=3))
+            unfused_v.append(time_it(lambda: step(False), reps=3))
+        fused_ms, unfused_ms = float(np.median(fused_v)), float(np.median(unfused_v))
         legs.update({"fused_step_ms": fused_ms,
                      "fused_step_TFLOPs": P * flops_launch / (fused_ms * 1e-3) / 1e12,
-                     "unfused_step_ms": ms_per_step})
+                     "unfused_step_ms": unfused_ms,
+                     "fused_vs_unfused": unfused_ms / fused_ms})
 
         # backward leg: dit_attn_bwd on the same head group (the forward's O and
         # LSE, a seeded dO); algorithmic FLOPs of the five products 10*B*H*N^2*D.

@@ -207,31 +207,41 @@ __device__ __forceinline__ void tile_barrier() {
   __syncthreads();
 }
 
-// Stage one 64-key tile of K (or V) into LDS.  Each load instruction writes
-// 1 KB contiguously (lane i -> bytes [16i, 16i+16)); voff[n] is the byte
-// offset, within a tile, of the global chunk whose swizzled position that
-// is (see piece_offsets).  The keys of one (b, h) lie in segments of kseg
-// rows, sstride bytes apart (a single segment unless the keys come from
-// Ulysses token shards, whose length is then a multiple of the tile).  The
-// descriptor covers the tile's rows up to the end of its segment, so rows
-// past the end read as zero (its 32-bit size is at most one tile).
+// A stream of 64-key tiles of K (or V) in key order.  The keys of one (b, h)
+// lie in segments of kseg rows (a single segment for contiguous keys; one per
+// Ulysses token shard otherwise, whose length is then a multiple of the
+// tile), the end of one segment `jump` bytes before the start of the next.
+// p is the next tile's first row and left the rows from there to the end of
+// its segment: moving to the next tile is a few scalar operations, with no
+// division to find the segment.
+struct TileStream {
+  const char* p;
+  int left;
+};
+
+// Stage the stream's next tile into LDS and advance.  Each load instruction
+// writes 1 KB contiguously (lane i -> bytes [16i, 16i+16)); voff[n] is the
+// byte offset, within a tile, of the global chunk whose swizzled position
+// that is (see piece_offsets).  The descriptor covers the tile's rows up to
+// the end of its segment, so rows past the end read as zero (its 32-bit size
+// is at most one tile).
 template <int ROWB, int PIECES>
-__device__ __forceinline__ void stage_tile(const char* __restrict__ G, int k0, int kseg,
-                                           int64_t sstride, lds_t* buf, int wave, const int* voff) {
-  int local = k0;
-  if (k0 >= kseg) {
-    const int sg = k0 / kseg;
-    local = k0 - sg * kseg;
-    G += sg * sstride;
-  }
+__device__ __forceinline__ void stage_next(TileStream& s, int kseg, int64_t jump, lds_t* buf,
+                                           int wave, const int* voff) {
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(G + (int64_t)local * ROWB), (short)0, min(kseg - local, kBN) * ROWB, 0x00020000);
+      (void*)s.p, (short)0, min(s.left, kBN) * ROWB, 0x00020000);
 #pragma unroll
   for (int n = 0; n < (PIECES + kWaves - 1) / kWaves; ++n) {
     const int inst = n * kWaves + wave;
     if (PIECES % kWaves != 0 && inst >= PIECES) break;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsrc, (__attribute__((address_space(3))) void*)(buf + inst * 1024), 16, voff[n], 0, 0, 0);
+  }
+  s.p += kBN * ROWB;
+  s.left -= kBN;
+  if (s.left == 0) {  // end of a segment: on to the next one
+    s.p += jump;
+    s.left = kseg;
   }
 }
 
@@ -263,8 +273,9 @@ struct PassCtx {
   const char* Kb;    // keys / values of this (b, h): segment 0
   const char* Vb;
   int kseg;          // keys per segment (Nkv for contiguous keys)
-  int64_t kstride;   // bytes from one K segment to the next
-  int64_t vstride;   // bytes from one V segment to the next
+  int64_t kjump;     // bytes from the end of one K segment to the start of the next
+  int64_t vjump;     // the same for V
+  TileStream ks, vs; // the next K / V tile to stage
   lds_t *k0, *k1, *k2;  // K stages (separate scalars: never an indexed array)
   lds_t *v0, *v1, *v2;  // V stages
   int Nkv, ntiles, wave, lane, g;
@@ -447,17 +458,15 @@ __device__ __forceinline__ void slot(Frags<D, F8>& f, const f32x4 (&Sc)[2][kQB],
 template <int D, bool F8, int PH, bool MASK>
 __device__ __forceinline__ void tile_trip(int t, Frags<D, F8>& f, f32x4 (&S0)[2][kQB], f32x4 (&S1)[2][kQB],
                                           bf16x8 (&Pa)[kQB], bf16x8 (&Pb)[kQB],
-                                          const PassCtx<D, F8>& x) {
+                                          PassCtx<D, F8>& x) {
   using Gm = Geo<D>;
   using QK = QKOps<D, F8>;
   tile_barrier();  // K_{t+1}, V_t landed; every wave is done with tile t-1
   const int p2 = PH >= 0 ? PH + 2 : -1, p1 = PH >= 0 ? PH + 1 : -1;
-  if (t + 2 < x.ntiles)
-    stage_tile<QK::ROWB, QK::PIECES>(x.Kb, (t + 2) * kBN, x.kseg, x.kstride, KSTAGE(x, p2, t + 2),
-                                     x.wave, x.kld);
-  if (t + 1 < x.ntiles)
-    stage_tile<Gm::ROWB, Gm::PIECES>(x.Vb, (t + 1) * kBN, x.kseg, x.vstride, VSTAGE(x, p1, t + 1),
-                                     x.wave, x.vld);
+  if (t + 2 < x.ntiles)  // K tile t+2 is the K stream's next tile
+    stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kseg, x.kjump, KSTAGE(x, p2, t + 2), x.wave, x.kld);
+  if (t + 1 < x.ntiles)  // V tile t+1 is the V stream's next tile
+    stage_next<Gm::ROWB, Gm::PIECES>(x.vs, x.kseg, x.vjump, VSTAGE(x, p1, t + 1), x.wave, x.vld);
   const lds_t* kcur = KSTAGE(x, PH, t);
   const lds_t* knext = KSTAGE(x, p1, t + 1);
   const lds_t* vcur = VSTAGE(x, PH, t);
@@ -492,17 +501,18 @@ __device__ __forceinline__ void pv_step(Frags<D, F8>& f, const bf16x8 (&P)[kQB],
 // stage count), the partial last tile (if any) with masking, then the PV of
 // the last step.  Returns true if some row's sum outgrew its reference.
 template <int D, bool F8>
-__device__ __forceinline__ bool run_pass(Frags<D, F8>& f, const PassCtx<D, F8>& x) {
+__device__ __forceinline__ bool run_pass(Frags<D, F8>& f, PassCtx<D, F8>& x) {
   using Gm = Geo<D>;
   using QK = QKOps<D, F8>;
   // The first slot multiplies P = 0 by the V stage of tile -1 (stage 2): zero
   // it so no stale Inf/NaN bit pattern can turn 0 * V into NaN.
   for (int i = threadIdx.x; i < Gm::TILE / 16; i += kThreads)
     reinterpret_cast<lds_u32x4*>(x.v2)[i] = u32x4{0u, 0u, 0u, 0u};
-  stage_tile<QK::ROWB, QK::PIECES>(x.Kb, 0, x.kseg, x.kstride, x.k0, x.wave, x.kld);
-  if (x.ntiles > 1)
-    stage_tile<QK::ROWB, QK::PIECES>(x.Kb, kBN, x.kseg, x.kstride, x.k1, x.wave, x.kld);
-  stage_tile<Gm::ROWB, Gm::PIECES>(x.Vb, 0, x.kseg, x.vstride, x.v0, x.wave, x.vld);
+  x.ks = TileStream{x.Kb, x.kseg};
+  x.vs = TileStream{x.Vb, x.kseg};
+  stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kseg, x.kjump, x.k0, x.wave, x.kld);
+  if (x.ntiles > 1) stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kseg, x.kjump, x.k1, x.wave, x.kld);
+  stage_next<Gm::ROWB, Gm::PIECES>(x.vs, x.kseg, x.vjump, x.v0, x.wave, x.vld);
   f32x4 S0[2][kQB], S1[2][kQB];
   bf16x8 Pa[kQB], Pb[kQB];
 #pragma unroll
@@ -539,14 +549,15 @@ __device__ __forceinline__ bool run_pass(Frags<D, F8>& f, const PassCtx<D, F8>& 
 
 // Exact row max over all keys (only when the fixed-reference loop flagged).
 template <int D, bool F8>
-__device__ __forceinline__ void exact_max_pass(Frags<D, F8>& f, const PassCtx<D, F8>& x) {
+__device__ __forceinline__ void exact_max_pass(Frags<D, F8>& f, PassCtx<D, F8>& x) {
   using QK = QKOps<D, F8>;
   float m[kQB];
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) m[qb] = -INFINITY;
+  x.ks = TileStream{x.Kb, x.kseg};
   for (int t = 0; t < x.ntiles; ++t) {
     __syncthreads();  // every wave is done reading the stage
-    stage_tile<QK::ROWB, QK::PIECES>(x.Kb, t * kBN, x.kseg, x.kstride, x.k0, x.wave, x.kld);
+    stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kseg, x.kjump, x.k0, x.wave, x.kld);
     tile_barrier();  // landed
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -640,8 +651,10 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
   x.Kb = static_cast<const char*>(K) + (((int64_t)bb * lay.htot + hh) * lay.kseg + kbeg) * D * QKB;
   x.Vb = reinterpret_cast<const char*>(V + (((int64_t)bb * lay.htot + hh) * lay.kseg + kbeg) * D);
   x.kseg = lay.kseg - kbeg;
-  x.kstride = (int64_t)lay.B * lay.htot * lay.kseg * D * QKB;
-  x.vstride = (int64_t)lay.B * lay.htot * lay.kseg * D * 2;
+  // segment starts are B*H*kseg rows apart; the jump is from one segment's end
+  // (only key-split launches start inside a segment, and they have one)
+  x.kjump = ((int64_t)lay.B * lay.htot - 1) * lay.kseg * D * QKB;
+  x.vjump = ((int64_t)lay.B * lay.htot - 1) * lay.kseg * D * 2;
   x.k0 = (lds_t*)k0s; x.k1 = (lds_t*)k1s; x.k2 = (lds_t*)k2s;
   x.v0 = (lds_t*)v0s; x.v1 = (lds_t*)v1s; x.v2 = (lds_t*)v2s;
   x.Nkv = Nkv;
