@@ -26,7 +26,7 @@ tokens, then attention) on 512 text + 4096 image tokens, B1 H24 D128, and the
 attention alone; the cross leg times dit_attn_fwd_block of the 10-head share's
 32768 queries over 512 text keys.
 
-The fp8 leg quantizes the share's q and k per head to E4M3 (dit_quant_fp8)
+The fp8 leg quantizes the share's q and k per head to E4M3 (dit_quant_fp8_qk)
 and times dit_attn_fwd_fp8 on them (same FLOP count as the bf16 launch).  Two
 more bf16 forward legs: all 40 heads of the draw in one call, and the
 [1,10,75600,128] long-video shape.
@@ -328,12 +328,14 @@ def main():
         qc, qd = dta.dit_quant_fp8(q0)
         kc, kd = dta.dit_quant_fp8(k0)
         fo, fl = torch.empty_like(outs[0]), torch.empty_like(lses[0])
-        quant_ms = time_it(lambda: (dta.dit_quant_fp8(q0, qc, qd), dta.dit_quant_fp8(k0, kc, kd)),
-                           reps=10)
+        quant_ms = time_it(lambda: dta.dit_quant_fp8_qk(q0, k0, qc, kc, qd, kd), reps=10)
         fp8_ms = time_it(lambda: dta.dit_attn_fwd_fp8(qc, kc, v0, qd, kd, out=fo, lse=fl), reps=5)
+        # quantizer traffic: q and k read twice (amax pass, code pass), codes written
+        qbytes = 2 * (2 * 2 + 1) * B * H * N * D
         legs.update({"fp8_attn_ms": fp8_ms,
                      "fp8_attn_TFLOPs": flops_launch / (fp8_ms * 1e-3) / 1e12,
-                     "fp8_quant_qk_ms": quant_ms})
+                     "fp8_quant_qk_ms": quant_ms,
+                     "fp8_quant_qk_GBps": qbytes / (quant_ms * 1e-3) / 1e9})
         del qc, kc, fo, fl
 
         # single-pass ring-merge shape: all 40 heads of the [1,40,32768,128]

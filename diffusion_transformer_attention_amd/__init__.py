@@ -27,7 +27,7 @@ EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_balanced",
             "dit_attn_fwd_balanced_workspace", "dit_attn_fwd_balanced_noalloc",
             "dit_attn_fwd_ulysses", "dit_attn_bwd",
             "dit_attn_merge", "dit_rope_pack", "dit_attn_fwd_joint", "dit_quant_fp8",
-            "dit_attn_fwd_fp8", "ulysses_seq2head", "ulysses_head2seq", "dit_strerror",
+            "dit_quant_fp8_qk", "dit_attn_fwd_fp8", "ulysses_seq2head", "ulysses_head2seq", "dit_strerror",
             "dit_abi_version")
 
 _lib = None
@@ -54,6 +54,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dit_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P]
     lib.dit_attn_merge.argtypes = [P, P, I, P, P, I, I, I, I, I, P]
     lib.dit_quant_fp8.argtypes = [P, P, P, I, I, I, I, P]
+    lib.dit_quant_fp8_qk.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
     lib.dit_attn_fwd_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, I, P]
     lib.dit_rope_pack.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
     lib.dit_attn_fwd_joint.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P,
@@ -64,7 +65,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                  "dit_attn_fwd_balanced_workspace", "dit_attn_fwd_balanced_noalloc",
                  "dit_attn_fwd_ulysses", "dit_attn_bwd",
                  "dit_attn_merge", "dit_rope_pack", "dit_attn_fwd_joint", "dit_quant_fp8",
-                 "dit_attn_fwd_fp8", "ulysses_seq2head", "ulysses_head2seq", "dit_abi_version"):
+                 "dit_quant_fp8_qk", "dit_attn_fwd_fp8", "ulysses_seq2head", "ulysses_head2seq", "dit_abi_version"):
         getattr(lib, name).restype = ctypes.c_int
     lib.dit_strerror.argtypes = [ctypes.c_int]
     lib.dit_strerror.restype = ctypes.c_char_p
@@ -462,6 +463,40 @@ def dit_quant_fp8(x, codes=None, descale=None):
     rc = lib.dit_quant_fp8(_ptr(x), _ptr(c), _ptr(ds), B, H, N, D, _stream())
     _check(rc, "dit_quant_fp8")
     return c, ds
+
+
+def dit_quant_fp8_qk(q, k, q_codes=None, k_codes=None, q_descale=None, k_descale=None):
+    """dit_quant_fp8 of q [B,H,Nq,D] and k [B,H,Nkv,D] (bf16) in one call.
+
+    Returns (q_codes, k_codes, q_descale, k_descale).
+    """
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k")):
+        _need(t, n, 4)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{n} must be bf16")
+    B, H, Nq, D = q.shape
+    if k.shape[:2] != q.shape[:2] or k.shape[3] != D:
+        raise ValueError("k must be [B,H,Nkv,D] matching q")
+    Nkv = k.shape[2]
+    out = []
+    for c, x, n in ((q_codes, q, "q_codes"), (k_codes, k, "k_codes")):
+        c = torch.empty(x.shape, device=x.device, dtype=torch.uint8) if c is None else c
+        _codes(c, n)
+        if c.shape != x.shape:
+            raise ValueError(f"{n} must match its input")
+        out.append(c)
+    ds = []
+    for d, n in ((q_descale, "q_descale"), (k_descale, "k_descale")):
+        d = torch.empty((B, H), device=q.device, dtype=torch.float32) if d is None else d
+        _need(d, n, 2)
+        if d.dtype != torch.float32 or tuple(d.shape) != (B, H):
+            raise ValueError(f"{n} must be float32 [B,H]")
+        ds.append(d)
+    rc = lib.dit_quant_fp8_qk(_ptr(q), _ptr(k), _ptr(out[0]), _ptr(out[1]), _ptr(ds[0]), _ptr(ds[1]),
+                              B, H, Nq, Nkv, D, _stream())
+    _check(rc, "dit_quant_fp8_qk")
+    return out[0], out[1], ds[0], ds[1]
 
 
 def dit_attn_fwd_fp8(q, k, v, q_descale, k_descale, scale=None, out_dtype=torch.bfloat16,

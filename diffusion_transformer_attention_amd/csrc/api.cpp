@@ -303,6 +303,26 @@ int dit_quant_fp8(const void* x, void* codes, float* descale, int B, int H, int 
                                               static_cast<hipStream_t>(stream)));
 }
 
+int dit_quant_fp8_qk(const void* q, const void* k, void* q_codes, void* k_codes, float* q_descale,
+                     float* k_descale, int B, int H, int Nq, int Nkv, int D, void* stream) {
+  if (B < 0 || H < 0 || Nq < 0 || Nkv < 0 || D <= 0) return DIT_EINVAL;
+  if (!supported_head_dim(D)) return DIT_EUNSUPPORTED;
+  if (!size_ok(B, H, Nq, D) || !size_ok(B, H, Nkv, D) || (int64_t)B * H > 0x7fffffff)
+    return DIT_ERANGE;
+  if (B == 0 || H == 0) return DIT_OK;
+  if (!q_descale || !k_descale || (Nq > 0 && (!q || !q_codes)) || (Nkv > 0 && (!k || !k_codes)))
+    return DIT_EINVAL;
+  if (!aligned(q_descale, 4) || !aligned(k_descale, 4)) return DIT_EALIGN;
+  if (Nq > 0 && (!aligned(q, 16) || !aligned(q_codes, 8))) return DIT_EALIGN;
+  if (Nkv > 0 && (!aligned(k, 16) || !aligned(k_codes, 8))) return DIT_EALIGN;
+  const void* x[2] = {q, k};
+  void* c[2] = {q_codes, k_codes};
+  float* ds[2] = {q_descale, k_descale};
+  const int n[2] = {Nq, Nkv};
+  return map_launch(ditattn::launch_quant_fp8_n(x, c, ds, n, 2, B, H, D,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 int dit_attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
                      const float* k_descale, void* o, float* lse, int B, int H, int Nq, int Nkv,
                      int D, float scale, int o_dtype, void* stream) {

@@ -53,6 +53,10 @@ hipError_t launch_attn_fp8(const void* q, const void* k, const void* v, const fl
 // bf16 x [B,H,N,D] -> E4M3 codes [B,H,N,D] and float32 descale [B,H] (D % 8 == 0).
 hipError_t launch_quant_fp8(const void* x, void* codes, float* descale, int B, int H, int N, int D,
                             hipStream_t stream);
+// The same for 1 or 2 tensors of one [B,H] head grid (token counts N[t]) in
+// three launches.
+hipError_t launch_quant_fp8_n(const void* const* x, void* const* codes, float* const* descale,
+                              const int* N, int ntensors, int B, int H, int D, hipStream_t stream);
 
 // Backward, bf16 q/k/v/o/dout (head dim 128), float32 lse in, delta out
 // ([B,H,Nq]), float32 dq/dk/dv.

@@ -7,11 +7,17 @@
 //                  head), amax = max |x| over the head
 //   code         = E4M3(clamp(x / descale, -448, 448)), the quotient correctly
 //                  rounded in float32, the conversion round-to-nearest-even
-// Four launches: zero the descale buffer, which then holds amax as float
-// bits (a non-negative float orders like its bit pattern, so an unsigned
-// atomic max is exact and order-independent); one pass for amax; one pass
-// writing the codes; last, amax -> descale in place.  HBM-bound: x is read twice and
-// the codes written once (5 bytes per element).
+// Three launches for one or two tensors (q and k of one attention call
+// together): clear the descale words; one pass for amax, whose blocks fold
+// their maxima into the head's word with an unsigned atomic max of
+// (amax bits | 0x80000000) (a non-negative float orders like its bit pattern,
+// so the max is exact and order-independent, and the set top bit marks the
+// word as an amax); one pass writing the codes, in which every block turns
+// the word into the descale itself -- a word with the top bit clear is
+// already the descale -- and the first block of each head stores it (every
+// block would store the same value, so the order of these stores does not
+// matter).  HBM-bound: x is read twice and the codes written once (5 bytes
+// per element).
 #include "launch.h"
 
 namespace ditattn {
@@ -20,40 +26,67 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kVec = 4;  // 16-byte vectors (8 elements) per thread per block step
 constexpr float kE4M3Max = 448.0f;
+constexpr unsigned kAmaxTag = 0x80000000u;
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-__global__ void zero_kernel(float* __restrict__ p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0.0f;
+// One or two tensors of the same [B,H] head grid.
+struct QuantJob {
+  const u32x4* x[2];
+  u32x2* codes[2];
+  unsigned* word[2];       // the descale buffers, as words
+  int64_t vec_per_head[2];  // 16-byte vectors per head (0: empty tensor)
+  int blocks[2];            // blocks per head of the pass
+  int ntensors, nbh;
+};
+
+// Block ids: tensor 0's heads first, then tensor 1's; within a tensor, head
+// then chunk.
+__device__ __forceinline__ void block_of(const QuantJob& j, int& t, int& bh, int& chunk) {
+  int b = blockIdx.x;
+  t = 0;
+  const int n0 = j.nbh * j.blocks[0];
+  if (b >= n0) {
+    t = 1;
+    b -= n0;
+  }
+  bh = b / j.blocks[t];
+  chunk = b - bh * j.blocks[t];
 }
 
-// Block b handles head b / bph and strides over it, so a head takes at most
-// kAmaxBlocks atomics (thousands of atomics on one address serialize at L2).
+// Clear every descale word; an empty tensor's heads get their final descale 1.
+__global__ void init_kernel(QuantJob j) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  for (int t = 0; t < j.ntensors; ++t)
+    if (i < j.nbh) j.word[t][i] = j.vec_per_head[t] > 0 ? 0u : __float_as_uint(1.0f);
+}
+
+// Block b of a head strides over it, so a head takes at most kAmaxBlocks
+// atomics (thousands of atomics on one address serialize at L2).
 constexpr int kAmaxBlocks = 64;
 
-__global__ __launch_bounds__(kThreads) void amax_kernel(const u32x4* __restrict__ x,
-                                                       unsigned* __restrict__ amax,
-                                                       int64_t vec_per_head, int bph) {
-  const int bh = blockIdx.x / bph;
-  const int chunk = blockIdx.x - bh * bph;
-  const u32x4* src = x + (int64_t)bh * vec_per_head;
+__global__ __launch_bounds__(kThreads) void amax_kernel(QuantJob j) {
+  int t, bh, chunk;
+  block_of(j, t, bh, chunk);
+  const int64_t vph = j.vec_per_head[t];
+  const u32x4* src = j.x[t] + (int64_t)bh * vph;
   float m = 0.0f;
-  const int64_t step = (int64_t)bph * kVec * kThreads;
-  for (int64_t base = (int64_t)chunk * kVec * kThreads; base < vec_per_head; base += step) {
+  const int64_t step = (int64_t)j.blocks[t] * kVec * kThreads;
+  for (int64_t base = (int64_t)chunk * kVec * kThreads; base < vph; base += step) {
+    u32x4 v[kVec];
 #pragma unroll
-    for (int u = 0; u < kVec; ++u) {
+    for (int u = 0; u < kVec; ++u) {  // all loads first
       const int64_t i = base + u * kThreads + threadIdx.x;
-      if (i < vec_per_head) {
-        const u32x4 v = src[i];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          m = fmaxf(m, __uint_as_float((v[w] & 0x7fffu) << 16));
-          m = fmaxf(m, __uint_as_float(v[w] & 0x7fff0000u));
-        }
-      }
+      v[u] = i < vph ? src[i] : u32x4{0u, 0u, 0u, 0u};
     }
+#pragma unroll
+    for (int u = 0; u < kVec; ++u)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        m = fmaxf(m, __uint_as_float((v[u][w] & 0x7fffu) << 16));
+        m = fmaxf(m, __uint_as_float(v[u][w] & 0x7fff0000u));
+      }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
@@ -63,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const u32x4* __restrict_
   if (threadIdx.x == 0) {
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, wmax[w]);
-    atomicMax(amax + bh, __float_as_uint(m));
+    atomicMax(j.word[t] + bh, __float_as_uint(m) | kAmaxTag);
   }
 }
 
@@ -72,28 +105,36 @@ __device__ __forceinline__ float descale_of(unsigned amax_bits) {
   return a > 0.0f ? __fdiv_rn(a, kE4M3Max) : 1.0f;
 }
 
+// The head's descale from its word: an amax (top bit set) or the descale.
+__device__ __forceinline__ float descale_from_word(unsigned w) {
+  return (w & kAmaxTag) ? descale_of(w & ~kAmaxTag) : __uint_as_float(w);
+}
+
 __device__ __forceinline__ float quotient(float v, float d) {
   return fminf(fmaxf(__fdiv_rn(v, d), -kE4M3Max), kE4M3Max);
 }
 
-__global__ __launch_bounds__(kThreads) void quant_kernel(const u32x4* __restrict__ x,
-                                                        u32x2* __restrict__ codes,
-                                                        const unsigned* __restrict__ amax,
-                                                        int64_t vec_per_head, int bph) {
-  const int bh = blockIdx.x / bph;
-  const int chunk = blockIdx.x - bh * bph;
-  const float d = descale_of(amax[bh]);
-  const u32x4* src = x + (int64_t)bh * vec_per_head;
-  u32x2* dst = codes + (int64_t)bh * vec_per_head;
+__global__ __launch_bounds__(kThreads) void quant_kernel(QuantJob j) {
+  int t, bh, chunk;
+  block_of(j, t, bh, chunk);
+  const int64_t vph = j.vec_per_head[t];
+  const float d = descale_from_word(__atomic_load_n(j.word[t] + bh, __ATOMIC_RELAXED));
+  const u32x4* src = j.x[t] + (int64_t)bh * vph;
+  u32x2* dst = j.codes[t] + (int64_t)bh * vph;
+  u32x4 v[kVec];
+#pragma unroll
+  for (int u = 0; u < kVec; ++u) {  // all loads first
+    const int64_t i = ((int64_t)chunk * kVec + u) * kThreads + threadIdx.x;
+    v[u] = i < vph ? src[i] : u32x4{0u, 0u, 0u, 0u};
+  }
 #pragma unroll
   for (int u = 0; u < kVec; ++u) {
     const int64_t i = ((int64_t)chunk * kVec + u) * kThreads + threadIdx.x;
-    if (i < vec_per_head) {
-      const u32x4 v = src[i];
+    if (i < vph) {
       unsigned out[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const unsigned w0 = v[2 * h], w1 = v[2 * h + 1];
+        const unsigned w0 = v[u][2 * h], w1 = v[u][2 * h + 1];
         unsigned r = __builtin_amdgcn_cvt_pk_fp8_f32(quotient(__uint_as_float(w0 << 16), d),
                                                      quotient(__uint_as_float(w0 & 0xffff0000u), d),
                                                      0, false);
@@ -104,35 +145,48 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const u32x4* __restrict
       dst[i] = u32x2{out[0], out[1]};
     }
   }
-}
-
-__global__ void finalize_kernel(float* __restrict__ descale, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) descale[i] = descale_of(__float_as_uint(descale[i]));
+  if (chunk == 0 && threadIdx.x == 0)
+    __atomic_store_n(j.word[t] + bh, __float_as_uint(d), __ATOMIC_RELAXED);
 }
 
 }  // namespace
 
+hipError_t launch_quant_fp8_n(const void* const* x, void* const* codes, float* const* descale,
+                              const int* N, int ntensors, int B, int H, int D,
+                              hipStream_t stream) {
+  QuantJob j{};
+  j.ntensors = ntensors;
+  j.nbh = B * H;
+  const int64_t per_block = (int64_t)kVec * kThreads;
+  int64_t qblocks = 0, ablocks = 0;
+  for (int t = 0; t < ntensors; ++t) {
+    j.x[t] = static_cast<const u32x4*>(x[t]);
+    j.codes[t] = static_cast<u32x2*>(codes[t]);
+    j.word[t] = reinterpret_cast<unsigned*>(descale[t]);
+    j.vec_per_head[t] = (int64_t)N[t] * D / 8;
+    const int64_t bph = (j.vec_per_head[t] + per_block - 1) / per_block;
+    if (bph * j.nbh > 0x3fffffff) return hipErrorInvalidValue;
+    qblocks += bph * j.nbh;
+    ablocks += (bph < kAmaxBlocks ? bph : kAmaxBlocks) * j.nbh;
+  }
+  const unsigned small = (unsigned)((j.nbh + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(init_kernel, dim3(small), dim3(kThreads), 0, stream, j);
+  if (qblocks > 0) {  // an empty tensor has 0 blocks; its descale is already final
+    QuantJob a = j;
+    for (int t = 0; t < ntensors; ++t) {
+      const int64_t bph = (j.vec_per_head[t] + per_block - 1) / per_block;
+      a.blocks[t] = (int)(bph < kAmaxBlocks ? bph : kAmaxBlocks);
+      j.blocks[t] = (int)bph;
+    }
+    hipLaunchKernelGGL(amax_kernel, dim3((unsigned)ablocks), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(quant_kernel, dim3((unsigned)qblocks), dim3(kThreads), 0, stream, j);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_fp8(const void* x, void* codes, float* descale, int B, int H, int N, int D,
                             hipStream_t stream) {
-  const int nbh = B * H;
-  const int64_t vec_per_head = (int64_t)N * D / 8;
-  const int64_t per_block = (int64_t)kVec * kThreads;
-  const int64_t bph = (vec_per_head + per_block - 1) / per_block;
-  if (bph * nbh > 0x7fffffff) return hipErrorInvalidValue;
-  const unsigned small = (unsigned)((nbh + kThreads - 1) / kThreads);
-  hipLaunchKernelGGL(zero_kernel, dim3(small), dim3(kThreads), 0, stream, descale, nbh);
-  if (bph > 0) {  // N == 0: every head is empty, amax stays 0 and descale becomes 1
-    const int64_t abph = bph < kAmaxBlocks ? bph : kAmaxBlocks;
-    hipLaunchKernelGGL(amax_kernel, dim3((unsigned)(abph * nbh)), dim3(kThreads), 0, stream,
-                       static_cast<const u32x4*>(x), reinterpret_cast<unsigned*>(descale),
-                       vec_per_head, (int)abph);
-    hipLaunchKernelGGL(quant_kernel, dim3((unsigned)(bph * nbh)), dim3(kThreads), 0, stream,
-                       static_cast<const u32x4*>(x), static_cast<u32x2*>(codes),
-                       reinterpret_cast<const unsigned*>(descale), vec_per_head, (int)bph);
-  }
-  hipLaunchKernelGGL(finalize_kernel, dim3(small), dim3(kThreads), 0, stream, descale, nbh);
-  return hipGetLastError();
+  return launch_quant_fp8_n(&x, &codes, &descale, &N, 1, B, H, D, stream);
 }
 
 }  // namespace ditattn

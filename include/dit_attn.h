@@ -313,6 +313,19 @@ int dit_quant_fp8(const void* x, void* codes, float* descale, int B, int H, int 
                   void* stream);
 
 /*
+ * dit_quant_fp8 of the queries and keys of one attention call together, in
+ * three launches instead of six (same codes and descales, bit for bit):
+ *
+ *   q : bf16 [B,H,Nq,D] -> q_codes uint8 [B,H,Nq,D], q_descale float32 [B,H]
+ *   k : bf16 [B,H,Nkv,D] -> k_codes uint8 [B,H,Nkv,D], k_descale float32 [B,H]
+ *
+ * Alignment and errors as dit_quant_fp8, for each tensor.  The four outputs
+ * must not overlap each other or the inputs.
+ */
+int dit_quant_fp8_qk(const void* q, const void* k, void* q_codes, void* k_codes, float* q_descale,
+                     float* k_descale, int B, int H, int Nq, int Nkv, int D, void* stream);
+
+/*
  * FP8 attention ([HC], reading as above): scores from E4M3 queries and keys,
  *
  *   s_ij = scale * q_descale[b,h] * k_descale[b,h] * (q_i . k_j)   (codes decoded)

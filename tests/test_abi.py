@@ -237,6 +237,22 @@ def test_quant_fp8_validation(lib):
     assert qz(B=2 ** 20, H=2 ** 12, N=1, D=32) == dta.DIT_ERANGE
 
 
+def test_quant_fp8_qk_validation(lib):
+    def qk(q=A, k=A, qc=A, kc=A, qd=A, kd=A, B=1, H=2, Nq=64, Nkv=32, D=128):
+        return lib.dit_quant_fp8_qk(q, k, qc, kc, qd, kd, B, H, Nq, Nkv, D, S)
+    assert qk(D=96) == dta.DIT_EUNSUPPORTED
+    assert qk(qd=NULL) == dta.DIT_EINVAL
+    assert qk(kd=NULL) == dta.DIT_EINVAL
+    assert qk(k=NULL) == dta.DIT_EINVAL
+    assert qk(qc=NULL) == dta.DIT_EINVAL
+    assert qk(kc=V(0x10004)) == dta.DIT_EALIGN
+    assert qk(q=MIS) == dta.DIT_EALIGN
+    assert qk(kd=V(0x10002)) == dta.DIT_EALIGN
+    assert qk(Nkv=-1) == dta.DIT_EINVAL
+    assert qk(B=0) == dta.DIT_OK
+    assert qk(B=2 ** 20, H=2 ** 12, Nq=1, Nkv=1, D=32) == dta.DIT_ERANGE
+
+
 def test_attn_fp8_validation(lib):
     def f(q=A, qd=A, kd=A, o=A, lse=A, Nq=64, Nkv=64, D=128, scale=0.125, od=0):
         return lib.dit_attn_fwd_fp8(q, A, A, qd, kd, o, lse, 1, 2, Nq, Nkv, D,

@@ -74,6 +74,34 @@ def test_quant_empty_sequence():
     assert codes.numel() == 0 and torch.equal(ds, torch.ones_like(ds))
 
 
+@pytest.mark.parametrize("B,H,Nq,Nkv,D", [(1, 3, 300, 77, 128), (2, 2, 64, 0, 64), (1, 10, 32768, 32768, 128)])
+def test_quant_qk_equals_two_single_calls_and_oracle(B, H, Nq, Nkv, D):
+    """dit_quant_fp8_qk (q and k in three launches) gives the bits of two
+    dit_quant_fp8 calls, and the oracle's codes and descales."""
+    say("quant qk", B, H, Nq, Nkv, D)
+    r = np.random.default_rng(Nq + 3 * Nkv)
+    xs = []
+    for n in (Nq, Nkv):
+        x = r.standard_normal((B, H, n, D)).astype(np.float32)
+        x *= np.exp(r.uniform(-4, 4, size=x.shape)).astype(np.float32)
+        if n and H > 2:
+            x[0, 1] = 0.0
+        xs.append(datagen.bf16_bits(x))
+    tq, tk = (bits_to_torch_bf16(x) for x in xs)
+    qc, kc, qd, kd = dta.dit_quant_fp8_qk(tq, tk)
+    qc1, qd1 = dta.dit_quant_fp8(tq)
+    kc1, kd1 = dta.dit_quant_fp8(tk)
+    assert torch.equal(qc, qc1) and torch.equal(qd, qd1)
+    assert torch.equal(kc, kc1) and torch.equal(kd, kd1)
+    if Nq * H <= 300 * 3:
+        for bits, c, d in ((xs[0], qc, qd), (xs[1], kc, kd)):
+            want_c, want_d = oracle.quantize_fp8(f32(bits))
+            assert np.array_equal(d.cpu().numpy(), want_d)
+            assert np.array_equal(c.cpu().numpy(), want_c)
+    if Nkv == 0:
+        assert torch.equal(kd, torch.ones_like(kd))
+
+
 def _oracle_inputs(qb, kb):
     qc, qd = oracle.quantize_fp8(f32(qb))
     kc, kd = oracle.quantize_fp8(f32(kb))
