@@ -202,8 +202,13 @@ __device__ __forceinline__ float quad_sum(float x) {
 // wave waits for its own loads (s_waitcnt vmcnt(0); gfx9 encoding: vmcnt
 // bits [3:0] and [15:14] zero, expcnt 7 and lgkmcnt 15 = no wait) before the
 // barrier that publishes the tile to the other waves.
+// WAITN > 0: wait only until at most WAITN memory operations are left, for
+// the first waits of a tile whose loads were issued before the previous
+// tile's WAITN output stores (vmcnt retires in order, so the loads are then
+// done and the stores may still be in flight).
+template <int WAITN = 0>
 __device__ __forceinline__ void tile_barrier() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (WAITN & 15) | ((WAITN >> 4) << 14));
   __syncthreads();
 }
 
@@ -455,13 +460,13 @@ __device__ __forceinline__ void slot(Frags<D, F8>& f, const f32x4 (&Sc)[2][kQB],
 // On entry S0 holds S^T of step 2t and Pa holds P of step 2t-1; on exit S0
 // holds S^T of step 2t+2 (garbage past the last tile, never used) and Pa
 // holds P of step 2t+1.
-template <int D, bool F8, int PH, bool MASK>
+template <int D, bool F8, int PH, bool MASK, int WAITN = 0>
 __device__ __forceinline__ void tile_trip(int t, Frags<D, F8>& f, f32x4 (&S0)[2][kQB], f32x4 (&S1)[2][kQB],
                                           bf16x8 (&Pa)[kQB], bf16x8 (&Pb)[kQB],
                                           PassCtx<D, F8>& x) {
   using Gm = Geo<D>;
   using QK = QKOps<D, F8>;
-  tile_barrier();  // K_{t+1}, V_t landed; every wave is done with tile t-1
+  tile_barrier<WAITN>();  // K_{t+1}, V_t landed; every wave is done with tile t-1
   const int p2 = PH >= 0 ? PH + 2 : -1, p1 = PH >= 0 ? PH + 1 : -1;
   if (t + 2 < x.ntiles)  // K tile t+2 is the K stream's next tile
     stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kseg, x.kjump, KSTAGE(x, p2, t + 2), x.wave, x.kld);
@@ -497,27 +502,38 @@ __device__ __forceinline__ void pv_step(Frags<D, F8>& f, const bf16x8 (&P)[kQB],
   for (int qb = 0; qb < kQB; ++qb) f.lb[qb] = mfma16(ones8, P[qb], f.lb[qb]);
 }
 
-// One full pass over the keys: stage, the unmasked tiles (unrolled by the
-// stage count), the partial last tile (if any) with masking, then the PV of
-// the last step.  Returns true if some row's sum outgrew its reference.
+// Stage the first K tiles (0 and 1) and V tile 0 of a pass.
 template <int D, bool F8>
-__device__ __forceinline__ bool run_pass(Frags<D, F8>& f, PassCtx<D, F8>& x) {
+__device__ __forceinline__ void stage_first(PassCtx<D, F8>& x) {
   using Gm = Geo<D>;
   using QK = QKOps<D, F8>;
-  // The first slot multiplies P = 0 by the V stage of tile -1 (stage 2): zero
-  // it so no stale Inf/NaN bit pattern can turn 0 * V into NaN.
-  for (int i = threadIdx.x; i < Gm::TILE / 16; i += kThreads)
-    reinterpret_cast<lds_u32x4*>(x.v2)[i] = u32x4{0u, 0u, 0u, 0u};
   x.ks = TileStream{x.Kb, x.kseg};
   x.vs = TileStream{x.Vb, x.kseg};
   stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kseg, x.kjump, x.k0, x.wave, x.kld);
   if (x.ntiles > 1) stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kseg, x.kjump, x.k1, x.wave, x.kld);
   stage_next<Gm::ROWB, Gm::PIECES>(x.vs, x.kseg, x.vjump, x.v0, x.wave, x.vld);
+}
+
+// One full pass over the keys whose first tiles stage_first has issued: the
+// unmasked tiles (unrolled by the stage count), the partial last tile (if
+// any) with masking, then the PV of the last step.  Returns true if some
+// row's sum outgrew its reference.  PF: the first tiles were issued before
+// the previous tile's NST output stores, so the first two waits leave those
+// stores in flight.
+template <int D, bool F8, bool PF>
+__device__ __forceinline__ bool run_pass_body(Frags<D, F8>& f, PassCtx<D, F8>& x) {
+  using Gm = Geo<D>;
+  using QK = QKOps<D, F8>;
+  constexpr int NST = PF ? kQB * Gm::DB : 0;  // output store instructions per wave
+  // The first slot multiplies P = 0 by the V stage of tile -1 (stage 2): zero
+  // it so no stale Inf/NaN bit pattern can turn 0 * V into NaN.
+  for (int i = threadIdx.x; i < Gm::TILE / 16; i += kThreads)
+    reinterpret_cast<lds_u32x4*>(x.v2)[i] = u32x4{0u, 0u, 0u, 0u};
   f32x4 S0[2][kQB], S1[2][kQB];
   bf16x8 Pa[kQB], Pb[kQB];
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) Pa[qb] = bf16x8{};
-  tile_barrier();  // K tile 0 (and K 1, V 0) landed
+  tile_barrier<NST>();  // K tile 0 (and K 1, V 0) landed
   qk_step<D, F8>(S0, x.k0, x, f);
   if (f.m[0] == -INFINITY) {  // first attempt: reference max = max of step 0
     float m[kQB];
@@ -533,6 +549,12 @@ __device__ __forceinline__ bool run_pass(Frags<D, F8>& f, PassCtx<D, F8>& x) {
   const bool partial = (x.Nkv % kBN) != 0;
   const int nfull = partial ? x.ntiles - 1 : x.ntiles;
   int t = 0;
+  if (PF && nfull >= kStages) {  // no load is issued between the first wait and trip 0's
+    tile_trip<D, F8, 0, false, NST>(0, f, S0, S1, Pa, Pb, x);
+    tile_trip<D, F8, 1, false>(1, f, S0, S1, Pa, Pb, x);
+    tile_trip<D, F8, 2, false>(2, f, S0, S1, Pa, Pb, x);
+    t = kStages;
+  }
   for (; t + kStages <= nfull; t += kStages) {
     tile_trip<D, F8, 0, false>(t, f, S0, S1, Pa, Pb, x);
     tile_trip<D, F8, 1, false>(t + 1, f, S0, S1, Pa, Pb, x);
@@ -606,10 +628,144 @@ struct Split {
   int64_t row0, rows;
 };
 
-// The kernel body.  F8: q and k are E4M3 codes (1 byte per element) whose
-// scores are rescaled by the per-(b, h) factors qds[bh] * kds[bh]; else q
-// and k are bf16 and qds, kds are unused.  SPLIT: a key-split launch (above),
-// total_tiles is then the number of units.
+// Where one work unit's rows and keys are: the unit's head (bh), query tile
+// (qt), key chunk (SPLIT), its key count and the pointers of its K and V.
+struct TileInfo {
+  int bh, qt, chunk, Nkv, kseg;
+  int64_t qhead;  // element offset of the head's segment 0 in Q and O
+  const char* Kb;
+  const char* Vb;
+  float c;        // softmax constant (F8: times the head's descales)
+};
+
+template <int D, bool F8, bool SPLIT>
+__device__ __forceinline__ TileInfo tile_info(int u, int total, int n_qtiles, int Nkv, const Layout& lay,
+                                              const void* K, const __bf16* V, float c,
+                                              const float* qds, const float* kds, const Split& sp) {
+  constexpr int QKB = F8 ? 1 : 2;  // bytes per q / k element
+  TileInfo ti;
+  int tile = remap_xcd(u, total);
+  ti.chunk = 0;
+  if (SPLIT) {
+    const int v = tile;
+    tile = sp.tile0 + v / sp.nsplit;
+    ti.chunk = v - (v / sp.nsplit) * sp.nsplit;
+  }
+  const int kbeg = SPLIT ? ti.chunk * sp.kc : 0;  // first key of the chunk
+  ti.Nkv = SPLIT ? min(sp.kc, Nkv - kbeg) : Nkv;
+  ti.bh = tile / n_qtiles;
+  ti.qt = tile - ti.bh * n_qtiles;
+  // bh = b * hg + h'; the buffers hold head hoff + h' of batch b.
+  const int bb = ti.bh / lay.hg;
+  const int hh = lay.hoff + (ti.bh - bb * lay.hg);
+  ti.qhead = ((int64_t)bb * lay.htot + hh) * lay.qseg * D;
+  ti.Kb = static_cast<const char*>(K) + (((int64_t)bb * lay.htot + hh) * lay.kseg + kbeg) * D * QKB;
+  ti.Vb = reinterpret_cast<const char*>(V + (((int64_t)bb * lay.htot + hh) * lay.kseg + kbeg) * D);
+  ti.kseg = lay.kseg - kbeg;
+  ti.c = F8 ? c * qds[ti.bh] * kds[ti.bh] : c;
+  return ti;
+}
+
+// Point the pass at a unit, issue its first K / V tiles and load its queries
+// (rows past Nq load row Nq - 1).
+template <int D, bool F8>
+__device__ __forceinline__ void begin_tile(Frags<D, F8>& f, PassCtx<D, F8>& x, const TileInfo& ti,
+                                           const void* Q, int Nq, const Layout& lay,
+                                           int64_t qsstride, int c16) {
+  using QK = QKOps<D, F8>;
+  constexpr int QKB = F8 ? 1 : 2;
+  x.Kb = ti.Kb;
+  x.Vb = ti.Vb;
+  x.kseg = ti.kseg;
+  x.Nkv = ti.Nkv;
+  x.ntiles = (ti.Nkv + kBN - 1) / kBN;
+  x.c = ti.c;
+  stage_first<D, F8>(x);
+  const int qrow0 = ti.qt * kBM + x.wave * (16 * kQB) + c16;
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int row = min(qrow0 + 16 * qb, Nq - 1);
+    const char* qrow_p =
+        static_cast<const char*>(Q) + token_offset(row, lay.qseg, ti.qhead, qsstride, D) * QKB;
+#pragma unroll
+    for (int ks = 0; ks < QK::KS; ++ks) f.q[qb][ks] = QK::load_q(qrow_p, x.g, ks);
+  }
+}
+
+// Attention of the unit begin_tile pointed the pass at.  Second attempt only
+// if some row's sum outgrew its reference max: then the tile is redone with
+// the exact row max (all waves decide together).  Ends with every wave done
+// with the LDS stages.
+template <int D, bool F8, bool PF>
+__device__ __forceinline__ void compute_tile(Frags<D, F8>& f, PassCtx<D, F8>& x) {
+  using Gm = Geo<D>;
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    f.m[qb] = -INFINITY;
+    f.l[qb] = 0.f;
+    f.lb[qb] = f32x4{};
+#pragma unroll
+    for (int db = 0; db < Gm::DB; ++db) f.o[qb][db] = f32x4{};
+  }
+  const bool flag = run_pass_body<D, F8, PF>(f, x);
+  if (__syncthreads_or(flag)) {
+    exact_max_pass<D, F8>(f, x);
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      f.l[qb] = 0.f;
+      f.lb[qb] = f32x4{};
+#pragma unroll
+      for (int db = 0; db < Gm::DB; ++db) f.o[qb][db] = f32x4{};
+    }
+    stage_first<D, F8>(x);
+    run_pass_body<D, F8, false>(f, x);
+    __syncthreads();
+  }
+}
+
+// Epilogue of one unit: O = O^T / lb, LSE = (m*c + log2 l) * ln 2.  Every
+// lane stores (a row past Nq stores row Nq - 1, which it computed from that
+// row's query, so the same bits), so each wave issues exactly kQB * DB output
+// stores, which the next unit's first waits count on.
+template <int D, bool OUT_F32, bool F8, bool SPLIT>
+__device__ __forceinline__ void store_tile(const Frags<D, F8>& f, const TileInfo& ti, void* Oout,
+                                           float* LSE, int Nq, const Layout& lay, int64_t qsstride,
+                                           const Split& sp, int wave, int c16, int g) {
+  using Gm = Geo<D>;
+  const int qrow0 = ti.qt * kBM + wave * (16 * kQB) + c16;
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const float l_tot = quad_sum(f.l[qb]);
+    const float inv = 1.0f / f.lb[qb][0];
+    const int qrow = min(qrow0 + 16 * qb, Nq - 1);
+    const int64_t wrow = (int64_t)ti.chunk * sp.rows + (int64_t)ti.bh * Nq + qrow - sp.row0;
+    const int64_t obase = SPLIT ? wrow * D : token_offset(qrow, lay.qseg, ti.qhead, qsstride, D);
+#pragma unroll
+    for (int db = 0; db < Gm::DB; ++db) {
+      const int d0 = db * 16 + 4 * g;
+      const f32x4 val = f.o[qb][db] * inv;
+      if (OUT_F32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(Oout) + obase + d0) = val;
+      } else {
+        const bf16x4 b = {(__bf16)val[0], (__bf16)val[1], (__bf16)val[2], (__bf16)val[3]};
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(Oout) + obase + d0) = b;
+      }
+    }
+    if (LSE && g == 0)
+      LSE[SPLIT ? wrow : (int64_t)ti.bh * Nq + qrow] =
+          (f.m[qb] * ti.c + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
+  }
+}
+
+// The kernel body: a persistent workgroup computes units blockIdx.x,
+// blockIdx.x + gridDim.x, ... (gridDim.x a multiple of 8, so they all map to
+// one XCD's range).  After a unit's last LDS read it issues the next unit's
+// first K / V tiles and query loads, and only then stores the unit's output,
+// so the next unit's first waits need not wait for those stores.  F8: q and
+// k are E4M3 codes (1 byte per element) whose scores are rescaled by the
+// per-(b, h) factors qds[bh] * kds[bh]; else q and k are bf16 and qds, kds
+// are unused.  SPLIT: a key-split launch, total_tiles is then the number of
+// units.
 template <int D, bool OUT_F32, bool F8, bool SPLIT = false>
 __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const void* __restrict__ K,
                                               const __bf16* __restrict__ V, void* __restrict__ Oout,
@@ -627,42 +783,21 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
   __shared__ __attribute__((aligned(1024))) char v1s[Gm::TILE];
   __shared__ __attribute__((aligned(1024))) char v2s[Gm::TILE];
 
-  int tile = remap_xcd(blockIdx.x, total_tiles), chunk = 0;
-  if (SPLIT) {
-    const int u = tile;
-    tile = sp.tile0 + u / sp.nsplit;
-    chunk = u - (u / sp.nsplit) * sp.nsplit;
-  }
-  const int kbeg = SPLIT ? chunk * sp.kc : 0;  // first key of the chunk
-  if (SPLIT) Nkv = min(sp.kc, Nkv - kbeg);
-  const int bh = tile / n_qtiles;
-  const int qt = tile - bh * n_qtiles;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15, g = lane >> 4;
-
-  // bh = b * hg + h'; the buffers hold head hoff + h' of batch b.
-  const int bb = bh / lay.hg;
-  const int hh = lay.hoff + (bh - bb * lay.hg);
-  const int64_t qhead = ((int64_t)bb * lay.htot + hh) * lay.qseg * D;
   const int64_t qsstride = (int64_t)lay.B * lay.htot * lay.qseg * D;
-  if (F8) c *= qds[bh] * kds[bh];
+
   PassCtx<D, F8> x;
-  x.Kb = static_cast<const char*>(K) + (((int64_t)bb * lay.htot + hh) * lay.kseg + kbeg) * D * QKB;
-  x.Vb = reinterpret_cast<const char*>(V + (((int64_t)bb * lay.htot + hh) * lay.kseg + kbeg) * D);
-  x.kseg = lay.kseg - kbeg;
   // segment starts are B*H*kseg rows apart; the jump is from one segment's end
   // (only key-split launches start inside a segment, and they have one)
   x.kjump = ((int64_t)lay.B * lay.htot - 1) * lay.kseg * D * QKB;
   x.vjump = ((int64_t)lay.B * lay.htot - 1) * lay.kseg * D * 2;
   x.k0 = (lds_t*)k0s; x.k1 = (lds_t*)k1s; x.k2 = (lds_t*)k2s;
   x.v0 = (lds_t*)v0s; x.v1 = (lds_t*)v1s; x.v2 = (lds_t*)v2s;
-  x.Nkv = Nkv;
-  x.ntiles = (Nkv + kBN - 1) / kBN;
   x.wave = wave;
   x.lane = lane;
   x.g = g;
-  x.c = c;
   piece_offsets<QK::ROWB, QK::PIECES>(x.kld, wave, lane, [](int r) { return QK::swz(r); });
   piece_offsets<Gm::ROWB, Gm::PIECES>(x.vld, wave, lane, [](int r) { return swz_v<D>(r); });
   // K fragment (ks): row c16 of a 16-key block (bf16: chunk 4ks + g).
@@ -691,61 +826,26 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
   }
 
   Frags<D, F8> f;
-  const int qrow0 = qt * kBM + wave * (16 * kQB) + c16;
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const int row = min(qrow0 + 16 * qb, Nq - 1);
-    const char* qrow_p =
-        static_cast<const char*>(Q) + token_offset(row, lay.qseg, qhead, qsstride, D) * QKB;
-#pragma unroll
-    for (int ks = 0; ks < QK::KS; ++ks) f.q[qb][ks] = QK::load_q(qrow_p, g, ks);
-    f.m[qb] = -INFINITY;
-    f.l[qb] = 0.f;
-    f.lb[qb] = f32x4{};
-#pragma unroll
-    for (int db = 0; db < Gm::DB; ++db) f.o[qb][db] = f32x4{};
-  }
-
-  // Second attempt only if some row's sum outgrew its reference max: then
-  // redo the tile with the exact row max (all waves decide together).
-  for (int attempt = 0;; ++attempt) {
-    const bool flag = run_pass<D, F8>(f, x);
-    if (attempt == 1 || !__syncthreads_or(flag)) break;
-    exact_max_pass<D, F8>(f, x);
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      f.l[qb] = 0.f;
-      f.lb[qb] = f32x4{};
-#pragma unroll
-      for (int db = 0; db < Gm::DB; ++db) f.o[qb][db] = f32x4{};
+  int u = blockIdx.x;
+  TileInfo ti = tile_info<D, F8, SPLIT>(u, total_tiles, n_qtiles, Nkv, lay, K, V, c, qds, kds, sp);
+  begin_tile<D, F8>(f, x, ti, Q, Nq, lay, qsstride, c16);
+  compute_tile<D, F8, false>(f, x);
+  for (;;) {
+    const int un = u + gridDim.x;
+    const bool more = un < total_tiles;
+    TileInfo tn;
+    if (more) {
+      tn = tile_info<D, F8, SPLIT>(un, total_tiles, n_qtiles, Nkv, lay, K, V, c, qds, kds, sp);
+      begin_tile<D, F8>(f, x, tn, Q, Nq, lay, qsstride, c16);
     }
-  }
-
-  // Epilogue: O = O^T / lb, LSE = (m*c + log2 l) * ln 2.
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const float l_tot = quad_sum(f.l[qb]);
-    const float inv = 1.0f / f.lb[qb][0];
-    const int qrow = qrow0 + 16 * qb;
-    if (qrow < Nq) {
-      const int64_t wrow = (int64_t)chunk * sp.rows + (int64_t)bh * Nq + qrow - sp.row0;
-      const int64_t obase =
-          SPLIT ? wrow * D : token_offset(qrow, lay.qseg, qhead, qsstride, D);
-#pragma unroll
-      for (int db = 0; db < Gm::DB; ++db) {
-        const int d0 = db * 16 + 4 * g;
-        const f32x4 val = f.o[qb][db] * inv;
-        if (OUT_F32) {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(Oout) + obase + d0) = val;
-        } else {
-          const bf16x4 b = {(__bf16)val[0], (__bf16)val[1], (__bf16)val[2], (__bf16)val[3]};
-          *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(Oout) + obase + d0) = b;
-        }
-      }
-      if (LSE && g == 0)
-        LSE[SPLIT ? wrow : (int64_t)bh * Nq + qrow] =
-            (f.m[qb] * c + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
-    }
+    // the next unit's loads stay ahead of this unit's stores
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    store_tile<D, OUT_F32, F8, SPLIT>(f, ti, Oout, LSE, Nq, lay, qsstride, sp, wave, c16, g);
+    if (!more) break;
+    u = un;
+    ti = tn;
+    compute_tile<D, F8, true>(f, x);
   }
 }
 
@@ -781,13 +881,31 @@ void attn_fwd_fp8_kernel(const unsigned char* __restrict__ Q, const unsigned cha
                                     qds, kds);
 }
 
+// Workgroups of a persistent launch over `total` units: one per compute unit
+// of the current device (the kernel holds a compute unit's LDS), or fewer
+// when there are fewer units.  The count is read once per device.
+unsigned persistent_grid(int64_t total) {
+  static int cus[64];
+  int dev = 0;
+  int n = 256;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    if (cus[dev] <= 0) {
+      int c = 0;
+      if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
+        cus[dev] = c;
+    }
+    if (cus[dev] > 0) n = cus[dev];
+  }
+  return (unsigned)(total < n ? total : n);
+}
+
 template <int D, bool OUT_F32>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float* lse, int Nq,
                     int Nkv, float c, const Layout& lay, hipStream_t stream) {
   const int n_qtiles = (Nq + kBM - 1) / kBM;
   const int64_t total = (int64_t)lay.B * lay.hg * n_qtiles;
   if (total > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OUT_F32>), dim3((unsigned)total), dim3(kThreads), 0,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OUT_F32>), dim3(persistent_grid(total)), dim3(kThreads), 0,
                      stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                      static_cast<const __bf16*>(v), o, lse, Nq, Nkv, n_qtiles, (int)total, c, lay);
   return hipGetLastError();
@@ -800,7 +918,7 @@ hipError_t launch_fp8(const void* q, const void* k, const void* v, const float* 
   const int n_qtiles = (Nq + kBM - 1) / kBM;
   const int64_t total = (int64_t)lay.B * lay.hg * n_qtiles;
   if (total > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<OUT_F32>), dim3((unsigned)total), dim3(kThreads), 0,
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<OUT_F32>), dim3(persistent_grid(total)), dim3(kThreads), 0,
                      stream, static_cast<const unsigned char*>(q),
                      static_cast<const unsigned char*>(k), static_cast<const __bf16*>(v), o, lse,
                      Nq, Nkv, n_qtiles, (int)total, c, lay, qds, kds);
@@ -840,7 +958,7 @@ hipError_t launch_attn_bf16_balanced(const void* q, const void* k, const void* v
   hipError_t e = hipSuccess;
   if (pl.whole > 0) {  // whole tiles: exact waves of the plain kernel
     auto run = [&](auto kern) {
-      hipLaunchKernelGGL(kern, dim3((unsigned)pl.whole), dim3(kThreads), 0, stream,
+      hipLaunchKernelGGL(kern, dim3(persistent_grid(pl.whole)), dim3(kThreads), 0, stream,
                          static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                          static_cast<const __bf16*>(v), o, lse, Nq, Nkv, n_qtiles, pl.whole, c,
                          lay);
@@ -860,7 +978,7 @@ hipError_t launch_attn_bf16_balanced(const void* q, const void* k, const void* v
   float* lpart = opart + (size_t)pl.nsplit * pl.rows * D;
   const Split sp{pl.whole, pl.nsplit, pl.kc, pl.row0, pl.rows};
   auto split = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3((unsigned)pl.units), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL(kern, dim3(persistent_grid(pl.units)), dim3(kThreads), 0, stream,
                        static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                        static_cast<const __bf16*>(v), opart, lpart, Nq, Nkv, n_qtiles, pl.units,
                        c, lay, sp);
