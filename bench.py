@@ -304,11 +304,14 @@ def main():
         jl = torch.empty((1, 24, 4608), device=dev, dtype=torch.float32)
         joint_ms = time_it(lambda: dta.dit_attn_fwd_joint(*jt, *ji, *tabs, workspace=jws, out=jo,
                                                           lse=jl), reps=20)
-        jattn_ms = time_it(lambda: dta.dit_attn_fwd(jws[0], jws[1], jws[2], out=jo, lse=jl), reps=20)
+        # the attention alone, on q, k, v packed (and q, k turned) by dit_rope_pack
+        jq, jk, jv = (dta.dit_rope_pack(a, b, *tb) for a, b, tb in
+                      zip(jt, ji, (tabs, tabs, [None] * 4)))
+        jattn_ms = time_it(lambda: dta.dit_attn_fwd(jq, jk, jv, out=jo, lse=jl), reps=20)
         jflops = attn_flops(1, 24, 4608, 4608, D)
         legs.update({"joint_ms": joint_ms, "joint_TFLOPs": jflops / (joint_ms * 1e-3) / 1e12,
                      "joint_attn_only_ms": jattn_ms, "joint_pack_ms": joint_ms - jattn_ms})
-        del jt, ji, jws, jo
+        del jt, ji, jws, jo, jq, jk, jv
 
         # cross leg: the 10-head share's 32768 image queries over 512 text keys
         # and values (dit_attn_fwd_block, bf16 out).

@@ -279,15 +279,20 @@ int dit_attn_fwd_joint(const void* q_txt, const void* k_txt, const void* v_txt,
   const int N = Nt + Ni;
   const int64_t elems = (int64_t)B * H * N * D;
   __bf16* ws = static_cast<__bf16*>(workspace);
-  const ditattn::RopePackTensor t[3] = {
-      {q_txt, q_img, ws, cos_txt, sin_txt, cos_img, sin_img},
+  // k is packed turned into the workspace's second slot; v is read from its
+  // parts when the text ends on a key-tile boundary, else packed into the
+  // third slot; the queries are read and turned by the attention kernel.
+  const bool v_parts = Nt % ditattn::kFwdKeyTile == 0;
+  const ditattn::RopePackTensor t[2] = {
       {k_txt, k_img, ws + elems, cos_txt, sin_txt, cos_img, sin_img},
       {v_txt, v_img, ws + 2 * elems, nullptr, nullptr, nullptr, nullptr}};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = ditattn::launch_rope_pack(t, 3, B, H, Ht, h0, Nt, Ni, D, s);
+  const hipError_t e = ditattn::launch_rope_pack(t, v_parts ? 1 : 2, B, H, Ht, h0, Nt, Ni, D, s);
   if (e != hipSuccess) return DIT_ELAUNCH;
-  return map_launch(ditattn::launch_attn_bf16(ws, ws + elems, ws + 2 * elems, o, lse, B, H, N, N,
-                                              D, scale, false, s));
+  const ditattn::JointParts parts{q_txt, q_img, v_txt, v_img, cos_txt, sin_txt, cos_img, sin_img,
+                                  Ht, h0};
+  return map_launch(ditattn::launch_attn_joint(ws + elems, v_parts ? nullptr : ws + 2 * elems, parts,
+                                               o, lse, B, H, Nt, Ni, D, scale, s));
 }
 
 int dit_quant_fp8(const void* x, void* codes, float* descale, int B, int H, int N, int D,

@@ -58,6 +58,7 @@
 #include <math.h>
 
 #include "launch.h"
+#include "rope.h"
 
 namespace ditattn {
 namespace {
@@ -222,6 +223,7 @@ __device__ __forceinline__ void tile_barrier() {
 struct TileStream {
   const char* p;
   int left;
+  int next;  // rows of each later segment
 };
 
 // Stage the stream's next tile into LDS and advance.  Each load instruction
@@ -231,8 +233,8 @@ struct TileStream {
 // the end of its segment, so rows past the end read as zero (its 32-bit size
 // is at most one tile).
 template <int ROWB, int PIECES>
-__device__ __forceinline__ void stage_next(TileStream& s, int kseg, int64_t jump, lds_t* buf,
-                                           int wave, const int* voff) {
+__device__ __forceinline__ void stage_next(TileStream& s, int64_t jump, lds_t* buf, int wave,
+                                           const int* voff) {
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)s.p, (short)0, min(s.left, kBN) * ROWB, 0x00020000);
 #pragma unroll
@@ -246,7 +248,7 @@ __device__ __forceinline__ void stage_next(TileStream& s, int kseg, int64_t jump
   s.left -= kBN;
   if (s.left == 0) {  // end of a segment: on to the next one
     s.p += jump;
-    s.left = kseg;
+    s.left = s.next;
   }
 }
 
@@ -277,7 +279,8 @@ struct PassCtx {
   using QK = QKOps<D, F8>;
   const char* Kb;    // keys / values of this (b, h): segment 0
   const char* Vb;
-  int kseg;          // keys per segment (Nkv for contiguous keys)
+  int kseg;          // keys per K segment (Nkv for contiguous keys)
+  int vfirst, vnext; // keys of the first V segment and of each later one
   int64_t kjump;     // bytes from the end of one K segment to the start of the next
   int64_t vjump;     // the same for V
   TileStream ks, vs; // the next K / V tile to stage
@@ -469,9 +472,9 @@ __device__ __forceinline__ void tile_trip(int t, Frags<D, F8>& f, f32x4 (&S0)[2]
   tile_barrier<WAITN>();  // K_{t+1}, V_t landed; every wave is done with tile t-1
   const int p2 = PH >= 0 ? PH + 2 : -1, p1 = PH >= 0 ? PH + 1 : -1;
   if (t + 2 < x.ntiles)  // K tile t+2 is the K stream's next tile
-    stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kseg, x.kjump, KSTAGE(x, p2, t + 2), x.wave, x.kld);
+    stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kjump, KSTAGE(x, p2, t + 2), x.wave, x.kld);
   if (t + 1 < x.ntiles)  // V tile t+1 is the V stream's next tile
-    stage_next<Gm::ROWB, Gm::PIECES>(x.vs, x.kseg, x.vjump, VSTAGE(x, p1, t + 1), x.wave, x.vld);
+    stage_next<Gm::ROWB, Gm::PIECES>(x.vs, x.vjump, VSTAGE(x, p1, t + 1), x.wave, x.vld);
   const lds_t* kcur = KSTAGE(x, PH, t);
   const lds_t* knext = KSTAGE(x, p1, t + 1);
   const lds_t* vcur = VSTAGE(x, PH, t);
@@ -507,11 +510,11 @@ template <int D, bool F8>
 __device__ __forceinline__ void stage_first(PassCtx<D, F8>& x) {
   using Gm = Geo<D>;
   using QK = QKOps<D, F8>;
-  x.ks = TileStream{x.Kb, x.kseg};
-  x.vs = TileStream{x.Vb, x.kseg};
-  stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kseg, x.kjump, x.k0, x.wave, x.kld);
-  if (x.ntiles > 1) stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kseg, x.kjump, x.k1, x.wave, x.kld);
-  stage_next<Gm::ROWB, Gm::PIECES>(x.vs, x.kseg, x.vjump, x.v0, x.wave, x.vld);
+  x.ks = TileStream{x.Kb, x.kseg, x.kseg};
+  x.vs = TileStream{x.Vb, x.vfirst, x.vnext};
+  stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kjump, x.k0, x.wave, x.kld);
+  if (x.ntiles > 1) stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kjump, x.k1, x.wave, x.kld);
+  stage_next<Gm::ROWB, Gm::PIECES>(x.vs, x.vjump, x.v0, x.wave, x.vld);
 }
 
 // One full pass over the keys whose first tiles stage_first has issued: the
@@ -576,10 +579,10 @@ __device__ __forceinline__ void exact_max_pass(Frags<D, F8>& f, PassCtx<D, F8>& 
   float m[kQB];
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) m[qb] = -INFINITY;
-  x.ks = TileStream{x.Kb, x.kseg};
+  x.ks = TileStream{x.Kb, x.kseg, x.kseg};
   for (int t = 0; t < x.ntiles; ++t) {
     __syncthreads();  // every wave is done reading the stage
-    stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kseg, x.kjump, x.k0, x.wave, x.kld);
+    stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kjump, x.k0, x.wave, x.kld);
     tile_barrier();  // landed
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -628,20 +631,45 @@ struct Split {
   int64_t row0, rows;
 };
 
+// Joint text + image attention ("Parallelism Acceleration Guide", vLLM-Omni
+// docs, "How to parallelize a new model"): the joint sequence is the Nt text
+// tokens of head h0 + h of [B,Ht,Nt,D] tensors, then the Ni image tokens of
+// head h of [B,H,Ni,D] tensors.  Queries are read from their parts and
+// turned by the part's rotary tables ([N, D/2] float32 cosines and sines; a
+// part without tables is not turned); V is read from its parts when v_txt /
+// v_img are given (Nt a multiple of the key tile), else from the packed V;
+// K always comes packed (turned).
+struct JointArgs {
+  const __bf16* q_txt;
+  const __bf16* q_img;
+  const __bf16* v_txt;
+  const __bf16* v_img;
+  const float* cos_txt;
+  const float* sin_txt;
+  const float* cos_img;
+  const float* sin_img;
+  int Nt, Ni, Ht, h0;
+};
+
 // Where one work unit's rows and keys are: the unit's head (bh), query tile
 // (qt), key chunk (SPLIT), its key count and the pointers of its K and V.
 struct TileInfo {
   int bh, qt, chunk, Nkv, kseg;
-  int64_t qhead;  // element offset of the head's segment 0 in Q and O
+  int vfirst, vnext;    // V stream: rows of its first segment and of each later one
+  int64_t vjump;        // bytes from the end of one V segment to the start of the next
+  int64_t qhead;        // element offset of the head's segment 0 in Q and O
   const char* Kb;
   const char* Vb;
-  float c;        // softmax constant (F8: times the head's descales)
+  const __bf16* qtxt;   // JOINT: the head's text and image queries
+  const __bf16* qimg;
+  float c;              // softmax constant (F8: times the head's descales)
 };
 
-template <int D, bool F8, bool SPLIT>
+template <int D, bool F8, bool SPLIT, bool JOINT>
 __device__ __forceinline__ TileInfo tile_info(int u, int total, int n_qtiles, int Nkv, const Layout& lay,
                                               const void* K, const __bf16* V, float c,
-                                              const float* qds, const float* kds, const Split& sp) {
+                                              const float* qds, const float* kds, const Split& sp,
+                                              const JointArgs& ja) {
   constexpr int QKB = F8 ? 1 : 2;  // bytes per q / k element
   TileInfo ti;
   int tile = remap_xcd(u, total);
@@ -662,21 +690,52 @@ __device__ __forceinline__ TileInfo tile_info(int u, int total, int n_qtiles, in
   ti.Kb = static_cast<const char*>(K) + (((int64_t)bb * lay.htot + hh) * lay.kseg + kbeg) * D * QKB;
   ti.Vb = reinterpret_cast<const char*>(V + (((int64_t)bb * lay.htot + hh) * lay.kseg + kbeg) * D);
   ti.kseg = lay.kseg - kbeg;
+  ti.vfirst = ti.kseg;
+  ti.vnext = ti.kseg;
+  // segment starts are B*H*kseg rows apart; the jump is from one segment's end
+  // (only key-split launches start inside a segment, and they have one)
+  ti.vjump = ((int64_t)lay.B * lay.htot - 1) * lay.kseg * D * 2;
   ti.c = F8 ? c * qds[ti.bh] * kds[ti.bh] : c;
+  ti.qtxt = ti.qimg = nullptr;
+  if (JOINT) {  // contiguous layout: bh = b * H + h, head h of the image, h0 + h of the text
+    const int64_t th = (int64_t)bb * ja.Ht + ja.h0 + hh, ih = (int64_t)bb * lay.htot + hh;
+    ti.qtxt = ja.Nt ? ja.q_txt + th * ja.Nt * D : nullptr;
+    ti.qimg = ja.Ni ? ja.q_img + ih * ja.Ni * D : nullptr;
+    if (ja.v_txt || ja.v_img) {  // V read from its two parts: the text rows, then the image rows
+      const char* vt = ja.Nt ? reinterpret_cast<const char*>(ja.v_txt + th * ja.Nt * D) : nullptr;
+      const char* vi = ja.Ni ? reinterpret_cast<const char*>(ja.v_img + ih * ja.Ni * D) : nullptr;
+      if (ja.Nt) {
+        ti.Vb = vt;
+        ti.vfirst = ja.Nt;
+        ti.vnext = ja.Ni;
+        ti.vjump = vi ? (int64_t)((uintptr_t)vi - (uintptr_t)vt) - (int64_t)ja.Nt * D * 2 : 0;
+      } else {
+        ti.Vb = vi;
+        ti.vfirst = ti.vnext = ja.Ni;
+        ti.vjump = 0;
+      }
+    }
+  }
   return ti;
 }
 
 // Point the pass at a unit, issue its first K / V tiles and load its queries
-// (rows past Nq load row Nq - 1).
-template <int D, bool F8>
+// (rows past Nq load row Nq - 1).  JOINT: a query is a text or an image token
+// of the joint sequence (text first), turned by its part's rotary table when
+// the part has one; the fragment of k-step ks holds channel pairs
+// 16 ks + 4 g .. +3 of the lane's token, one per 32-bit word.
+template <int D, bool F8, bool JOINT>
 __device__ __forceinline__ void begin_tile(Frags<D, F8>& f, PassCtx<D, F8>& x, const TileInfo& ti,
                                            const void* Q, int Nq, const Layout& lay,
-                                           int64_t qsstride, int c16) {
+                                           int64_t qsstride, int c16, const JointArgs& ja) {
   using QK = QKOps<D, F8>;
   constexpr int QKB = F8 ? 1 : 2;
   x.Kb = ti.Kb;
   x.Vb = ti.Vb;
   x.kseg = ti.kseg;
+  x.vfirst = ti.vfirst;
+  x.vnext = ti.vnext;
+  x.vjump = ti.vjump;
   x.Nkv = ti.Nkv;
   x.ntiles = (ti.Nkv + kBN - 1) / kBN;
   x.c = ti.c;
@@ -685,10 +744,30 @@ __device__ __forceinline__ void begin_tile(Frags<D, F8>& f, PassCtx<D, F8>& x, c
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     const int row = min(qrow0 + 16 * qb, Nq - 1);
-    const char* qrow_p =
-        static_cast<const char*>(Q) + token_offset(row, lay.qseg, ti.qhead, qsstride, D) * QKB;
+    if constexpr (JOINT && !F8) {
+      const bool txt = row < ja.Nt;
+      const int m = txt ? row : row - ja.Nt;
+      const __bf16* src = (txt ? ti.qtxt : ti.qimg) + (int64_t)m * D;
+      const float* ct = txt ? ja.cos_txt : ja.cos_img;
+      const float* st = txt ? ja.sin_txt : ja.sin_img;
 #pragma unroll
-    for (int ks = 0; ks < QK::KS; ++ks) f.q[qb][ks] = QK::load_q(qrow_p, x.g, ks);
+      for (int ks = 0; ks < QK::KS; ++ks) {
+        u32x4 w = *reinterpret_cast<const u32x4*>(src + ks * 32 + x.g * 8);
+        if (ct) {
+          const int pr = (int64_t)m * (D / 2) + 16 * ks + 4 * x.g;
+          const f32x4 cv = *reinterpret_cast<const f32x4*>(ct + pr);
+          const f32x4 sv = *reinterpret_cast<const f32x4*>(st + pr);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w[j] = rope_turn_pair(w[j], cv[j], sv[j]);
+        }
+        f.q[qb][ks] = __builtin_bit_cast(bf16x8, w);
+      }
+    } else {
+      const char* qrow_p =
+          static_cast<const char*>(Q) + token_offset(row, lay.qseg, ti.qhead, qsstride, D) * QKB;
+#pragma unroll
+      for (int ks = 0; ks < QK::KS; ++ks) f.q[qb][ks] = QK::load_q(qrow_p, x.g, ks);
+    }
   }
 }
 
@@ -766,13 +845,14 @@ __device__ __forceinline__ void store_tile(const Frags<D, F8>& f, const TileInfo
 // per-(b, h) factors qds[bh] * kds[bh]; else q and k are bf16 and qds, kds
 // are unused.  SPLIT: a key-split launch, total_tiles is then the number of
 // units.
-template <int D, bool OUT_F32, bool F8, bool SPLIT = false>
+template <int D, bool OUT_F32, bool F8, bool SPLIT = false, bool JOINT = false>
 __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const void* __restrict__ K,
                                               const __bf16* __restrict__ V, void* __restrict__ Oout,
                                               float* __restrict__ LSE, int Nq, int Nkv,
                                               int n_qtiles, int total_tiles, float c, Layout lay,
                                               const float* __restrict__ qds,
-                                              const float* __restrict__ kds, Split sp = {}) {
+                                              const float* __restrict__ kds, Split sp = {},
+                                              JointArgs ja = {}) {
   using Gm = Geo<D>;
   using QK = QKOps<D, F8>;
   constexpr int QKB = F8 ? 1 : 2;  // bytes per q / k element
@@ -792,7 +872,6 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
   // segment starts are B*H*kseg rows apart; the jump is from one segment's end
   // (only key-split launches start inside a segment, and they have one)
   x.kjump = ((int64_t)lay.B * lay.htot - 1) * lay.kseg * D * QKB;
-  x.vjump = ((int64_t)lay.B * lay.htot - 1) * lay.kseg * D * 2;
   x.k0 = (lds_t*)k0s; x.k1 = (lds_t*)k1s; x.k2 = (lds_t*)k2s;
   x.v0 = (lds_t*)v0s; x.v1 = (lds_t*)v1s; x.v2 = (lds_t*)v2s;
   x.wave = wave;
@@ -827,16 +906,18 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
 
   Frags<D, F8> f;
   int u = blockIdx.x;
-  TileInfo ti = tile_info<D, F8, SPLIT>(u, total_tiles, n_qtiles, Nkv, lay, K, V, c, qds, kds, sp);
-  begin_tile<D, F8>(f, x, ti, Q, Nq, lay, qsstride, c16);
+  TileInfo ti =
+      tile_info<D, F8, SPLIT, JOINT>(u, total_tiles, n_qtiles, Nkv, lay, K, V, c, qds, kds, sp, ja);
+  begin_tile<D, F8, JOINT>(f, x, ti, Q, Nq, lay, qsstride, c16, ja);
   compute_tile<D, F8, false>(f, x);
   for (;;) {
     const int un = u + gridDim.x;
     const bool more = un < total_tiles;
     TileInfo tn;
     if (more) {
-      tn = tile_info<D, F8, SPLIT>(un, total_tiles, n_qtiles, Nkv, lay, K, V, c, qds, kds, sp);
-      begin_tile<D, F8>(f, x, tn, Q, Nq, lay, qsstride, c16);
+      tn = tile_info<D, F8, SPLIT, JOINT>(un, total_tiles, n_qtiles, Nkv, lay, K, V, c, qds, kds,
+                                          sp, ja);
+      begin_tile<D, F8, JOINT>(f, x, tn, Q, Nq, lay, qsstride, c16, ja);
     }
     // the next unit's loads stay ahead of this unit's stores
     asm volatile("" ::: "memory");
@@ -879,6 +960,17 @@ void attn_fwd_fp8_kernel(const unsigned char* __restrict__ Q, const unsigned cha
                          const float* __restrict__ kds) {
   attn_fwd_body<128, OUT_F32, true>(Q, K, V, Oout, LSE, Nq, Nkv, n_qtiles, total_tiles, c, lay,
                                     qds, kds);
+}
+
+// Joint text + image attention (JointArgs): K packed and turned in
+// [B,H,Nt+Ni,D], V packed there too or read from its parts.
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
+void attn_fwd_joint_kernel(const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+                           __bf16* __restrict__ Oout, float* __restrict__ LSE, int N, int n_qtiles,
+                           int total_tiles, float c, Layout lay, JointArgs ja) {
+  attn_fwd_body<D, false, false, false, true>(nullptr, K, V, Oout, LSE, N, N, n_qtiles, total_tiles,
+                                              c, lay, nullptr, nullptr, Split{}, ja);
 }
 
 // Workgroups of a persistent launch over `total` units: one per compute unit
@@ -990,6 +1082,33 @@ hipError_t launch_attn_bf16_balanced(const void* q, const void* k, const void* v
   char* otail = static_cast<char*>(o) + pl.row0 * D * (o_f32 ? 4 : 2);
   return launch_merge(opart, lpart, pl.nsplit, otail, lse ? lse + pl.row0 : nullptr, pl.rows, D,
                       o_f32, stream);
+}
+
+hipError_t launch_attn_joint(const void* k_packed, const void* v_packed, const JointParts& parts,
+                             void* o, float* lse, int B, int H, int Nt, int Ni, int D, float scale,
+                             hipStream_t stream) {
+  const int N = Nt + Ni;
+  const Layout lay{N, N, H, H, 0, B};
+  const float c = scale * 1.4426950408889634f;
+  const int n_qtiles = (N + kBM - 1) / kBM;
+  const int64_t total = (int64_t)B * H * n_qtiles;
+  if (total > 0x7fffffff) return hipErrorInvalidValue;
+  JointArgs ja{static_cast<const __bf16*>(parts.q_txt), static_cast<const __bf16*>(parts.q_img),
+               v_packed ? nullptr : static_cast<const __bf16*>(parts.v_txt),
+               v_packed ? nullptr : static_cast<const __bf16*>(parts.v_img),
+               parts.cos_txt, parts.sin_txt, parts.cos_img, parts.sin_img, Nt, Ni, parts.Ht,
+               parts.h0};
+  auto run = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(persistent_grid(total)), dim3(kThreads), 0, stream,
+                       static_cast<const __bf16*>(k_packed), static_cast<const __bf16*>(v_packed),
+                       static_cast<__bf16*>(o), lse, N, n_qtiles, (int)total, c, lay, ja);
+  };
+  switch (D) {
+    case 32: run(attn_fwd_joint_kernel<32>); break;
+    case 64: run(attn_fwd_joint_kernel<64>); break;
+    default: run(attn_fwd_joint_kernel<128>); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_fp8(const void* q, const void* k, const void* v, const float* q_descale,

@@ -78,6 +78,25 @@ struct RopePackTensor {
   const float* sin_img;
 };
 
+// Joint text + image attention reading the queries (turned in the kernel)
+// and, unless v_packed is given, the values from their parts; K comes packed
+// and turned in [B,H,Nt+Ni,D] (v_packed likewise).  Two-part V needs Nt a
+// multiple of kFwdKeyTile.
+struct JointParts {
+  const void* q_txt;  // [B,Ht,Nt,D], heads h0 .. h0+H-1 used
+  const void* q_img;  // [B,H,Ni,D]
+  const void* v_txt;
+  const void* v_img;
+  const float* cos_txt;
+  const float* sin_txt;
+  const float* cos_img;
+  const float* sin_img;
+  int Ht, h0;
+};
+hipError_t launch_attn_joint(const void* k_packed, const void* v_packed, const JointParts& parts,
+                             void* o, float* lse, int B, int H, int Nt, int Ni, int D, float scale,
+                             hipStream_t stream);
+
 // Packs 1 to 3 tensors in one launch.
 hipError_t launch_rope_pack(const RopePackTensor* tensors, int ntensors, int B, int H, int Ht,
                             int h0, int Nt, int Ni, int D, hipStream_t stream);

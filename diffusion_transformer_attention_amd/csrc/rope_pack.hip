@@ -17,6 +17,7 @@
 // sines, which the heads of a launch share through L2.  One launch packs up
 // to three tensors (q, k, v): blockIdx.y picks the tensor.
 #include "launch.h"
+#include "rope.h"
 
 namespace ditattn {
 namespace {
@@ -30,21 +31,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 struct PackSet {
   RopePackTensor t[3];
 };
-
-__device__ __forceinline__ float lo_f(unsigned w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi_f(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ unsigned pack2(float a, float b) {
-  const __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (unsigned)__builtin_bit_cast(unsigned short, x) |
-         ((unsigned)__builtin_bit_cast(unsigned short, y) << 16);
-}
-
-// One 32-bit word holds the pair (x[2i], x[2i+1]) in its low and high halves.
-__device__ __forceinline__ unsigned turn_pair(unsigned w, float c, float s) {
-  const float x0 = lo_f(w), x1 = hi_f(w);
-  return pack2(fmaf(x0, c, -(x1 * s)), fmaf(x0, s, x1 * c));
-}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void rope_pack_kernel(PackSet set, int H, int Ht, int h0,
@@ -75,7 +61,7 @@ __global__ __launch_bounds__(kThreads) void rope_pack_kernel(PackSet set, int H,
       const f32x4 cv = *reinterpret_cast<const f32x4*>(ct + (int64_t)m * (D / 2) + 4 * c);
       const f32x4 sv = *reinterpret_cast<const f32x4*>(st + (int64_t)m * (D / 2) + 4 * c);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) y[p] = turn_pair(x[p], cv[p], sv[p]);
+      for (int p = 0; p < 4; ++p) y[p] = rope_turn_pair(x[p], cv[p], sv[p]);
     }
     *reinterpret_cast<u32x4*>(out + ((int64_t)n * D + 8 * c)) = y;
   }

@@ -273,15 +273,19 @@ int dit_rope_pack(const void* x_txt, const void* x_img, const float* cos_txt,
 
 /*
  * Joint attention ([VO]): every text and image query attends over every text
- * and image key, with the rotary embedding on queries and keys (not values):
- * dit_rope_pack of q and k (with the tables) and of v (without), then
- * dit_attn_fwd over the N = Nt + Ni joint tokens.
+ * and image key, with the rotary embedding on queries and keys (not values).
+ * The result is, bit for bit, dit_rope_pack of q and k (with the tables) and
+ * of v (without), then dit_attn_fwd over the N = Nt + Ni joint tokens; the
+ * call itself packs only k (turned), and v too when Nt is not a multiple of
+ * 64, while the attention kernel turns the queries as it loads them and
+ * reads v from its two parts.
  *
  *   q_txt, k_txt, v_txt : bf16 [B,Ht,Nt,D] (heads h0 .. h0+H-1 used)
  *   q_img, k_img, v_img : bf16 [B,H,Ni,D]
  *   tables              : as in dit_rope_pack
  *   workspace           : bf16 [3][B,H,N,D] scratch owned by the caller (the
- *                         packed q, k, v; overwritten)
+ *                         second slot receives the packed k, the third the
+ *                         packed v when Nt % 64 != 0; overwritten)
  *   o                   : bf16 [B,H,N,D], text rows first
  *   lse                 : float32 [B,H,N], or NULL to skip
  * Cross attention (image queries over text keys only) needs no packing: it

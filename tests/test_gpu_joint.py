@@ -130,12 +130,22 @@ def test_joint_small(B, H, Ht, h0, Nt, Ni, D, tt, it):
     _check_joint(to_f64(O), to_f64(L), [f64(x)[:, h0:h0 + H] for x in txt], img, tabs)
 
 
-def test_joint_equals_pack_then_attention():
-    say("joint == rope_pack x3 + dit_attn_fwd")
-    txt, img, tabs = _case(1, 3, 3, 50, 400, 128, seed=21)
-    O, L = _joint_gpu(txt, img, tabs, scale=0.1)
+@pytest.mark.parametrize("H,Ht,h0,Nt,Ni,D,tt", [
+    (3, 3, 0, 50, 400, 128, True),     # text not on a 64-key boundary: v packed too
+    (3, 3, 0, 128, 400, 128, True),    # v read from its two parts
+    (2, 6, 2, 64, 300, 64, False),     # head group of a replicated text, text unturned
+    (2, 2, 0, 0, 300, 32, True),       # image only
+    (2, 4, 1, 192, 0, 128, True),      # text only
+])
+def test_joint_equals_pack_then_attention(H, Ht, h0, Nt, Ni, D, tt):
+    """The joint call (queries turned in the attention kernel, v read from its
+    parts when Nt % 64 == 0) gives the bits of packing q, k, v with
+    dit_rope_pack and running dit_attn_fwd on the joint sequence."""
+    say("joint == rope_pack x3 + dit_attn_fwd", H, Ht, h0, Nt, Ni, D, tt)
+    txt, img, tabs = _case(1, H, Ht, Nt, Ni, D, seed=21 + Nt, text_tables=tt)
+    O, L = _joint_gpu(txt, img, tabs, h0=h0, scale=0.1)
     dt = _dev_tables(tabs)
-    q, k, v = (dta.dit_rope_pack(bits_to_torch_bf16(a), bits_to_torch_bf16(b), *tb)
+    q, k, v = (dta.dit_rope_pack(bits_to_torch_bf16(a), bits_to_torch_bf16(b), *tb, h0=h0)
                for a, b, tb in zip(txt, img, (dt, dt, [None] * 4)))
     O2, L2 = dta.dit_attn_fwd(q, k, v, scale=0.1)
     assert torch.equal(O, O2) and torch.equal(L, L2)
