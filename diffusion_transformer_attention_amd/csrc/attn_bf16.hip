@@ -80,7 +80,7 @@ typedef __attribute__((address_space(3))) const u32x4 lds_cu32x4;
 
 constexpr int kWaves = 8;               // two waves per SIMD
 constexpr int kThreads = 64 * kWaves;
-constexpr int kQB = 2;                  // 16-row query blocks per wave
+constexpr int kQB = 2;                  // 16-row query blocks per wave (1: half-height tiles)
 constexpr int kBM = 16 * kQB * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;                 // keys per LDS tile (two 32-key slots)
 static_assert(kBM == kFwdQueryTile && kBN == kFwdKeyTile, "launch.h tile sizes");
@@ -264,13 +264,13 @@ __device__ __forceinline__ void piece_offsets(int* voff, int wave, int lane, Swz
   }
 }
 
-template <int D, bool F8>
+template <int D, bool F8, int QB = kQB>
 struct Frags {
   using QK = QKOps<D, F8>;
-  f32x4 o[kQB][Geo<D>::DB];           // O^T blocks: lane holds channels 16db+4g+r of its query
-  typename QK::Frag q[kQB][QK::KS];   // Q^T operand of the lane's query (bf16: channels 32ks+8g..+7)
-  float m[kQB], l[kQB];
-  f32x4 lb[kQB];                      // sum of the bf16 p: an all-ones V^T block, every row alike
+  f32x4 o[QB][Geo<D>::DB];           // O^T blocks: lane holds channels 16db+4g+r of its query
+  typename QK::Frag q[QB][QK::KS];   // Q^T operand of the lane's query (bf16: channels 32ks+8g..+7)
+  float m[QB], l[QB];
+  f32x4 lb[QB];                      // sum of the bf16 p: an all-ones V^T block, every row alike
 };
 
 // Everything one pass over the keys needs.
@@ -311,31 +311,31 @@ __device__ __forceinline__ lds_t* stage_of(lds_t* s0, lds_t* s1, lds_t* s2, int 
 
 // S^T of one 32-key step (rows [0, 32) at kst): S[kb][qb] holds keys
 // 16kb + 4g + r for the lane's query of block qb.
-template <int D, bool F8>
-__device__ __forceinline__ void qk_step(f32x4 (&S)[2][kQB], const lds_t* kst,
-                                        const PassCtx<D, F8>& x, const Frags<D, F8>& f) {
+template <int D, bool F8, int QB>
+__device__ __forceinline__ void qk_step(f32x4 (&S)[2][QB], const lds_t* kst,
+                                        const PassCtx<D, F8>& x, const Frags<D, F8, QB>& f) {
   using QK = QKOps<D, F8>;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) S[kb][qb] = f32x4{};
+    for (int qb = 0; qb < QB; ++qb) S[kb][qb] = f32x4{};
 #pragma unroll
   for (int ks = 0; ks < QK::KS; ++ks)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const typename QK::Frag a = QK::load(kst - x.kbase + kb * 16 * QK::ROWB, x.kof[ks]);
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) S[kb][qb] = QK::mma(a, f.q[qb][ks], S[kb][qb]);
+      for (int qb = 0; qb < QB; ++qb) S[kb][qb] = QK::mma(a, f.q[qb][ks], S[kb][qb]);
     }
 }
 
 // Row max of one 32-key step (reference max / exact-max pass); keys >= Nkv
 // excluded when MASK.
-template <bool MASK>
-__device__ __forceinline__ void rowmax_step(const f32x4 (&S)[2][kQB], float (&m)[kQB], int key0,
+template <bool MASK, int QB>
+__device__ __forceinline__ void rowmax_step(const f32x4 (&S)[2][QB], float (&m)[QB], int key0,
                                             int Nkv, int g) {
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -351,24 +351,24 @@ __device__ __forceinline__ void rowmax_step(const f32x4 (&S)[2][kQB], float (&m)
 // One 32-key slot: QK^T of the next step into Sn (K rows at k_next), PV of
 // the previous step from Pp (V rows at v_prev), softmax of this step from Sc
 // into Pc.  Laid out as 16 groups fenced by sched_barrier(0): group g runs
-// the QK^T MFMAs [g NQK/16, (g+1) NQK/16) (index i: ks = i / 2kQB, kb =
-// (i / kQB) % 2, qb = i % kQB), the PV MFMAs [g NPV/16, (g+1) NPV/16)
-// (index j: db = j / kQB, qb = j % kQB) and the softmax scores
+// the QK^T MFMAs [g NQK/16, (g+1) NQK/16) (index i: ks = i / 2QB, kb =
+// (i / QB) % 2, qb = i % QB), the PV MFMAs [g NPV/16, (g+1) NPV/16)
+// (index j: db = j / QB, qb = j % QB) and the softmax scores
 // [g NS/16, (g+1) NS/16) (index e: qb = e / 8, kb = (e / 4) % 2, r = e % 4),
 // and issues the LDS reads of the fragments first needed LA groups later.
 // The P^T operand of block qb packs the keys 4g + r (kb 0) and 16 + 4g + r
 // (kb 1): MFMA k index 8g + j <-> key 4g + j (j < 4), 16 + 4g + j - 4 (j >= 4).
-template <int D, bool F8, bool MASK>
-__device__ __forceinline__ void slot(Frags<D, F8>& f, const f32x4 (&Sc)[2][kQB], f32x4 (&Sn)[2][kQB],
-                                     const bf16x8 (&Pp)[kQB], bf16x8 (&Pc)[kQB],
+template <int D, bool F8, bool MASK, int QB>
+__device__ __forceinline__ void slot(Frags<D, F8, QB>& f, const f32x4 (&Sc)[2][QB], f32x4 (&Sn)[2][QB],
+                                     const bf16x8 (&Pp)[QB], bf16x8 (&Pc)[QB],
                                      const lds_t* k_next, const lds_t* v_prev,
                                      const PassCtx<D, F8>& x, int key0) {
   using Gm = Geo<D>;
   using QK = QKOps<D, F8>;
   constexpr int NG = 16;                       // groups
-  constexpr int NQK = 2 * kQB * QK::KS;        // QK^T MFMAs
-  constexpr int NPV = kQB * Gm::DB;            // PV MFMAs
-  constexpr int NS = 8 * kQB;                  // softmax scores per lane
+  constexpr int NQK = 2 * QB * QK::KS;        // QK^T MFMAs
+  constexpr int NPV = QB * Gm::DB;            // PV MFMAs
+  constexpr int NS = 8 * QB;                  // softmax scores per lane
   constexpr int NKF = 2 * QK::KS;              // K fragments (ks, kb), ks-major
   constexpr int NVF = Gm::DB;                  // V^T fragments (db)
   constexpr int LA = 1;                        // read lookahead, in groups
@@ -385,8 +385,8 @@ __device__ __forceinline__ void slot(Frags<D, F8>& f, const f32x4 (&Sc)[2][kQB],
     vf[i] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
   // first group that uses K fragment f / V^T fragment f
-  auto kfirst = [](int fi) { return fi * kQB * NG / NQK; };
-  auto vfirst = [](int fi) { return fi * kQB * NG / NPV; };
+  auto kfirst = [](int fi) { return fi * QB * NG / NQK; };
+  auto vfirst = [](int fi) { return fi * QB * NG / NPV; };
 #pragma unroll
   for (int fi = 0; fi < NKF; ++fi)
     if (kfirst(fi) < LA) load_k(fi);
@@ -395,16 +395,16 @@ __device__ __forceinline__ void slot(Frags<D, F8>& f, const f32x4 (&Sc)[2][kQB],
     if (vfirst(fi) < LA) load_v(fi);
   const bf16x8 ones8 = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
                         (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
-  float l[kQB], mc[kQB], p[kQB][8];
+  float l[QB], mc[QB], p[QB][8];
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     l[qb] = f.l[qb];
     mc[qb] = f.m[qb] * x.c;
   }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) Sn[kb][qb] = f32x4{};
+    for (int qb = 0; qb < QB; ++qb) Sn[kb][qb] = f32x4{};
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
@@ -416,19 +416,19 @@ __device__ __forceinline__ void slot(Frags<D, F8>& f, const f32x4 (&Sc)[2][kQB],
       if (vfirst(fi) >= LA && vfirst(fi) == g + LA) load_v(fi);
 #pragma unroll
     for (int i = g * NQK / NG; i < (g + 1) * NQK / NG; ++i) {
-      const int ks = i / (2 * kQB), kb = (i / kQB) % 2, qb = i % kQB;
+      const int ks = i / (2 * QB), kb = (i / QB) % 2, qb = i % QB;
       Sn[kb][qb] = QK::mma(kf[ks * 2 + kb], f.q[qb][ks], Sn[kb][qb]);
     }
 #pragma unroll
     for (int j = g * NPV / NG; j < (g + 1) * NPV / NG; ++j) {
-      const int db = j / kQB, qb = j % kQB;
+      const int db = j / QB, qb = j % QB;
       f.o[qb][db] = mfma16(vf[db], Pp[qb], f.o[qb][db]);
     }
     // The row sums of the bf16 P^T the PV product multiplies, on the matrix
     // cores: an all-ones V^T block, one MFMA per query block.
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb)
-      if (g == NG - 1 - (NG / kQB) * qb) f.lb[qb] = mfma16(ones8, Pp[qb], f.lb[qb]);
+    for (int qb = 0; qb < QB; ++qb)
+      if (g == NG - 1 - (NG / QB) * qb) f.lb[qb] = mfma16(ones8, Pp[qb], f.lb[qb]);
 #pragma unroll
     for (int e = g * NS / NG; e < (g + 1) * NS / NG; ++e) {
       const int qb = e / 8, kb = (e / 4) % 2, r = e % 4;
@@ -452,7 +452,7 @@ __device__ __forceinline__ void slot(Frags<D, F8>& f, const f32x4 (&Sc)[2][kQB],
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     f.l[qb] = l[qb];
   }
 }
@@ -463,9 +463,9 @@ __device__ __forceinline__ void slot(Frags<D, F8>& f, const f32x4 (&Sc)[2][kQB],
 // On entry S0 holds S^T of step 2t and Pa holds P of step 2t-1; on exit S0
 // holds S^T of step 2t+2 (garbage past the last tile, never used) and Pa
 // holds P of step 2t+1.
-template <int D, bool F8, int PH, bool MASK, int WAITN = 0>
-__device__ __forceinline__ void tile_trip(int t, Frags<D, F8>& f, f32x4 (&S0)[2][kQB], f32x4 (&S1)[2][kQB],
-                                          bf16x8 (&Pa)[kQB], bf16x8 (&Pb)[kQB],
+template <int D, bool F8, int PH, bool MASK, int WAITN = 0, int QB>
+__device__ __forceinline__ void tile_trip(int t, Frags<D, F8, QB>& f, f32x4 (&S0)[2][QB], f32x4 (&S1)[2][QB],
+                                          bf16x8 (&Pa)[QB], bf16x8 (&Pb)[QB],
                                           PassCtx<D, F8>& x) {
   using Gm = Geo<D>;
   using QK = QKOps<D, F8>;
@@ -485,8 +485,8 @@ __device__ __forceinline__ void tile_trip(int t, Frags<D, F8>& f, f32x4 (&S0)[2]
 }
 
 // O^T += V^T P^T for one 32-key step (used once, after the loop).
-template <int D, bool F8>
-__device__ __forceinline__ void pv_step(Frags<D, F8>& f, const bf16x8 (&P)[kQB], const lds_t* vst,
+template <int D, bool F8, int QB>
+__device__ __forceinline__ void pv_step(Frags<D, F8, QB>& f, const bf16x8 (&P)[QB], const lds_t* vst,
                                         const PassCtx<D, F8>& x) {
   using Gm = Geo<D>;
 #pragma unroll
@@ -497,12 +497,12 @@ __device__ __forceinline__ void pv_step(Frags<D, F8>& f, const bf16x8 (&P)[kQB],
         bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 16 * Gm::ROWB)));
     const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) f.o[qb][db] = mfma16(a, P[qb], f.o[qb][db]);
+    for (int qb = 0; qb < QB; ++qb) f.o[qb][db] = mfma16(a, P[qb], f.o[qb][db]);
   }
   const bf16x8 ones8 = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
                         (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) f.lb[qb] = mfma16(ones8, P[qb], f.lb[qb]);
+  for (int qb = 0; qb < QB; ++qb) f.lb[qb] = mfma16(ones8, P[qb], f.lb[qb]);
 }
 
 // Stage the first K tiles (0 and 1) and V tile 0 of a pass.
@@ -523,31 +523,30 @@ __device__ __forceinline__ void stage_first(PassCtx<D, F8>& x) {
 // row's sum outgrew its reference.  PF: the first tiles were issued before
 // the previous tile's NST output stores, so the first two waits leave those
 // stores in flight.
-template <int D, bool F8, bool PF>
-__device__ __forceinline__ bool run_pass_body(Frags<D, F8>& f, PassCtx<D, F8>& x) {
+template <int D, bool F8, bool PF, int QB>
+__device__ __forceinline__ bool run_pass_body(Frags<D, F8, QB>& f, PassCtx<D, F8>& x) {
   using Gm = Geo<D>;
-  using QK = QKOps<D, F8>;
-  constexpr int NST = PF ? kQB * Gm::DB : 0;  // output store instructions per wave
+  constexpr int NST = PF ? QB * Gm::DB : 0;  // output store instructions per wave
   // The first slot multiplies P = 0 by the V stage of tile -1 (stage 2): zero
   // it so no stale Inf/NaN bit pattern can turn 0 * V into NaN.
   for (int i = threadIdx.x; i < Gm::TILE / 16; i += kThreads)
     reinterpret_cast<lds_u32x4*>(x.v2)[i] = u32x4{0u, 0u, 0u, 0u};
-  f32x4 S0[2][kQB], S1[2][kQB];
-  bf16x8 Pa[kQB], Pb[kQB];
+  f32x4 S0[2][QB], S1[2][QB];
+  bf16x8 Pa[QB], Pb[QB];
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) Pa[qb] = bf16x8{};
+  for (int qb = 0; qb < QB; ++qb) Pa[qb] = bf16x8{};
   tile_barrier<NST>();  // K tile 0 (and K 1, V 0) landed
   qk_step<D, F8>(S0, x.k0, x, f);
   if (f.m[0] == -INFINITY) {  // first attempt: reference max = max of step 0
-    float m[kQB];
+    float m[QB];
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) m[qb] = -INFINITY;
+    for (int qb = 0; qb < QB; ++qb) m[qb] = -INFINITY;
     if (x.Nkv < 32)
       rowmax_step<true>(S0, m, 0, x.Nkv, x.g);
     else
       rowmax_step<false>(S0, m, 0, x.Nkv, x.g);
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) f.m[qb] = m[qb];
+    for (int qb = 0; qb < QB; ++qb) f.m[qb] = m[qb];
   }
   const bool partial = (x.Nkv % kBN) != 0;
   const int nfull = partial ? x.ntiles - 1 : x.ntiles;
@@ -568,17 +567,20 @@ __device__ __forceinline__ bool run_pass_body(Frags<D, F8>& f, PassCtx<D, F8>& x
   pv_step<D, F8>(f, Pa, VSTAGE(x, -1, x.ntiles - 1) + 32 * Gm::ROWB, x);
   bool flag = false;
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) flag |= !(quad_sum(f.l[qb]) < kMaxSum);
+  for (int qb = 0; qb < QB; ++qb) flag |= !(quad_sum(f.l[qb]) < kMaxSum);
   return flag;
 }
 
-// Exact row max over all keys (only when the fixed-reference loop flagged).
-template <int D, bool F8>
-__device__ __forceinline__ void exact_max_pass(Frags<D, F8>& f, PassCtx<D, F8>& x) {
+// Exact row max over all keys, taken as the reference of the rows whose sum
+// outgrew theirs (only when the fixed-reference loop flagged some row); the
+// other rows keep their first reference, so a row's result does not depend
+// on which rows share its tile.
+template <int D, bool F8, int QB>
+__device__ __forceinline__ void exact_max_pass(Frags<D, F8, QB>& f, PassCtx<D, F8>& x) {
   using QK = QKOps<D, F8>;
-  float m[kQB];
+  float m[QB];
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) m[qb] = -INFINITY;
+  for (int qb = 0; qb < QB; ++qb) m[qb] = -INFINITY;
   x.ks = TileStream{x.Kb, x.kseg, x.kseg};
   for (int t = 0; t < x.ntiles; ++t) {
     __syncthreads();  // every wave is done reading the stage
@@ -586,7 +588,7 @@ __device__ __forceinline__ void exact_max_pass(Frags<D, F8>& f, PassCtx<D, F8>& 
     tile_barrier();  // landed
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      f32x4 S[2][kQB];
+      f32x4 S[2][QB];
       qk_step<D, F8>(S, x.k0 + sub * 32 * QK::ROWB, x, f);
       if (t * kBN + kBN > x.Nkv)
         rowmax_step<true>(S, m, t * kBN + sub * 32, x.Nkv, x.g);
@@ -596,7 +598,8 @@ __device__ __forceinline__ void exact_max_pass(Frags<D, F8>& f, PassCtx<D, F8>& 
   }
   __syncthreads();
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) f.m[qb] = m[qb];
+  for (int qb = 0; qb < QB; ++qb)
+    if (!(quad_sum(f.l[qb]) < kMaxSum)) f.m[qb] = m[qb];
 }
 
 // Where the tokens of one (b, h) live.  Contiguous [B,H,N,D] tensors are one
@@ -610,6 +613,7 @@ struct Layout {
   int htot;        // heads in the buffers
   int hoff;        // first head of the launch
   int B;
+  int tile0;       // first query tile of the launch (tiles of 16 * QB * kWaves rows)
 };
 
 // Element offset of token n of the (b, hh) head: segment n / seg.
@@ -673,6 +677,7 @@ __device__ __forceinline__ TileInfo tile_info(int u, int total, int n_qtiles, in
   constexpr int QKB = F8 ? 1 : 2;  // bytes per q / k element
   TileInfo ti;
   int tile = remap_xcd(u, total);
+  if (!SPLIT) tile += lay.tile0;
   ti.chunk = 0;
   if (SPLIT) {
     const int v = tile;
@@ -724,8 +729,8 @@ __device__ __forceinline__ TileInfo tile_info(int u, int total, int n_qtiles, in
 // of the joint sequence (text first), turned by its part's rotary table when
 // the part has one; the fragment of k-step ks holds channel pairs
 // 16 ks + 4 g .. +3 of the lane's token, one per 32-bit word.
-template <int D, bool F8, bool JOINT>
-__device__ __forceinline__ void begin_tile(Frags<D, F8>& f, PassCtx<D, F8>& x, const TileInfo& ti,
+template <int D, bool F8, bool JOINT, int QB>
+__device__ __forceinline__ void begin_tile(Frags<D, F8, QB>& f, PassCtx<D, F8>& x, const TileInfo& ti,
                                            const void* Q, int Nq, const Layout& lay,
                                            int64_t qsstride, int c16, const JointArgs& ja) {
   using QK = QKOps<D, F8>;
@@ -740,9 +745,9 @@ __device__ __forceinline__ void begin_tile(Frags<D, F8>& f, PassCtx<D, F8>& x, c
   x.ntiles = (ti.Nkv + kBN - 1) / kBN;
   x.c = ti.c;
   stage_first<D, F8>(x);
-  const int qrow0 = ti.qt * kBM + x.wave * (16 * kQB) + c16;
+  const int qrow0 = ti.qt * (16 * QB * kWaves) + x.wave * (16 * QB) + c16;
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const int row = min(qrow0 + 16 * qb, Nq - 1);
     if constexpr (JOINT && !F8) {
       const bool txt = row < ja.Nt;
@@ -772,14 +777,14 @@ __device__ __forceinline__ void begin_tile(Frags<D, F8>& f, PassCtx<D, F8>& x, c
 }
 
 // Attention of the unit begin_tile pointed the pass at.  Second attempt only
-// if some row's sum outgrew its reference max: then the tile is redone with
-// the exact row max (all waves decide together).  Ends with every wave done
+// if some row's sum outgrew its reference max: then the tile is redone (all
+// waves decide together) with the exact row max for those rows.  Ends with every wave done
 // with the LDS stages.
-template <int D, bool F8, bool PF>
-__device__ __forceinline__ void compute_tile(Frags<D, F8>& f, PassCtx<D, F8>& x) {
+template <int D, bool F8, bool PF, int QB>
+__device__ __forceinline__ void compute_tile(Frags<D, F8, QB>& f, PassCtx<D, F8>& x) {
   using Gm = Geo<D>;
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     f.m[qb] = -INFINITY;
     f.l[qb] = 0.f;
     f.lb[qb] = f32x4{};
@@ -790,7 +795,7 @@ __device__ __forceinline__ void compute_tile(Frags<D, F8>& f, PassCtx<D, F8>& x)
   if (__syncthreads_or(flag)) {
     exact_max_pass<D, F8>(f, x);
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       f.l[qb] = 0.f;
       f.lb[qb] = f32x4{};
 #pragma unroll
@@ -804,16 +809,16 @@ __device__ __forceinline__ void compute_tile(Frags<D, F8>& f, PassCtx<D, F8>& x)
 
 // Epilogue of one unit: O = O^T / lb, LSE = (m*c + log2 l) * ln 2.  Every
 // lane stores (a row past Nq stores row Nq - 1, which it computed from that
-// row's query, so the same bits), so each wave issues exactly kQB * DB output
+// row's query, so the same bits), so each wave issues exactly QB * DB output
 // stores, which the next unit's first waits count on.
-template <int D, bool OUT_F32, bool F8, bool SPLIT>
-__device__ __forceinline__ void store_tile(const Frags<D, F8>& f, const TileInfo& ti, void* Oout,
+template <int D, bool OUT_F32, bool F8, bool SPLIT, int QB>
+__device__ __forceinline__ void store_tile(const Frags<D, F8, QB>& f, const TileInfo& ti, void* Oout,
                                            float* LSE, int Nq, const Layout& lay, int64_t qsstride,
                                            const Split& sp, int wave, int c16, int g) {
   using Gm = Geo<D>;
-  const int qrow0 = ti.qt * kBM + wave * (16 * kQB) + c16;
+  const int qrow0 = ti.qt * (16 * QB * kWaves) + wave * (16 * QB) + c16;
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = quad_sum(f.l[qb]);
     const float inv = 1.0f / f.lb[qb][0];
     const int qrow = min(qrow0 + 16 * qb, Nq - 1);
@@ -845,7 +850,7 @@ __device__ __forceinline__ void store_tile(const Frags<D, F8>& f, const TileInfo
 // per-(b, h) factors qds[bh] * kds[bh]; else q and k are bf16 and qds, kds
 // are unused.  SPLIT: a key-split launch, total_tiles is then the number of
 // units.
-template <int D, bool OUT_F32, bool F8, bool SPLIT = false, bool JOINT = false>
+template <int D, bool OUT_F32, bool F8, bool SPLIT = false, bool JOINT = false, int QB = kQB>
 __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const void* __restrict__ K,
                                               const __bf16* __restrict__ V, void* __restrict__ Oout,
                                               float* __restrict__ LSE, int Nq, int Nkv,
@@ -904,7 +909,7 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
     }
   }
 
-  Frags<D, F8> f;
+  Frags<D, F8, QB> f;
   int u = blockIdx.x;
   TileInfo ti =
       tile_info<D, F8, SPLIT, JOINT>(u, total_tiles, n_qtiles, Nkv, lay, K, V, c, qds, kds, sp, ja);
@@ -930,14 +935,15 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
   }
 }
 
-template <int D, bool OUT_F32>
+// QB = 1: half-height tiles (128 query rows), for the last partial round.
+template <int D, bool OUT_F32, int QB = kQB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                           const __bf16* __restrict__ V, void* __restrict__ Oout,
                           float* __restrict__ LSE, int Nq, int Nkv, int n_qtiles, int total_tiles,
                           float c, Layout lay) {
-  attn_fwd_body<D, OUT_F32, false>(Q, K, V, Oout, LSE, Nq, Nkv, n_qtiles, total_tiles, c, lay,
-                                   nullptr, nullptr);
+  attn_fwd_body<D, OUT_F32, false, false, false, QB>(Q, K, V, Oout, LSE, Nq, Nkv, n_qtiles,
+                                                     total_tiles, c, lay, nullptr, nullptr);
 }
 
 // Key-split partials (float32 O and LSE into the workspace).
@@ -991,15 +997,54 @@ unsigned persistent_grid(int64_t total) {
   return (unsigned)(total < n ? total : n);
 }
 
+// Query tiles of a plain launch: whole rounds of full tiles over the
+// persistent grid's slots, then, when the tiles of the last partial round
+// would fill at most half the slots, those tiles as half-height ones (two
+// each), which then take one round of about half the time.  Full tile t
+// covers half tiles 2t and 2t + 1 of its head (its second half may lie
+// past the head's last row, and then it does not exist).
+struct FwdSplitRounds {
+  int n_full, n_half;          // query tiles per head, full / half height
+  int64_t full_units;          // full tiles of the main launch
+  int half_tile0, half_units;  // half tiles of the second launch
+};
+FwdSplitRounds fwd_rounds(int Nq, int64_t heads) {
+  FwdSplitRounds r;
+  r.n_full = (Nq + kBM - 1) / kBM;
+  r.n_half = (Nq + kBM / 2 - 1) / (kBM / 2);
+  const int64_t total = heads * r.n_full;
+  const int64_t slots = persistent_grid(total);
+  const int64_t rem = slots > 0 ? total % slots : 0;
+  r.full_units = total;
+  r.half_tile0 = r.half_units = 0;
+  if (total > slots && rem > 0 && 2 * rem <= slots) {
+    r.full_units = total - rem;
+    const int64_t h0 = r.full_units / r.n_full, t0 = r.full_units - h0 * r.n_full;
+    const int64_t g0 = h0 * r.n_half + 2 * t0;
+    r.half_tile0 = (int)g0;
+    r.half_units = (int)(heads * r.n_half - g0);
+  }
+  return r;
+}
+
 template <int D, bool OUT_F32>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float* lse, int Nq,
                     int Nkv, float c, const Layout& lay, hipStream_t stream) {
-  const int n_qtiles = (Nq + kBM - 1) / kBM;
-  const int64_t total = (int64_t)lay.B * lay.hg * n_qtiles;
-  if (total > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OUT_F32>), dim3(persistent_grid(total)), dim3(kThreads), 0,
-                     stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                     static_cast<const __bf16*>(v), o, lse, Nq, Nkv, n_qtiles, (int)total, c, lay);
+  const int64_t heads = (int64_t)lay.B * lay.hg;
+  if (heads * ((Nq + kBM / 2 - 1) / (kBM / 2)) > 0x7fffffff) return hipErrorInvalidValue;
+  const FwdSplitRounds r = fwd_rounds(Nq, heads);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OUT_F32>), dim3(persistent_grid(r.full_units)),
+                     dim3(kThreads), 0, stream, static_cast<const __bf16*>(q),
+                     static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), o, lse, Nq, Nkv,
+                     r.n_full, (int)r.full_units, c, lay);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || r.half_units == 0) return e;
+  Layout lh = lay;
+  lh.tile0 = r.half_tile0;
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OUT_F32, 1>), dim3(persistent_grid(r.half_units)),
+                     dim3(kThreads), 0, stream, static_cast<const __bf16*>(q),
+                     static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), o, lse, Nq, Nkv,
+                     r.n_half, r.half_units, c, lh);
   return hipGetLastError();
 }
 
@@ -1033,7 +1078,7 @@ hipError_t launch_layout(const void* q, const void* k, const void* v, void* o, f
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                             int B, int H, int Nq, int Nkv, int D, float scale, bool o_f32,
                             hipStream_t stream) {
-  const Layout lay{Nq, Nkv, H, H, 0, B};
+  const Layout lay{Nq, Nkv, H, H, 0, B, 0};
   return o_f32 ? launch_layout<true>(q, k, v, o, lse, Nq, Nkv, D, scale, lay, stream)
                : launch_layout<false>(q, k, v, o, lse, Nq, Nkv, D, scale, lay, stream);
 }
@@ -1044,7 +1089,7 @@ hipError_t launch_attn_bf16_balanced(const void* q, const void* k, const void* v
                                      hipStream_t stream) {
   if (pl.nsplit <= 1)
     return launch_attn_bf16(q, k, v, o, lse, B, H, Nq, Nkv, D, scale, o_f32, stream);
-  const Layout lay{Nq, Nkv, H, H, 0, B};
+  const Layout lay{Nq, Nkv, H, H, 0, B, 0};
   const float c = scale * 1.4426950408889634f;
   const int n_qtiles = (Nq + kBM - 1) / kBM;
   hipError_t e = hipSuccess;
@@ -1088,7 +1133,7 @@ hipError_t launch_attn_joint(const void* k_packed, const void* v_packed, const J
                              void* o, float* lse, int B, int H, int Nt, int Ni, int D, float scale,
                              hipStream_t stream) {
   const int N = Nt + Ni;
-  const Layout lay{N, N, H, H, 0, B};
+  const Layout lay{N, N, H, H, 0, B, 0};
   const float c = scale * 1.4426950408889634f;
   const int n_qtiles = (N + kBM - 1) / kBM;
   const int64_t total = (int64_t)B * H * n_qtiles;
@@ -1114,7 +1159,7 @@ hipError_t launch_attn_joint(const void* k_packed, const void* v_packed, const J
 hipError_t launch_attn_fp8(const void* q, const void* k, const void* v, const float* q_descale,
                            const float* k_descale, void* o, float* lse, int B, int H, int Nq,
                            int Nkv, float scale, bool o_f32, hipStream_t stream) {
-  const Layout lay{Nq, Nkv, H, H, 0, B};
+  const Layout lay{Nq, Nkv, H, H, 0, B, 0};
   const float c = scale * 1.4426950408889634f;
   return o_f32 ? launch_fp8<true>(q, k, v, q_descale, k_descale, o, lse, Nq, Nkv, c, lay, stream)
                : launch_fp8<false>(q, k, v, q_descale, k_descale, o, lse, Nq, Nkv, c, lay, stream);
@@ -1124,7 +1169,7 @@ hipError_t launch_attn_bf16_ulysses(const void* q, const void* k, const void* v,
                                     float* lse, int P, int r, int B, int H, int N, int D,
                                     float scale, hipStream_t stream) {
   const int ns = N / P, hg = H / P;
-  const Layout lay{ns, ns, hg, H, r * hg, B};
+  const Layout lay{ns, ns, hg, H, r * hg, B, 0};
   return launch_layout<false>(q, k, v, o, lse, N, N, D, scale, lay, stream);
 }
 

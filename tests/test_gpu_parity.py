@@ -172,6 +172,41 @@ def test_bf16_score_jump_takes_exact_max_path(Nkv):
     assert abs(to_f64(O)[0, 0, 5] - f64(vb)[0, 0, 700]).max() < 2e-2
 
 
+def test_exact_max_fallback_is_per_row():
+    """Only the rows whose sum outgrew the fixed reference are redone with the
+    exact max: the other rows of the same tile come out bit for bit as they
+    do when no row of the tile needs the second pass."""
+    say("bf16 per-row fallback")
+    rng = np.random.default_rng(92)
+    q = rng.standard_normal((1, 1, 256, 128)).astype(np.float32)
+    k = rng.standard_normal((1, 1, 1000, 128)).astype(np.float32)
+    v = rng.standard_normal((1, 1, 1000, 128)).astype(np.float32)
+    k[0, 0, 700] = 6.0 * q[0, 0, 5]
+    qb, kb, vb = (datagen.bf16_bits(x) for x in (q, k, v))
+    q2 = qb.copy()
+    q2[0, 0, 5] = q2[0, 0, 6]                # no row of the tile jumps now
+    O1, L1 = dta.dit_attn_fwd_block(*(bits_to_torch_bf16(x) for x in (qb, kb, vb)))
+    O2, L2 = dta.dit_attn_fwd_block(*(bits_to_torch_bf16(x) for x in (q2, kb, vb)))
+    keep = [i for i in range(256) if i != 5]
+    assert torch.equal(O1[0, 0, keep], O2[0, 0, keep])
+    assert torch.equal(L1[0, 0, keep], L2[0, 0, keep])
+    Oref, _ = oracle.attention(f64(qb), f64(kb), f64(vb))
+    assert max_abs(to_f64(O1)[0, 0, 5], Oref[0, 0, 5]) <= 2e-2
+
+
+def test_half_height_tail_equals_head_by_head():
+    """The image-DiT share (B1 H24 N4096 D128) is 384 query tiles of 256 rows
+    on 256 compute units: the last 128 run as 256 half-height tiles.  Each row
+    must come out bit for bit as in a one-head launch (16 full tiles)."""
+    say("bf16 half-height tail, image share")
+    q, k, v = (bits_to_torch_bf16(x) for x in datagen.small_bf16(1, 24, 4096, 128, seed=21))
+    O, L = dta.dit_attn_fwd(q, k, v)
+    for h in range(24):
+        Oh, Lh = dta.dit_attn_fwd(*(t[:, h:h + 1].contiguous() for t in (q, k, v)))
+        assert torch.equal(O[:, h:h + 1], Oh), h
+        assert torch.equal(L[:, h:h + 1], Lh), h
+
+
 def test_uniform_v_returns_v():
     say("bf16 uniform V")
     qb, kb, _ = datagen.small_bf16(1, 2, 200, 128, seed=5)
