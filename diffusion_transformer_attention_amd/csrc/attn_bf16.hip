@@ -69,6 +69,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // LDS pointers are 32-bit address-space-3 pointers throughout.
@@ -520,13 +521,13 @@ __device__ __forceinline__ void stage_first(PassCtx<D, F8>& x) {
 // One full pass over the keys whose first tiles stage_first has issued: the
 // unmasked tiles (unrolled by the stage count), the partial last tile (if
 // any) with masking, then the PV of the last step.  Returns true if some
-// row's sum outgrew its reference.  PF: the first tiles were issued before
-// the previous tile's NST output stores, so the first two waits leave those
-// stores in flight.
-template <int D, bool F8, bool PF, int QB>
+// row's sum outgrew its reference.  NST > 0: the first tiles were issued
+// before the previous tile's NST output and LSE stores, so the first two
+// waits leave those stores in flight.
+template <int D, bool F8, int NST, int QB>
 __device__ __forceinline__ bool run_pass_body(Frags<D, F8, QB>& f, PassCtx<D, F8>& x) {
   using Gm = Geo<D>;
-  constexpr int NST = PF ? QB * Gm::DB : 0;  // output store instructions per wave
+  constexpr bool PF = NST > 0;
   // The first slot multiplies P = 0 by the V stage of tile -1 (stage 2): zero
   // it so no stale Inf/NaN bit pattern can turn 0 * V into NaN.
   for (int i = threadIdx.x; i < Gm::TILE / 16; i += kThreads)
@@ -780,7 +781,9 @@ __device__ __forceinline__ void begin_tile(Frags<D, F8, QB>& f, PassCtx<D, F8>& 
 // if some row's sum outgrew its reference max: then the tile is redone (all
 // waves decide together) with the exact row max for those rows.  Ends with every wave done
 // with the LDS stages.
-template <int D, bool F8, bool PF, int QB>
+// NST: output store instructions per wave still in flight from the previous
+// unit (0 for the first unit).
+template <int D, bool F8, int NST, int QB>
 __device__ __forceinline__ void compute_tile(Frags<D, F8, QB>& f, PassCtx<D, F8>& x) {
   using Gm = Geo<D>;
 #pragma unroll
@@ -791,7 +794,7 @@ __device__ __forceinline__ void compute_tile(Frags<D, F8, QB>& f, PassCtx<D, F8>
 #pragma unroll
     for (int db = 0; db < Gm::DB; ++db) f.o[qb][db] = f32x4{};
   }
-  const bool flag = run_pass_body<D, F8, PF>(f, x);
+  const bool flag = run_pass_body<D, F8, NST>(f, x);
   if (__syncthreads_or(flag)) {
     exact_max_pass<D, F8>(f, x);
 #pragma unroll
@@ -802,21 +805,35 @@ __device__ __forceinline__ void compute_tile(Frags<D, F8, QB>& f, PassCtx<D, F8>
       for (int db = 0; db < Gm::DB; ++db) f.o[qb][db] = f32x4{};
     }
     stage_first<D, F8>(x);
-    run_pass_body<D, F8, false>(f, x);
+    run_pass_body<D, F8, 0>(f, x);
     __syncthreads();
   }
 }
 
+// Store instructions per wave of one unit's epilogue: per query block, one
+// per 16-channel block (float32) or per 32-channel pair of blocks (bf16),
+// and one for the LSE.
+template <int D, bool OUT_F32, int QB>
+constexpr int kStoreInsts = QB * ((OUT_F32 ? Geo<D>::DB : Geo<D>::DB / 2) + 1);
+
 // Epilogue of one unit: O = O^T / lb, LSE = (m*c + log2 l) * ln 2.  Every
 // lane stores (a row past Nq stores row Nq - 1, which it computed from that
-// row's query, so the same bits), so each wave issues exactly QB * DB output
-// stores, which the next unit's first waits count on.
+// row's query, so the same bits), so each wave issues exactly kStoreInsts
+// stores, with or without an LSE, which the next unit's first waits count on.
+// bf16 output: a lane of group g holds channels 16 db + 4 g .. +3 of its row;
+// blocks 2p and 2p + 1 are exchanged between groups g and g ^ 1
+// (v_permlane16_swap swaps the odd 16-lane rows of one register with the
+// even rows of another), after which group g holds the 8 channels
+// 16 (2p + (g & 1)) + 8 (g >> 1) .. +7 and each row's 4 lanes write its
+// channels [32p, 32p + 32) as 16-byte pieces: half the instructions, and
+// 64-byte row pieces instead of 32-byte ones.
 template <int D, bool OUT_F32, bool F8, bool SPLIT, int QB>
 __device__ __forceinline__ void store_tile(const Frags<D, F8, QB>& f, const TileInfo& ti, void* Oout,
                                            float* LSE, int Nq, const Layout& lay, int64_t qsstride,
                                            const Split& sp, int wave, int c16, int g) {
   using Gm = Geo<D>;
-  const int qrow0 = ti.qt * (16 * QB * kWaves) + wave * (16 * QB) + c16;
+  const int qtop = ti.qt * (16 * QB * kWaves) + wave * (16 * QB);  // the wave's first row
+  const int qrow0 = qtop + c16;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = quad_sum(f.l[qb]);
@@ -824,20 +841,38 @@ __device__ __forceinline__ void store_tile(const Frags<D, F8, QB>& f, const Tile
     const int qrow = min(qrow0 + 16 * qb, Nq - 1);
     const int64_t wrow = (int64_t)ti.chunk * sp.rows + (int64_t)ti.bh * Nq + qrow - sp.row0;
     const int64_t obase = SPLIT ? wrow * D : token_offset(qrow, lay.qseg, ti.qhead, qsstride, D);
+    if (OUT_F32) {
 #pragma unroll
-    for (int db = 0; db < Gm::DB; ++db) {
-      const int d0 = db * 16 + 4 * g;
-      const f32x4 val = f.o[qb][db] * inv;
-      if (OUT_F32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(Oout) + obase + d0) = val;
-      } else {
-        const bf16x4 b = {(__bf16)val[0], (__bf16)val[1], (__bf16)val[2], (__bf16)val[3]};
-        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(Oout) + obase + d0) = b;
+      for (int db = 0; db < Gm::DB; ++db)
+        *reinterpret_cast<f32x4*>(static_cast<float*>(Oout) + obase + db * 16 + 4 * g) =
+            f.o[qb][db] * inv;
+    } else {
+#pragma unroll
+      for (int p = 0; p < Gm::DB / 2; ++p) {
+        const f32x4 a = f.o[qb][2 * p] * inv, b = f.o[qb][2 * p + 1] * inv;
+        const u32x2 aw = __builtin_bit_cast(
+            u32x2, bf16x4{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3]});
+        const u32x2 bw = __builtin_bit_cast(
+            u32x2, bf16x4{(__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]});
+        const auto lo = __builtin_amdgcn_permlane16_swap(aw[0], bw[0], false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap(aw[1], bw[1], false, false);
+        const int ch = 32 * p + 16 * (g & 1) + 8 * (g >> 1);
+        *reinterpret_cast<u32x4*>(static_cast<__bf16*>(Oout) + obase + ch) =
+            u32x4{lo[0], hi[0], lo[1], hi[1]};
       }
     }
-    if (LSE && g == 0)
-      LSE[SPLIT ? wrow : (int64_t)ti.bh * Nq + qrow] =
-          (f.m[qb] * ti.c + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
+    // The LSE goes through a buffer descriptor over the block's 16 rows from
+    // its first (clamped) row r0: the lanes of groups 1-3, and all lanes when
+    // LSE is null (a zero-size record), address past its end, and the
+    // hardware drops those stores, so the store instruction is always issued.
+    const int r0 = min(qtop + 16 * qb, Nq - 1);
+    const int64_t lrow = SPLIT ? (int64_t)ti.chunk * sp.rows + (int64_t)ti.bh * Nq + r0 - sp.row0
+                               : (int64_t)ti.bh * Nq + r0;
+    const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
+        LSE ? (void*)(LSE + lrow) : nullptr, (short)0, LSE ? 64 : 0, 0x00020000);
+    const float lse = (f.m[qb] * ti.c + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse), lr,
+                                          g == 0 ? (qrow - r0) * 4 : (1 << 30), 0, 0);
   }
 }
 
@@ -914,7 +949,7 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
   TileInfo ti =
       tile_info<D, F8, SPLIT, JOINT>(u, total_tiles, n_qtiles, Nkv, lay, K, V, c, qds, kds, sp, ja);
   begin_tile<D, F8, JOINT>(f, x, ti, Q, Nq, lay, qsstride, c16, ja);
-  compute_tile<D, F8, false>(f, x);
+  compute_tile<D, F8, 0>(f, x);
   for (;;) {
     const int un = u + gridDim.x;
     const bool more = un < total_tiles;
@@ -931,7 +966,7 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
     if (!more) break;
     u = un;
     ti = tn;
-    compute_tile<D, F8, true>(f, x);
+    compute_tile<D, F8, kStoreInsts<D, OUT_F32, QB>>(f, x);
   }
 }
 
