@@ -229,16 +229,28 @@ def main():
     achieved = flops_launch / (attn_avg_ms * 1e-3) / 1e12
 
     # permute legs, timed alone (bytes moved = read + write of one tensor)
-    def time_it(fn, reps=10):
+    def time_it(fn, reps=10, min_ms=25.0):
+        """Mean event time of back-to-back calls: after one call, warm up for
+        about min_ms (a short kernel timed right after a long leg otherwise
+        runs at the clock that leg left), then time at least `reps` calls and
+        at least min_ms."""
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         fn()
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        for _ in range(reps):
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        n = max(1, math.ceil(min_ms / max(a.elapsed_time(b), 1e-3)))
+        for _ in range(min(n, 200) - 1):
+            fn()
+        n = min(max(reps, n), 500)
+        a.record(stream)
+        for _ in range(n):
             fn()
         b.record(stream)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
+        return a.elapsed_time(b) / n
 
     perm_bytes = 2.0 * B * H_FULL * N * D * 2
     s2h_ms = time_it(lambda: dta.ulysses_seq2head(shards[0], out=groups[0]))
