@@ -78,6 +78,7 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) const u32x4 lds_cu32x4;
+typedef __attribute__((address_space(3))) int lds_i32;
 
 constexpr int kWaves = 8;               // two waves per SIMD
 constexpr int kThreads = 64 * kWaves;
@@ -298,6 +299,12 @@ struct PassCtx {
   int kof[QK::KS];       // K fragment (ks): byte offset within a 16-key block + kbase
   int vxo[Geo<D>::DB];   // V^T fragment (db): byte offset within a 32-key step + vbase
   int kbase, vbase;      // LDS addresses of the stages k0 and v0
+  // The lane's query rows (one per 16-row block) of this unit and of the
+  // next one (null: the next unit's queries are loaded by begin_tile).
+  const char* cq[2];
+  const char* nq[2];
+  bool nqv;              // nq holds the next unit's rows
+  lds_i32* anyw;         // one word per wave for any_row_flagged
   int kld[(QK::PIECES + kWaves - 1) / kWaves];      // K load-piece source offsets
   int vld[(Geo<D>::PIECES + kWaves - 1) / kWaves];  // V load-piece source offsets
 };
@@ -359,7 +366,9 @@ __device__ __forceinline__ void rowmax_step(const f32x4 (&S)[2][QB], float (&m)[
 // and issues the LDS reads of the fragments first needed LA groups later.
 // The P^T operand of block qb packs the keys 4g + r (kb 0) and 16 + 4g + r
 // (kb 1): MFMA k index 8g + j <-> key 4g + j (j < 4), 16 + 4g + j - 4 (j >= 4).
-template <int D, bool F8, bool MASK, int QB>
+// NOQK: the last slot of a pass, which has no next step: no QK^T MFMAs and
+// no K fragment reads.
+template <int D, bool F8, bool MASK, bool NOQK = false, int QB>
 __device__ __forceinline__ void slot(Frags<D, F8, QB>& f, const f32x4 (&Sc)[2][QB], f32x4 (&Sn)[2][QB],
                                      const bf16x8 (&Pp)[QB], bf16x8 (&Pc)[QB],
                                      const lds_t* k_next, const lds_t* v_prev,
@@ -390,7 +399,7 @@ __device__ __forceinline__ void slot(Frags<D, F8, QB>& f, const f32x4 (&Sc)[2][Q
   auto vfirst = [](int fi) { return fi * QB * NG / NPV; };
 #pragma unroll
   for (int fi = 0; fi < NKF; ++fi)
-    if (kfirst(fi) < LA) load_k(fi);
+    if (!NOQK && kfirst(fi) < LA) load_k(fi);
 #pragma unroll
   for (int fi = 0; fi < NVF; ++fi)
     if (vfirst(fi) < LA) load_v(fi);
@@ -405,20 +414,21 @@ __device__ __forceinline__ void slot(Frags<D, F8, QB>& f, const f32x4 (&Sc)[2][Q
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) Sn[kb][qb] = f32x4{};
+    for (int qb = 0; qb < QB; ++qb)
+      if (!NOQK) Sn[kb][qb] = f32x4{};
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
 #pragma unroll
     for (int fi = 0; fi < NKF; ++fi)
-      if (kfirst(fi) >= LA && kfirst(fi) == g + LA) load_k(fi);
+      if (!NOQK && kfirst(fi) >= LA && kfirst(fi) == g + LA) load_k(fi);
 #pragma unroll
     for (int fi = 0; fi < NVF; ++fi)
       if (vfirst(fi) >= LA && vfirst(fi) == g + LA) load_v(fi);
 #pragma unroll
     for (int i = g * NQK / NG; i < (g + 1) * NQK / NG; ++i) {
       const int ks = i / (2 * QB), kb = (i / QB) % 2, qb = i % QB;
-      Sn[kb][qb] = QK::mma(kf[ks * 2 + kb], f.q[qb][ks], Sn[kb][qb]);
+      if (!NOQK) Sn[kb][qb] = QK::mma(kf[ks * 2 + kb], f.q[qb][ks], Sn[kb][qb]);
     }
 #pragma unroll
     for (int j = g * NPV / NG; j < (g + 1) * NPV / NG; ++j) {
@@ -458,13 +468,26 @@ __device__ __forceinline__ void slot(Frags<D, F8, QB>& f, const f32x4 (&Sc)[2][Q
   }
 }
 
+// Load the queries of the lane's rows (one row pointer per 16-row block) as
+// the Q^T operands.
+template <int D, bool F8, int QB>
+__device__ __forceinline__ void load_queries(Frags<D, F8, QB>& f, const char* const (&rows)[2], int g) {
+  using QK = QKOps<D, F8>;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < QK::KS; ++ks) f.q[qb][ks] = QK::load_q(rows[qb], g, ks);
+}
+
 // One 64-key tile t = slots 2t and 2t+1.  PH = t % 3 when known at compile
 // time (the unrolled main loop: every LDS stage is then a distinct array and
 // the loads into stage t+2 overlap the reads of the others), or -1.
 // On entry S0 holds S^T of step 2t and Pa holds P of step 2t-1; on exit S0
-// holds S^T of step 2t+2 (garbage past the last tile, never used) and Pa
-// holds P of step 2t+1.
-template <int D, bool F8, int PH, bool MASK, int WAITN = 0, int QB>
+// holds S^T of step 2t+2 and Pa holds P of step 2t+1.  LAST: t is the last
+// tile, so there is no step 2t+2: its slot has no QK^T, and once the first
+// slot's QK^T has read the queries, the next unit's queries are loaded in
+// their place (when x.nqv), a tile and the epilogue ahead of their use.
+template <int D, bool F8, int PH, bool MASK, int WAITN = 0, bool LAST = false, int QB>
 __device__ __forceinline__ void tile_trip(int t, Frags<D, F8, QB>& f, f32x4 (&S0)[2][QB], f32x4 (&S1)[2][QB],
                                           bf16x8 (&Pa)[QB], bf16x8 (&Pb)[QB],
                                           PassCtx<D, F8>& x) {
@@ -482,7 +505,12 @@ __device__ __forceinline__ void tile_trip(int t, Frags<D, F8, QB>& f, f32x4 (&S0
   const lds_t* vprev = VSTAGE(x, p2, t + 2);  // stage of tile t-1
   const int key0 = t * kBN;
   slot<D, F8, MASK>(f, S0, S1, Pa, Pb, kcur + 32 * QK::ROWB, vprev + 32 * Gm::ROWB, x, key0);
-  slot<D, F8, MASK>(f, S1, S0, Pb, Pa, knext, vcur, x, key0 + 32);
+  if (LAST) {
+    if (x.nqv) load_queries<D, F8>(f, x.nq, x.g);
+    slot<D, F8, MASK, true>(f, S1, S0, Pb, Pa, knext, vcur, x, key0 + 32);
+  } else {
+    slot<D, F8, MASK>(f, S1, S0, Pb, Pa, knext, vcur, x, key0 + 32);
+  }
 }
 
 // O^T += V^T P^T for one 32-key step (used once, after the loop).
@@ -549,22 +577,23 @@ __device__ __forceinline__ bool run_pass_body(Frags<D, F8, QB>& f, PassCtx<D, F8
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) f.m[qb] = m[qb];
   }
-  const bool partial = (x.Nkv % kBN) != 0;
-  const int nfull = partial ? x.ntiles - 1 : x.ntiles;
+  const int nmid = x.ntiles - 1;  // tiles before the last
   int t = 0;
-  if (PF && nfull >= kStages) {  // no load is issued between the first wait and trip 0's
+  if (PF && nmid >= kStages) {  // no load is issued between the first wait and trip 0's
     tile_trip<D, F8, 0, false, NST>(0, f, S0, S1, Pa, Pb, x);
     tile_trip<D, F8, 1, false>(1, f, S0, S1, Pa, Pb, x);
     tile_trip<D, F8, 2, false>(2, f, S0, S1, Pa, Pb, x);
     t = kStages;
   }
-  for (; t + kStages <= nfull; t += kStages) {
+  for (; t + kStages <= nmid; t += kStages) {
     tile_trip<D, F8, 0, false>(t, f, S0, S1, Pa, Pb, x);
     tile_trip<D, F8, 1, false>(t + 1, f, S0, S1, Pa, Pb, x);
     tile_trip<D, F8, 2, false>(t + 2, f, S0, S1, Pa, Pb, x);
   }
-  for (; t < nfull; ++t) tile_trip<D, F8, -1, false>(t, f, S0, S1, Pa, Pb, x);
-  if (partial) tile_trip<D, F8, -1, true>(t, f, S0, S1, Pa, Pb, x);
+  for (; t < nmid; ++t) tile_trip<D, F8, -1, false>(t, f, S0, S1, Pa, Pb, x);
+  // the last tile, masked whether or not it is partial (one instantiation
+  // for both keeps the kernel within its registers)
+  tile_trip<D, F8, -1, true, 0, true>(t, f, S0, S1, Pa, Pb, x);
   pv_step<D, F8>(f, Pa, VSTAGE(x, -1, x.ntiles - 1) + 32 * Gm::ROWB, x);
   bool flag = false;
 #pragma unroll
@@ -725,17 +754,33 @@ __device__ __forceinline__ TileInfo tile_info(int u, int total, int n_qtiles, in
   return ti;
 }
 
-// Point the pass at a unit, issue its first K / V tiles and load its queries
-// (rows past Nq load row Nq - 1).  JOINT: a query is a text or an image token
-// of the joint sequence (text first), turned by its part's rotary table when
-// the part has one; the fragment of k-step ks holds channel pairs
-// 16 ks + 4 g .. +3 of the lane's token, one per 32-bit word.
+// The lane's query row pointers of a unit, one per 16-row block (rows past
+// Nq point at row Nq - 1).
+template <int D, bool F8, int QB>
+__device__ __forceinline__ void query_rows(const char* (&rows)[2], const TileInfo& ti, const void* Q,
+                                           int Nq, const Layout& lay, int64_t qsstride, int wave,
+                                           int c16) {
+  constexpr int QKB = F8 ? 1 : 2;
+  const int qrow0 = ti.qt * (16 * QB * kWaves) + wave * (16 * QB) + c16;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = min(qrow0 + 16 * (qb < QB ? qb : 0), Nq - 1);
+    rows[qb] = static_cast<const char*>(Q) + token_offset(row, lay.qseg, ti.qhead, qsstride, D) * QKB;
+  }
+}
+
+// Point the pass at a unit and issue its first K / V tiles; load its queries
+// when `loadq` (otherwise the previous unit's last tile has loaded them).
+// JOINT: a query is a text or an image token of the joint sequence (text
+// first), turned by its part's rotary table when the part has one; the
+// fragment of k-step ks holds channel pairs 16 ks + 4 g .. +3 of the lane's
+// token, one per 32-bit word.
 template <int D, bool F8, bool JOINT, int QB>
 __device__ __forceinline__ void begin_tile(Frags<D, F8, QB>& f, PassCtx<D, F8>& x, const TileInfo& ti,
                                            const void* Q, int Nq, const Layout& lay,
-                                           int64_t qsstride, int c16, const JointArgs& ja) {
+                                           int64_t qsstride, int c16, const JointArgs& ja,
+                                           bool loadq) {
   using QK = QKOps<D, F8>;
-  constexpr int QKB = F8 ? 1 : 2;
   x.Kb = ti.Kb;
   x.Vb = ti.Vb;
   x.kseg = ti.kseg;
@@ -746,6 +791,11 @@ __device__ __forceinline__ void begin_tile(Frags<D, F8, QB>& f, PassCtx<D, F8>& 
   x.ntiles = (ti.Nkv + kBN - 1) / kBN;
   x.c = ti.c;
   stage_first<D, F8>(x);
+  if (!JOINT) {
+    query_rows<D, F8, QB>(x.cq, ti, Q, Nq, lay, qsstride, x.wave, c16);
+    if (loadq) load_queries<D, F8>(f, x.cq, x.g);
+    return;
+  }
   const int qrow0 = ti.qt * (16 * QB * kWaves) + x.wave * (16 * QB) + c16;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -768,13 +818,28 @@ __device__ __forceinline__ void begin_tile(Frags<D, F8, QB>& f, PassCtx<D, F8>& 
         }
         f.q[qb][ks] = __builtin_bit_cast(bf16x8, w);
       }
-    } else {
-      const char* qrow_p =
-          static_cast<const char*>(Q) + token_offset(row, lay.qseg, ti.qhead, qsstride, D) * QKB;
-#pragma unroll
-      for (int ks = 0; ks < QK::KS; ++ks) f.q[qb][ks] = QK::load_q(qrow_p, x.g, ks);
     }
   }
+}
+
+// Whether a row of any wave has `flag`: one LDS word per wave, a wait for
+// the LDS write alone (s_waitcnt lgkmcnt(0); vmcnt and expcnt at their
+// maxima, no wait) and s_barrier.  __syncthreads_or, and a workgroup fence,
+// would also wait for every outstanding vector memory operation, here the
+// next unit's query loads.  The words are next written a unit later, after
+// barriers every wave has passed, so no wave still reads them then.
+template <int D, bool F8>
+__device__ __forceinline__ bool any_row_flagged(const PassCtx<D, F8>& x, bool flag) {
+  const bool w = __builtin_amdgcn_ballot_w64(flag) != 0;
+  if (x.lane == 0) x.anyw[x.wave] = w;
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  int any = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) any |= x.anyw[i];
+  return any != 0;
 }
 
 // Attention of the unit begin_tile pointed the pass at.  Second attempt only
@@ -795,7 +860,8 @@ __device__ __forceinline__ void compute_tile(Frags<D, F8, QB>& f, PassCtx<D, F8>
     for (int db = 0; db < Gm::DB; ++db) f.o[qb][db] = f32x4{};
   }
   const bool flag = run_pass_body<D, F8, NST>(f, x);
-  if (__syncthreads_or(flag)) {
+  if (any_row_flagged(x, flag)) {
+    if (x.nqv) load_queries<D, F8>(f, x.cq, x.g);  // the last tile replaced them
     exact_max_pass<D, F8>(f, x);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -902,6 +968,7 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
   __shared__ __attribute__((aligned(1024))) char v0s[Gm::TILE];
   __shared__ __attribute__((aligned(1024))) char v1s[Gm::TILE];
   __shared__ __attribute__((aligned(1024))) char v2s[Gm::TILE];
+  __shared__ int any_words[kWaves];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -916,6 +983,7 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
   x.v0 = (lds_t*)v0s; x.v1 = (lds_t*)v1s; x.v2 = (lds_t*)v2s;
   x.wave = wave;
   x.lane = lane;
+  x.anyw = (lds_i32*)any_words;
   x.g = g;
   piece_offsets<QK::ROWB, QK::PIECES>(x.kld, wave, lane, [](int r) { return QK::swz(r); });
   piece_offsets<Gm::ROWB, Gm::PIECES>(x.vld, wave, lane, [](int r) { return swz_v<D>(r); });
@@ -944,11 +1012,23 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
     }
   }
 
+  // The next unit's query rows, which this unit's last key tile loads
+  // (JOINT: begin_tile loads and turns them).
+  auto point_next = [&](int un) {
+    x.nqv = !JOINT && un < total_tiles;
+    if (x.nqv) {
+      const TileInfo tp = tile_info<D, F8, SPLIT, JOINT>(un, total_tiles, n_qtiles, Nkv, lay, K, V,
+                                                         c, qds, kds, sp, ja);
+      query_rows<D, F8, QB>(x.nq, tp, Q, Nq, lay, qsstride, wave, c16);
+    }
+  };
+
   Frags<D, F8, QB> f;
   int u = blockIdx.x;
   TileInfo ti =
       tile_info<D, F8, SPLIT, JOINT>(u, total_tiles, n_qtiles, Nkv, lay, K, V, c, qds, kds, sp, ja);
-  begin_tile<D, F8, JOINT>(f, x, ti, Q, Nq, lay, qsstride, c16, ja);
+  begin_tile<D, F8, JOINT>(f, x, ti, Q, Nq, lay, qsstride, c16, ja, true);
+  point_next(u + gridDim.x);
   compute_tile<D, F8, 0>(f, x);
   for (;;) {
     const int un = u + gridDim.x;
@@ -957,7 +1037,7 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
     if (more) {
       tn = tile_info<D, F8, SPLIT, JOINT>(un, total_tiles, n_qtiles, Nkv, lay, K, V, c, qds, kds,
                                           sp, ja);
-      begin_tile<D, F8, JOINT>(f, x, tn, Q, Nq, lay, qsstride, c16, ja);
+      begin_tile<D, F8, JOINT>(f, x, tn, Q, Nq, lay, qsstride, c16, ja, !x.nqv);
     }
     // the next unit's loads stay ahead of this unit's stores
     asm volatile("" ::: "memory");
@@ -966,6 +1046,7 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
     if (!more) break;
     u = un;
     ti = tn;
+    point_next(u + gridDim.x);
     compute_tile<D, F8, kStoreInsts<D, OUT_F32, QB>>(f, x);
   }
 }

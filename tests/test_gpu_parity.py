@@ -194,6 +194,31 @@ def test_exact_max_fallback_is_per_row():
     assert max_abs(to_f64(O1)[0, 0, 5], Oref[0, 0, 5]) <= 2e-2
 
 
+def test_exact_max_fallback_in_later_units():
+    """Score jumps planted in query tiles all over a launch of more tiles than
+    compute units (2 heads x 157 tiles of 256 rows), so that some tiles that
+    need the exact-max pass are not their workgroup's first unit: their
+    queries were loaded by the previous unit's last key tile and must be
+    loaded again for the second pass."""
+    say("bf16 exact-max pass in later persistent units")
+    rng = np.random.default_rng(93)
+    H, N, D = 2, 40000, 128
+    q = rng.standard_normal((1, H, N, D), dtype=np.float32)
+    k = rng.standard_normal((1, H, N, D), dtype=np.float32)
+    v = rng.standard_normal((1, H, N, D), dtype=np.float32)
+    planted = list(range(100, N, 2048))        # one row every 8 tiles
+    for h in range(H):
+        for i, r in enumerate(planted):
+            k[0, h, (7 * r + 13 * i + 5) % N] = 6.0 * q[0, h, r]
+    qb, kb, vb = (datagen.bf16_bits(x) for x in (q, k, v))
+    del q, k, v
+    O, L = dta.dit_attn_fwd(*(bits_to_torch_bf16(x) for x in (qb, kb, vb)))
+    rows = sorted(set(planted) | {r + 1 for r in planted} | {N - 1})
+    Oref, Lref = oracle.attention_rows(f64(qb), f64(kb), f64(vb), rows)
+    Og, Lg = to_f64(O)[:, :, rows], to_f64(L)[:, :, rows]
+    assert_bf16_close(Og, Lg, Oref, Lref, "fallback in later units")
+
+
 def test_half_height_tail_equals_head_by_head():
     """The image-DiT share (B1 H24 N4096 D128) is 384 query tiles of 256 rows
     on 256 compute units: the last 128 run as 256 half-height tiles.  Each row
