@@ -232,6 +232,27 @@ def test_half_height_tail_equals_head_by_head():
         assert torch.equal(L[:, h:h + 1], Lh), h
 
 
+@pytest.mark.parametrize("D,out", [(32, "bf16"), (64, "f32"), (128, "f32")])
+def test_half_height_tail_other_dims_and_f32(D, out):
+    """B1 H40 N4096: 640 query tiles, 2.5 rounds of 256 compute units, so the
+    last 128 tiles run as half-height tiles; every head head-for-head equal,
+    bit for bit, to a launch over 8 heads (160 tiles, one partial round with
+    no tail), and sampled rows within the bars of the oracle."""
+    say("bf16 half-height tail", D, out)
+    H, N = 40, 4096
+    qb, kb, vb = datagen.small_bf16(1, H, N, D, seed=22)
+    q, k, v = (bits_to_torch_bf16(x) for x in (qb, kb, vb))
+    od = torch.float32 if out == "f32" else torch.bfloat16
+    O, L = dta.dit_attn_fwd_block(q, k, v, out_dtype=od)
+    for h0 in range(0, H, 8):
+        Oh, Lh = dta.dit_attn_fwd_block(*(t[:, h0:h0 + 8].contiguous() for t in (q, k, v)), out_dtype=od)
+        assert torch.equal(O[:, h0:h0 + 8], Oh), h0
+        assert torch.equal(L[:, h0:h0 + 8], Lh), h0
+    rows = [0, 127, 128, 255, 2047, 3968, 4095]
+    Oref, Lref = oracle.attention_rows(f64(qb), f64(kb), f64(vb), rows)
+    assert_bf16_close(to_f64(O)[:, :, rows], to_f64(L)[:, :, rows], Oref, Lref, f"tail D{D} {out}")
+
+
 def test_uniform_v_returns_v():
     say("bf16 uniform V")
     qb, kb, _ = datagen.small_bf16(1, 2, 200, 128, seed=5)
