@@ -943,10 +943,13 @@ __device__ __forceinline__ void store_tile(const Frags<D, F8, QB>& f, const Tile
 }
 
 // The kernel body: a persistent workgroup computes units blockIdx.x,
-// blockIdx.x + gridDim.x, ... (gridDim.x a multiple of 8, so they all map to
-// one XCD's range).  After a unit's last LDS read it issues the next unit's
-// first K / V tiles and query loads, and only then stores the unit's output,
-// so the next unit's first waits need not wait for those stores.  F8: q and
+// blockIdx.x + gridDim.x, ... (with more units than workgroups gridDim.x is
+// the compute-unit count, 256, a multiple of 8, so they all map to one XCD's
+// range).  A unit's last key tile loads the next unit's queries (JOINT: the
+// next unit's begin_tile loads and turns them); after the unit's last LDS
+// read it issues the next unit's first K / V tiles, and only then stores the
+// unit's output, so the next unit's first waits need not wait for those
+// stores.  F8: q and
 // k are E4M3 codes (1 byte per element) whose scores are rescaled by the
 // per-(b, h) factors qds[bh] * kds[bh]; else q and k are bf16 and qds, kds
 // are unused.  SPLIT: a key-split launch, total_tiles is then the number of
