@@ -328,6 +328,31 @@ def test_fused_ulysses_small(P, B, H, N, D):
     assert_bf16_close(to_f64(O_full), None, Oref, Lref, f"fused P{P} B{B} H{H} N{N} D{D}")
 
 
+def test_fused_ulysses_with_half_height_tail():
+    """P = 4 over 96 heads of 4096 tokens: each head group of 24 heads is 384
+    query tiles, so every launch ends with a round of half-height tiles.  The
+    fused call equals seq2head -> dit_attn_fwd -> head2seq bit for bit, and
+    sampled rows match the oracle."""
+    P, B, H, N, D = 4, 1, 96, 4096, 64
+    say("fused ulysses with a half-height tail", P, B, H, N, D)
+    qb, kb, vb = datagen.small_bf16(B, H, N, D, seed=71)
+    full = [bits_to_torch_bf16(x) for x in (qb, kb, vb)]
+    sh = [_shard(t, P) for t in full]
+    groups = [dta.ulysses_seq2head(t) for t in sh]
+    out = torch.empty_like(sh[0])
+    outs = []
+    for r in range(P):
+        O_ref, L_ref = dta.dit_attn_fwd(groups[0][r], groups[1][r], groups[2][r])
+        _, L = dta.dit_attn_fwd_ulysses(*sh, r, out=out)
+        assert torch.equal(L, L_ref), f"LSE of group {r}"
+        outs.append(O_ref)
+    assert torch.equal(out, dta.ulysses_head2seq(torch.stack(outs)))
+    rows = [0, 255, 256, 1023, 1024, 3071, 3072, 4095]
+    Oref, _ = oracle.attention_rows(f64(qb), f64(kb), f64(vb), rows)
+    O_full = to_f64(torch.cat(list(out), dim=2))[:, :, rows]
+    assert max_abs(O_full, Oref) <= 2e-2 and rel_rms(O_full, Oref) <= 1e-2
+
+
 # ------------------------------------------------------------ full-size workloads
 @pytest.fixture(scope="module")
 def wan_draw():
