@@ -10,6 +10,9 @@ float32-input kernel, the FP8 kernel (D = 128; codes made by the oracle), and
 the merge of the bf16 kernel's float32 partials over two key blocks; sixteen
 more shapes (D = 128) go through the backward.  Every output element is
 compared with the fp64 oracle at the tolerances of the other parity tests.
+Twelve more shapes of more query tiles than compute units (several units per
+persistent workgroup, some ending in a half-height round) are compared on
+sampled rows.
 """
 import sys
 
@@ -118,3 +121,39 @@ def test_sweep_backward(i, B, H, Nq, Nkv, scale):
         assert rr <= GRAD_REL_RMS, f"bwd sweep {i} {n} rel-RMS {rr:.3e}"
         if n != "delta":
             assert ma <= GRAD_MAX_ABS_REL, f"bwd sweep {i} {n} max-abs {ma:.3e}"
+
+
+# Launches of more query tiles than compute units: the persistent loop over
+# several units per workgroup (the next unit's queries loaded during the last
+# key tile), and a half-height last round when it fills at most half the
+# units.  Twelve shapes drawn once from a fixed seed: B H in 2..12 heads,
+# Nq from 8000 to 40000 (ragged), Nkv from 1 to 3000, D in {32, 64, 128};
+# sampled query rows (first, last, tile edges, random) compared with the
+# oracle, bf16 and float32 O.
+def _multi_unit_shapes():
+    r = np.random.default_rng(2025)
+    out = []
+    for i in range(12):
+        B, H = int(r.integers(1, 3)), int(r.integers(1, 7))
+        Nq = int(r.integers(8000, 40001))
+        Nkv = int(r.integers(1, 9)) if r.random() < 0.25 else int(r.integers(9, 3001))
+        D = int(r.choice([32, 64, 128]))
+        out.append((i, B, H, Nq, Nkv, D))
+    return out
+
+
+@pytest.mark.parametrize("i,B,H,Nq,Nkv,D", _multi_unit_shapes())
+def test_sweep_multi_unit(i, B, H, Nq, Nkv, D):
+    tiles = B * H * ((Nq + 255) // 256)
+    say(f"multi-unit {i}: B{B} H{H} Nq{Nq} Nkv{Nkv} D{D} ({tiles} tiles)")
+    qb, kb, vb = datagen.small_bf16(B, H, Nq, D, seed=3000 + i, Nkv=Nkv)
+    q, k, v = (bits_to_torch_bf16(x) for x in (qb, kb, vb))
+    rg = np.random.default_rng(i)
+    rows = sorted(set([0, 127, 128, 255, 256, Nq - 1, Nq - 129, Nq // 2]) |
+                  set(int(x) for x in rg.integers(0, Nq, 24)))
+    rows = [x for x in rows if 0 <= x < Nq]
+    Oref, Lref = oracle.attention_rows(_f64(qb), _f64(kb), _f64(vb), rows)
+    for od in (torch.bfloat16, torch.float32):
+        O, L = dta.dit_attn_fwd_block(q, k, v, out_dtype=od)
+        assert_bf16_close(to_f64(O)[:, :, rows], to_f64(L)[:, :, rows], Oref, Lref,
+                          f"multi-unit {i} {od}")
