@@ -450,7 +450,7 @@ def main():
                                "attention per head group B1 H10 N32768 D128 (x4), seed 2",
                    "B": B, "H": H, "N": N, "D": D, "P": P, "heads_before_split": H_FULL},
         "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16_kernel<128,false>",
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16_kernel<128,false,2>",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
                      "flops_per_launch": flops_launch, "launches_timed": len(attn_ms)},
