@@ -142,7 +142,10 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantJob j) {
                                             quotient(__uint_as_float(w1 & 0xffff0000u), d), r, true);
         out[h] = r;
       }
-      dst[i] = u32x2{out[0], out[1]};
+      // streaming store: the codes are not read again by this call
+      // (non-temporal: 78.2 -> 74.9 us for the q and k of B1 H10 N32768 D128;
+      // non-temporal loads of x as well measured slower)
+      __builtin_nontemporal_store(u32x2{out[0], out[1]}, dst + i);
     }
   }
   if (chunk == 0 && threadIdx.x == 0)
