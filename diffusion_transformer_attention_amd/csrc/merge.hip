@@ -79,7 +79,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict
       __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(static_cast<float*>(o) + off));
     } else {
       bf16x4 b = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
-      *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(o) + off) = b;
+      // streaming store, as for float32 O (531 -> 485 us for 4 partials of
+      // [1,40,32768,128] into bf16, bit-identical)
+      __builtin_nontemporal_store(__builtin_bit_cast(unsigned long long, b),
+                                  reinterpret_cast<unsigned long long*>(static_cast<__bf16*>(o) + off));
     }
     if (lse && c4 == 0)
       lse[row] = (M == -INFINITY) ? -INFINITY : M + __builtin_amdgcn_logf(tot) * kLn2;
