@@ -161,6 +161,27 @@ def test_fp8_large_scores_take_the_exact_max_pass():
     assert np.all(err <= bound)
 
 
+def test_fp8_exact_max_pass_in_later_units():
+    """The wide-score case over 2 heads x 157 query tiles (more than the
+    compute units): units past a workgroup's first take the exact-max pass
+    after their queries' codes were replaced by the next unit's during the
+    last key tile, and must load them again."""
+    say("fp8 wide score range, later persistent units")
+    qb, kb, vb = datagen.small_bf16(1, 2, 40000, 128, seed=63, Nkv=700)
+    q3 = datagen.bf16_bits(f32(qb) * 3.0)
+    kw = f32(kb).copy()
+    kw[:, :, 650:] *= 4.0
+    qc, qd, kc, kd = _oracle_inputs(q3, datagen.bf16_bits(kw))
+    O, L = _gpu_fp8(qc, qd, kc, kd, vb, scale=0.5)
+    rows = np.unique(np.concatenate([[0, 255, 256, 39999], datagen.sample_rows(40000, 40, 64)]))
+    Oref, Lref = oracle.attention_fp8(qc, kc, f32(vb), qd, kd, 0.5, rows=rows)
+    ri = torch.from_numpy(rows).cuda()
+    assert_bf16_close(to_f64(O[:, :, ri]), None, Oref, None, "fp8 wide, later units")
+    err = np.abs(to_f64(L[:, :, ri]) - Lref)
+    bound = 1e-3 + _score_error_bound(qc[:, :, rows], qd, kc, kd, 0.5)
+    assert np.all(err <= bound)
+
+
 def test_fp8_quant_then_attention_and_determinism():
     say("fp8 end to end on the GPU")
     qb, kb, vb = datagen.small_bf16(1, 3, 500, 128, seed=62, Nkv=400)
