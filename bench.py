@@ -14,8 +14,8 @@ attention FLOPs of the step (4 * 4*B*H*N^2*D) over the step's wall time.
 The fused leg runs the same step as four dit_attn_fwd_ulysses calls that
 read the token shards and write the token-shard output directly, with no
 exchange buffers; it is reported under "legs" beside the unfused step, both
-timed with events on the launch stream, three repetitions each, interleaved
-three times (medians).
+timed with events on the launch stream, four repetitions each, in six
+interleaved pairs whose order alternates (medians).
 
 The backward leg times dit_attn_bwd (dQ, dK, dV from the forward's O and
 LSE) on one head group; its TFLOP/s counts the five products of the
@@ -276,11 +276,18 @@ def main():
             for r in range(P):
                 dta.dit_attn_fwd_ulysses(*shards, r, out=fused_out, lse=lses[r])
 
-        # the same timer and repetition count for both forms, interleaved
+        # the same timer and repetition count for both forms, interleaved in
+        # alternating order (fused first in even pairs, unfused first in odd
+        # ones) so that a drift of the clock over the leg favours neither;
+        # medians of six pairs
         fused_v, unfused_v = [], []
-        for _ in range(3):
-            fused_v.append(time_it(fused_step, reps=3))
-            unfused_v.append(time_it(lambda: step(False), reps=3))
+        for i in range(6):
+            if i % 2 == 0:
+                fused_v.append(time_it(fused_step, reps=4))
+                unfused_v.append(time_it(lambda: step(False), reps=4))
+            else:
+                unfused_v.append(time_it(lambda: step(False), reps=4))
+                fused_v.append(time_it(fused_step, reps=4))
         fused_ms, unfused_ms = float(np.median(fused_v)), float(np.median(unfused_v))
         legs.update({"fused_step_ms": fused_ms,
                      "fused_step_TFLOPs": P * flops_launch / (fused_ms * 1e-3) / 1e12,
