@@ -31,13 +31,21 @@ EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_balanced",
             "dit_abi_version")
 
 _lib = None
+_lib_path = None
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libditattn.so and declare its prototypes (no device call is made)."""
-    global _lib
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libditattn.so (the in-tree build unless `path` names another) and
+    declare its prototypes (no device call is made).
+
+    One library per process: without a path, the one already loaded is
+    returned; a later call naming another path raises."""
+    global _lib, _lib_path
     if _lib is not None:
+        if path is not None and os.path.realpath(path) != _lib_path:
+            raise RuntimeError(f"{_lib_path} is already loaded; cannot switch to {path}")
         return _lib
+    path = LIB_PATH if path is None else path
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m diffusion_transformer_attention_amd.build`")
@@ -70,7 +78,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dit_strerror.argtypes = [ctypes.c_int]
     lib.dit_strerror.restype = ctypes.c_char_p
     lib.dit_abi_version.argtypes = []
-    _lib = lib
+    _lib, _lib_path = lib, os.path.realpath(path)
     return lib
 
 

@@ -30,6 +30,13 @@ def test_header_declares_the_boundary():
     assert _declared_functions() == sorted(dta.EXPORTED)
 
 
+def test_one_library_per_process(lib):
+    assert dta.load_library() is lib
+    assert dta.load_library(dta.LIB_PATH) is lib
+    with pytest.raises(RuntimeError, match="already loaded"):
+        dta.load_library(os.path.join(ROOT, "elsewhere", "libditattn.so"))
+
+
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
