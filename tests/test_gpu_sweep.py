@@ -12,7 +12,9 @@ more shapes (D = 128) go through the backward.  Every output element is
 compared with the fp64 oracle at the tolerances of the other parity tests.
 Twelve more shapes of more query tiles than compute units (several units per
 persistent workgroup, some ending in a half-height round) are compared on
-sampled rows.
+sampled rows, and 96 drawn cases take every forward entry point (plain,
+Ring partial in float32 and bf16, work-balanced, fused Ulysses, FP8) through
+launches of one to several rounds, also on sampled rows.
 """
 import sys
 
@@ -157,3 +159,64 @@ def test_sweep_multi_unit(i, B, H, Nq, Nkv, D):
         O, L = dta.dit_attn_fwd_block(q, k, v, out_dtype=od)
         assert_bf16_close(to_f64(O)[:, :, rows], to_f64(L)[:, :, rows], Oref, Lref,
                           f"multi-unit {i} {od}")
+
+
+# Every forward entry point on launches of one to several rounds of query
+# tiles: 96 cases drawn once from a fixed seed, each an entry point (plain
+# bf16, Ring partial with float32 or bf16 O, work-balanced, fused Ulysses with
+# P in {2, 4, 8}, FP8) on B in {1, 2}, H up to 24, N up to 9000 (keys ragged
+# and independent of the queries for the Ring partials), D in {32, 64, 128},
+# q scaled by 2.5 in half the bf16 cases (peaked softmax rows); 24 sampled
+# query rows per head compared with the oracle at the bf16 tolerances.
+def _entry_point_cases():
+    r = np.random.default_rng(2026)
+    kinds = ("plain", "block_f32", "block_bf16", "balanced", "ulysses", "fp8")
+    out = []
+    for i in range(96):
+        kind = kinds[i % len(kinds)]
+        B, H = int(r.integers(1, 3)), int(r.integers(1, 25))
+        D = int(r.choice([32, 64, 128], p=[0.2, 0.2, 0.6]))
+        Nq = int(r.integers(1, 9001))
+        Nkv = int(r.integers(1, 6001)) if kind.startswith("block") else Nq
+        P, qscale = 1, float(r.choice([1.0, 2.5]))
+        if kind == "ulysses":
+            P = int(r.choice([2, 4, 8]))
+            H = P * int(r.integers(1, 7))
+            Nq = Nkv = P * 64 * int(r.integers(1, 24))  # shards of whole key tiles
+        if kind == "fp8":
+            D, H, Nq, qscale = 128, min(H, 6), min(Nq, 4000), 1.0
+            Nkv = Nq
+        out.append((i, kind, B, H, Nq, Nkv, D, P, qscale))
+    return out
+
+
+@pytest.mark.parametrize("i,kind,B,H,Nq,Nkv,D,P,qscale", _entry_point_cases())
+def test_sweep_entry_points(i, kind, B, H, Nq, Nkv, D, P, qscale):
+    say(f"entry {i}: {kind} B{B} H{H} Nq{Nq} Nkv{Nkv} D{D} P{P} q x{qscale}")
+    qb, kb, vb = datagen.small_bf16(B, H, Nq, D, seed=7000 + i, Nkv=Nkv)
+    if qscale != 1.0:
+        qb = datagen.bf16_bits(datagen.bf16_to_f32(qb) * np.float32(qscale))
+    rows = datagen.sample_rows(Nq, min(Nq, 24), 8000 + i)
+    q, k, v = (bits_to_torch_bf16(x) for x in (qb, kb, vb))
+    if kind == "fp8":
+        qc, qd = oracle.quantize_fp8(datagen.bf16_to_f32(qb))
+        kc, kd = oracle.quantize_fp8(datagen.bf16_to_f32(kb))
+        O, L = dta.dit_attn_fwd_fp8(torch.from_numpy(qc).cuda(), torch.from_numpy(kc).cuda(), v,
+                                    torch.from_numpy(qd).cuda(), torch.from_numpy(kd).cuda())
+        Oref, Lref = oracle.attention_fp8(qc, kc, _f64(vb), qd, kd, rows=rows)
+    else:
+        Oref, Lref = oracle.attention_rows(_f64(qb), _f64(kb), _f64(vb), rows)
+        if kind == "plain":
+            O, L = dta.dit_attn_fwd(q, k, v)
+        elif kind == "block_f32":
+            O, L = dta.dit_attn_fwd_block(q, k, v, out_dtype=torch.float32)
+        elif kind == "block_bf16":
+            O, L = dta.dit_attn_fwd_block(q, k, v, out_dtype=torch.bfloat16)
+        elif kind == "balanced":
+            O, L = dta.dit_attn_fwd_balanced(q, k, v)
+        else:  # token shards in, token shards out; rank r holds heads [r H/P, (r+1) H/P)
+            shards = [torch.stack(t.chunk(P, dim=2)).contiguous() for t in (q, k, v)]
+            out = torch.empty_like(shards[0])
+            L = torch.cat([dta.dit_attn_fwd_ulysses(*shards, r, out=out)[1] for r in range(P)], dim=1)
+            O = torch.cat(list(out), dim=2)
+    assert_bf16_close(to_f64(O)[:, :, rows], to_f64(L)[:, :, rows], Oref, Lref, f"entry {i} {kind}")
