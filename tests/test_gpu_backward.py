@@ -156,3 +156,45 @@ def test_backward_ulysses_share_sampled_rows():
     _check_grad(to_f64(dk[:, :, ki]), rk, "dk", "ulysses share sampled keys")
     _check_grad(to_f64(dv[:, :, ki]), rv, "dv", "ulysses share sampled keys")
     assert torch.isfinite(dk).all() and torch.isfinite(dv).all()
+
+
+# Grids of tens to several hundred dK/dV and dQ workgroups: 12 cases drawn
+# once from a fixed seed, B in {1, 2}, H up to 12, independent ragged Nq and
+# Nkv up to 6000, an explicit scale half the time; dq and delta on 24 sampled
+# query rows, dk and dv on 24 sampled keys, per head.
+def _grid_cases():
+    r = np.random.default_rng(2027)
+    out = []
+    for i in range(12):
+        B, H = int(r.integers(1, 3)), int(r.integers(1, 13))
+        Nq, Nkv = int(r.integers(1, 6001)), int(r.integers(1, 6001))
+        scale = None if r.random() < 0.5 else float(r.uniform(0.03, 0.2))
+        out.append((i, B, H, Nq, Nkv, scale))
+    return out
+
+
+@pytest.mark.parametrize("i,B,H,Nq,Nkv,scale", _grid_cases())
+def test_backward_grids_sampled(i, B, H, Nq, Nkv, scale):
+    say(f"bwd grid {i}: B{B} H{H} Nq{Nq} Nkv{Nkv} scale {scale}")
+    qb, kb, vb, dob = _inputs(B, H, Nq, Nkv, seed=9100 + 2 * i)
+    _, (dq, dk, dv, delta) = _gpu_fwd_bwd(qb, kb, vb, dob, scale)
+    q64, k64, v64, do64 = f64(qb), f64(kb), f64(vb), f64(dob)
+    rows = datagen.sample_rows(Nq, min(Nq, 24), 9300 + i)
+    keys = datagen.sample_rows(Nkv, min(Nkv, 24), 9400 + i)
+    ri, ki = torch.from_numpy(rows).cuda(), torch.from_numpy(keys).cuda()
+    heads = [(b, h) for b in range(B) for h in range(H)]
+
+    def task(bh):
+        b, h = bh
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rq, rd = oracle.attention_backward_rows(q64[sl], k64[sl], v64[sl], do64[sl], rows, scale)
+        rk, rv = oracle.attention_backward_keys(q64[sl], k64[sl], v64[sl], do64[sl], keys, scale)
+        return rq, rd, rk, rv
+
+    res = run_threaded(task, heads)
+    pick = lambda j: np.stack([np.stack([res[b * H + h][j][0, 0] for h in range(H)]) for b in range(B)])
+    _check_grad(to_f64(dq[:, :, ri]), pick(0), "dq", f"grid {i} sampled rows")
+    rd = pick(1)
+    assert np.abs(to_f64(delta[:, :, ri]) - rd).max() <= 1e-2 * max(np.abs(rd).max(), 1e-30)
+    _check_grad(to_f64(dk[:, :, ki]), pick(2), "dk", f"grid {i} sampled keys")
+    _check_grad(to_f64(dv[:, :, ki]), pick(3), "dv", f"grid {i} sampled keys")
