@@ -57,6 +57,8 @@
 //    and share its L2 while they stream the same K/V.
 #include <math.h>
 
+#include <atomic>
+
 #include "launch.h"
 #include "rope.h"
 
@@ -1102,16 +1104,15 @@ void attn_fwd_joint_kernel(const __bf16* __restrict__ K, const __bf16* __restric
 // of the current device (the kernel holds a compute unit's LDS), or fewer
 // when there are fewer units.  The count is read once per device.
 unsigned persistent_grid(int64_t total) {
-  static int cus[64];
+  static std::atomic<int> cus[64];  // host threads may launch at once: each reads or sets its device's count
   int dev = 0;
   int n = 256;
   if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-    if (cus[dev] <= 0) {
-      int c = 0;
-      if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
-        cus[dev] = c;
-    }
-    if (cus[dev] > 0) n = cus[dev];
+    int c = cus[dev].load(std::memory_order_relaxed);
+    if (c <= 0 &&
+        hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
+      cus[dev].store(c, std::memory_order_relaxed);
+    if (c > 0) n = c;
   }
   return (unsigned)(total < n ? total : n);
 }
