@@ -30,8 +30,9 @@
  *    [B, H, N, D] (batch, head, token, channel); lse is float32 [B, H, N].
  *  - Every pointer is a DEVICE pointer on the current HIP device, allocated
  *    and owned by the caller.  The library allocates no memory and keeps no
- *    state between calls; calls are reentrant.  Outputs must not overlap
- *    inputs.
+ *    state between calls (the one exception, the static scratch array of
+ *    dit_attn_fwd_balanced_noalloc, is described there); calls are
+ *    reentrant.  Outputs must not overlap inputs.
  *  - Every call enqueues its kernels on `stream` (a hipStream_t; NULL = the
  *    legacy default stream) and returns without synchronising.
  *  - All arguments are validated on the host BEFORE any HIP call, so an
