@@ -214,7 +214,12 @@ int dit_attn_fwd_ulysses(const void* q, const void* k, const void* v, void* o, f
   if (H % P != 0 || N % P != 0) return DIT_EINVAL;
   if (dtype != DIT_BF16) return DIT_EUNSUPPORTED;
   if (!supported_head_dim(D)) return DIT_EUNSUPPORTED;
-  if ((N / P) % 64 != 0) return DIT_EUNSUPPORTED;  // a key tile must not straddle two shards
+  if ((N / P) % 64 != 0) {  // key tiles that span two shards (never three) ...
+    if (N / P < 64) return DIT_EUNSUPPORTED;
+    // ... reached through 32-bit offsets from one shard into the next
+    if (((int64_t)B * H - 1) * (N / P) * D * 2 + 64 * D * 2 >= ((int64_t)1 << 31))
+      return DIT_EUNSUPPORTED;
+  }
   if (!size_ok(B, H, N, D)) return DIT_ERANGE;
   if (B == 0 || H == 0 || N == 0) return DIT_OK;
   if (!q || !k || !v || !o) return DIT_EINVAL;

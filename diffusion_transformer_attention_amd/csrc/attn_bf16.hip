@@ -218,39 +218,74 @@ __device__ __forceinline__ void tile_barrier() {
 }
 
 // A stream of 64-key tiles of K (or V) in key order.  The keys of one (b, h)
-// lie in segments of kseg rows (a single segment for contiguous keys; one per
-// Ulysses token shard otherwise, whose length is then a multiple of the
-// tile), the end of one segment `jump` bytes before the start of the next.
-// p is the next tile's first row and left the rows from there to the end of
-// its segment: moving to the next tile is a few scalar operations, with no
-// division to find the segment.
+// lie in segments (a single segment for contiguous keys; one per Ulysses
+// token shard otherwise, each of at least a tile), the end of one segment
+// `jump` bytes before the start of the next.  p is the next tile's first row,
+// left the rows from there to the end of its segment and rem the rows from
+// there to the end of the stream: moving to the next tile is a few scalar
+// operations, with no division to find the segment.
 struct TileStream {
   const char* p;
   int left;
   int next;  // rows of each later segment
+  int rem;
 };
 
 // Stage the stream's next tile into LDS and advance.  Each load instruction
 // writes 1 KB contiguously (lane i -> bytes [16i, 16i+16)); voff[n] is the
 // byte offset, within a tile, of the global chunk whose swizzled position
-// that is (see piece_offsets).  The descriptor covers the tile's rows up to
-// the end of its segment, so rows past the end read as zero (its 32-bit size
-// is at most one tile).
+// that is (see piece_offsets; its row is voff[n] / ROWB).  The descriptor
+// covers the tile's rows up to the end of its segment, so rows past the end
+// of the stream read as zero (its 32-bit size is at most one tile).  A tile
+// that runs past the end of its segment into the next one (shards whose
+// length is not a multiple of the tile) takes its later rows from the next
+// segment through per-lane offsets.  `straddle` is a
+// compile-time constant after inlining (the pass context's str), false in
+// every launch whose segments are whole tiles, so their code has no such
+// branch.
 template <int ROWB, int PIECES>
 __device__ __forceinline__ void stage_next(TileStream& s, int64_t jump, lds_t* buf, int wave,
-                                           const int* voff) {
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)s.p, (short)0, min(s.left, kBN) * ROWB, 0x00020000);
+                                           const int* voff, bool straddle) {
+  constexpr int kLogRowB = __builtin_ctz(ROWB);
+  static_assert((1 << kLogRowB) == ROWB, "row bytes a power of two");
+  const int take = min(s.left, kBN);  // rows from the current segment
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)s.p, (short)0, take * ROWB, 0x00020000);
+  if (!straddle || take == kBN || s.rem <= take) {
 #pragma unroll
-  for (int n = 0; n < (PIECES + kWaves - 1) / kWaves; ++n) {
-    const int inst = n * kWaves + wave;
-    if (PIECES % kWaves != 0 && inst >= PIECES) break;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc, (__attribute__((address_space(3))) void*)(buf + inst * 1024), 16, voff[n], 0, 0, 0);
+    for (int n = 0; n < (PIECES + kWaves - 1) / kWaves; ++n) {
+      const int inst = n * kWaves + wave;
+      if (PIECES % kWaves != 0 && inst >= PIECES) break;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(buf + inst * 1024), 16, voff[n], 0, 0,
+          0);
+    }
+  } else {
+    // rows [take, min(kBN, rem)) from the next segment, which starts at
+    // p + take*ROWB + jump: one descriptor based at p that reaches that far
+    // (the launch keeps jump + a tile below 2^31 bytes), the lanes of those
+    // rows adding jump to their offset; rows past the end of the stream fall
+    // outside the record and read as zero
+    const __amdgpu_buffer_rsrc_t rsrc2 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)s.p, (short)0, (int)jump + min(kBN, s.rem) * ROWB, 0x00020000);
+#pragma unroll
+    for (int n = 0; n < (PIECES + kWaves - 1) / kWaves; ++n) {
+      const int inst = n * kWaves + wave;
+      if (PIECES % kWaves != 0 && inst >= PIECES) break;
+      const int off = voff[n] + ((voff[n] >> kLogRowB) >= take ? (int)jump : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc2, (__attribute__((address_space(3))) void*)(buf + inst * 1024), 16, off, 0, 0, 0);
+    }
   }
   s.p += kBN * ROWB;
   s.left -= kBN;
-  if (s.left == 0) {  // end of a segment: on to the next one
+  if (straddle) {
+    s.rem -= kBN;
+    if (s.left <= 0) {  // past the end of a segment: into the next one
+      s.p += jump;
+      s.left += s.next;
+    }
+  } else if (s.left == 0) {  // end of a segment: on to the next one
     s.p += jump;
     s.left = s.next;
   }
@@ -292,6 +327,7 @@ struct PassCtx {
   lds_t *v0, *v1, *v2;  // V stages
   int Nkv, ntiles, wave, lane, g;
   float c;
+  bool str;          // segments may end inside a tile (set from a template parameter)
   // Fragment offsets, each plus the LDS address of stage 0 and held in a
   // register the compiler cannot see through: a read of stage j is then
   // that register plus the constant (stage j - stage 0 + in-tile offset),
@@ -498,9 +534,9 @@ __device__ __forceinline__ void tile_trip(int t, Frags<D, F8, QB>& f, f32x4 (&S0
   tile_barrier<WAITN>();  // K_{t+1}, V_t landed; every wave is done with tile t-1
   const int p2 = PH >= 0 ? PH + 2 : -1, p1 = PH >= 0 ? PH + 1 : -1;
   if (t + 2 < x.ntiles)  // K tile t+2 is the K stream's next tile
-    stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kjump, KSTAGE(x, p2, t + 2), x.wave, x.kld);
+    stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kjump, KSTAGE(x, p2, t + 2), x.wave, x.kld, x.str);
   if (t + 1 < x.ntiles)  // V tile t+1 is the V stream's next tile
-    stage_next<Gm::ROWB, Gm::PIECES>(x.vs, x.vjump, VSTAGE(x, p1, t + 1), x.wave, x.vld);
+    stage_next<Gm::ROWB, Gm::PIECES>(x.vs, x.vjump, VSTAGE(x, p1, t + 1), x.wave, x.vld, x.str);
   const lds_t* kcur = KSTAGE(x, PH, t);
   const lds_t* knext = KSTAGE(x, p1, t + 1);
   const lds_t* vcur = VSTAGE(x, PH, t);
@@ -541,11 +577,11 @@ template <int D, bool F8>
 __device__ __forceinline__ void stage_first(PassCtx<D, F8>& x) {
   using Gm = Geo<D>;
   using QK = QKOps<D, F8>;
-  x.ks = TileStream{x.Kb, x.kseg, x.kseg};
-  x.vs = TileStream{x.Vb, x.vfirst, x.vnext};
-  stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kjump, x.k0, x.wave, x.kld);
-  if (x.ntiles > 1) stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kjump, x.k1, x.wave, x.kld);
-  stage_next<Gm::ROWB, Gm::PIECES>(x.vs, x.vjump, x.v0, x.wave, x.vld);
+  x.ks = TileStream{x.Kb, x.kseg, x.kseg, x.Nkv};
+  x.vs = TileStream{x.Vb, x.vfirst, x.vnext, x.Nkv};
+  stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kjump, x.k0, x.wave, x.kld, x.str);
+  if (x.ntiles > 1) stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kjump, x.k1, x.wave, x.kld, x.str);
+  stage_next<Gm::ROWB, Gm::PIECES>(x.vs, x.vjump, x.v0, x.wave, x.vld, x.str);
 }
 
 // One full pass over the keys whose first tiles stage_first has issued: the
@@ -613,10 +649,10 @@ __device__ __forceinline__ void exact_max_pass(Frags<D, F8, QB>& f, PassCtx<D, F
   float m[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) m[qb] = -INFINITY;
-  x.ks = TileStream{x.Kb, x.kseg, x.kseg};
+  x.ks = TileStream{x.Kb, x.kseg, x.kseg, x.Nkv};
   for (int t = 0; t < x.ntiles; ++t) {
     __syncthreads();  // every wave is done reading the stage
-    stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kjump, x.k0, x.wave, x.kld);
+    stage_next<QK::ROWB, QK::PIECES>(x.ks, x.kjump, x.k0, x.wave, x.kld, x.str);
     tile_barrier();  // landed
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -956,7 +992,8 @@ __device__ __forceinline__ void store_tile(const Frags<D, F8, QB>& f, const Tile
 // per-(b, h) factors qds[bh] * kds[bh]; else q and k are bf16 and qds, kds
 // are unused.  SPLIT: a key-split launch, total_tiles is then the number of
 // units.
-template <int D, bool OUT_F32, bool F8, bool SPLIT = false, bool JOINT = false, int QB = kQB>
+template <int D, bool OUT_F32, bool F8, bool SPLIT = false, bool JOINT = false, int QB = kQB,
+          bool STR = false>
 __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const void* __restrict__ K,
                                               const __bf16* __restrict__ V, void* __restrict__ Oout,
                                               float* __restrict__ LSE, int Nq, int Nkv,
@@ -988,6 +1025,7 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
   x.v0 = (lds_t*)v0s; x.v1 = (lds_t*)v1s; x.v2 = (lds_t*)v2s;
   x.wave = wave;
   x.lane = lane;
+  x.str = STR;
   x.anyw = (lds_i32*)any_words;
   x.g = g;
   piece_offsets<QK::ROWB, QK::PIECES>(x.kld, wave, lane, [](int r) { return QK::swz(r); });
@@ -1057,14 +1095,15 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
 }
 
 // QB = 1: half-height tiles (128 query rows), for the last partial round.
-template <int D, bool OUT_F32, int QB = kQB>
+// STR: Ulysses token shards whose length is not a multiple of the key tile.
+template <int D, bool OUT_F32, int QB = kQB, bool STR = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                           const __bf16* __restrict__ V, void* __restrict__ Oout,
                           float* __restrict__ LSE, int Nq, int Nkv, int n_qtiles, int total_tiles,
                           float c, Layout lay) {
-  attn_fwd_body<D, OUT_F32, false, false, false, QB>(Q, K, V, Oout, LSE, Nq, Nkv, n_qtiles,
-                                                     total_tiles, c, lay, nullptr, nullptr);
+  attn_fwd_body<D, OUT_F32, false, false, false, QB, STR>(Q, K, V, Oout, LSE, Nq, Nkv, n_qtiles,
+                                                          total_tiles, c, lay, nullptr, nullptr);
 }
 
 // Key-split partials (float32 O and LSE into the workspace).
@@ -1147,13 +1186,13 @@ FwdSplitRounds fwd_rounds(int Nq, int64_t heads) {
   return r;
 }
 
-template <int D, bool OUT_F32>
+template <int D, bool OUT_F32, bool STR = false>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float* lse, int Nq,
                     int Nkv, float c, const Layout& lay, hipStream_t stream) {
   const int64_t heads = (int64_t)lay.B * lay.hg;
   if (heads * ((Nq + kBM / 2 - 1) / (kBM / 2)) > 0x7fffffff) return hipErrorInvalidValue;
   const FwdSplitRounds r = fwd_rounds(Nq, heads);
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OUT_F32>), dim3(persistent_grid(r.full_units)),
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OUT_F32, kQB, STR>), dim3(persistent_grid(r.full_units)),
                      dim3(kThreads), 0, stream, static_cast<const __bf16*>(q),
                      static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), o, lse, Nq, Nkv,
                      r.n_full, (int)r.full_units, c, lay);
@@ -1161,7 +1200,7 @@ hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float*
   if (e != hipSuccess || r.half_units == 0) return e;
   Layout lh = lay;
   lh.tile0 = r.half_tile0;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OUT_F32, 1>), dim3(persistent_grid(r.half_units)),
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OUT_F32, 1, STR>), dim3(persistent_grid(r.half_units)),
                      dim3(kThreads), 0, stream, static_cast<const __bf16*>(q),
                      static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), o, lse, Nq, Nkv,
                      r.n_half, r.half_units, c, lh);
@@ -1290,7 +1329,14 @@ hipError_t launch_attn_bf16_ulysses(const void* q, const void* k, const void* v,
                                     float scale, hipStream_t stream) {
   const int ns = N / P, hg = H / P;
   const Layout lay{ns, ns, hg, H, r * hg, B, 0};
-  return launch_layout<false>(q, k, v, o, lse, N, N, D, scale, lay, stream);
+  if (ns % kBN == 0) return launch_layout<false>(q, k, v, o, lse, N, N, D, scale, lay, stream);
+  // shards that end inside a key tile: the kernels that stage such tiles from two shards
+  const float c = scale * 1.4426950408889634f;
+  switch (D) {
+    case 32: return launch_d<32, false, true>(q, k, v, o, lse, N, N, c, lay, stream);
+    case 64: return launch_d<64, false, true>(q, k, v, o, lse, N, N, c, lay, stream);
+    default: return launch_d<128, false, true>(q, k, v, o, lse, N, N, c, lay, stream);
+  }
 }
 
 }  // namespace ditattn

@@ -238,8 +238,10 @@ int dit_attn_merge(const float* o_parts, const float* lse_parts, int nblk,
  * The O and LSE values are bit-identical to the unfused sequence above (the
  * same kernel, with different addressing).  Requires H % P == 0 and
  * N % P == 0 (DIT_EINVAL otherwise, [PR] "Limitations") and, as a limit of
- * this implementation, (N/P) % 64 == 0 (DIT_EUNSUPPORTED otherwise; use the
- * unfused sequence).
+ * this implementation, when N/P is not a multiple of 64, N/P >= 64 and
+ * (B*H - 1)*(N/P)*D*2 + 128*D < 2^31 (DIT_EUNSUPPORTED otherwise; use the
+ * unfused sequence): a 64-key tile may then span two shards, never three,
+ * and the second is reached through a 32-bit offset from the first.
  */
 int dit_attn_fwd_ulysses(const void* q, const void* k, const void* v, void* o, float* lse,
                          int P, int r, int B, int H, int N, int D, float scale, int dtype,

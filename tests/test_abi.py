@@ -158,7 +158,9 @@ def test_fused_ulysses_validation(lib):
     assert u(P=0) == dta.DIT_EINVAL
     assert u(H=6) == dta.DIT_EINVAL          # heads not divisible by P
     assert u(N=514) == dta.DIT_EINVAL        # tokens not divisible by P
-    assert u(N=4 * 96) == dta.DIT_EUNSUPPORTED  # shard length 96 not a multiple of 64
+    assert u(N=4 * 48) == dta.DIT_EUNSUPPORTED  # shards shorter than a key tile and not whole tiles
+    # ragged shards more than 2^31 bytes apart (the next shard out of 32-bit offset reach)
+    assert u(H=4096, N=4 * 20001) == dta.DIT_EUNSUPPORTED
     assert u(dt=1) == dta.DIT_EUNSUPPORTED   # bf16 only
     assert u(D=80) == dta.DIT_EUNSUPPORTED
     assert u(scale=0.0) == dta.DIT_EINVAL

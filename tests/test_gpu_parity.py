@@ -299,6 +299,11 @@ def _shard(t, P):
     (4, 2, 8, 256, 64),      # shards of one 64-key tile: every tile starts a new shard
     (2, 1, 6, 384, 32),      # three heads per group, shards of 192 tokens (ragged query tiles)
     (1, 1, 3, 320, 128),     # P = 1: the shard is the whole sequence
+    (4, 1, 8, 4 * 100, 128),  # shards of 100 tokens: key tiles that span two shards
+    (2, 2, 6, 2 * 77, 64),    # shards of 77
+    (8, 1, 8, 8 * 65, 128),   # shards of 65: one key past a whole tile
+    (4, 1, 4, 4 * 70, 32),    # shards of 70 (ragged query and key tiles)
+    (3, 1, 3, 3 * 1001, 128),  # shards of 1001, three of them
 ])
 def test_fused_ulysses_small(P, B, H, N, D):
     """dit_attn_fwd_ulysses == seq2head -> dit_attn_fwd -> head2seq bit for bit,
@@ -326,6 +331,34 @@ def test_fused_ulysses_small(P, B, H, N, D):
     Oref, Lref = oracle.attention(f64(qb), f64(kb), f64(vb))
     O_full = torch.cat(list(out), dim=2)
     assert_bf16_close(to_f64(O_full), None, Oref, Lref, f"fused P{P} B{B} H{H} N{N} D{D}")
+
+
+def test_fused_ulysses_long_video_shards():
+    """The long-video sequence (75600 tokens) over P = 4 ranks: shards of 18900
+    tokens, which end inside key tiles.  Head groups 0 and 3 of 8 heads, each
+    bit-identical to the plain forward on the exchanged tensors and close to
+    the oracle on sampled rows."""
+    P, B, H, N, D = 4, 1, 8, 75600, 128
+    say("fused ulysses long video", P, B, H, N, D)
+    qb, kb, vb = datagen.small_bf16(B, H, N, D, seed=75600)
+    full = [bits_to_torch_bf16(x) for x in (qb, kb, vb)]
+    sh = [_shard(t, P) for t in full]
+    del full
+    groups = [dta.ulysses_seq2head(t) for t in sh]
+    out = torch.zeros_like(sh[0])
+    hg = H // P
+    rows = datagen.sample_rows(N, 64, 75601)
+    ri = torch.from_numpy(rows).cuda()
+    for r in (0, 3):
+        O_ref, L_ref = dta.dit_attn_fwd(groups[0][r], groups[1][r], groups[2][r])
+        _, L = dta.dit_attn_fwd_ulysses(*sh, r, out=out)
+        assert torch.equal(L, L_ref), f"LSE of group {r}"
+        heads = slice(r * hg, (r + 1) * hg)
+        O = torch.cat(list(out[:, :, heads]), dim=2)          # [B, hg, N, D]
+        assert torch.equal(O, O_ref), f"O of group {r}"
+        hs = range(r * hg, (r + 1) * hg)
+        Oref, Lref = oracle.attention_rows(f64(qb[:, hs]), f64(kb[:, hs]), f64(vb[:, hs]), rows)
+        assert_bf16_close(to_f64(O[:, :, ri]), to_f64(L[:, :, ri]), Oref, Lref, f"long video group {r}")
 
 
 def test_fused_ulysses_with_half_height_tail():

@@ -182,7 +182,7 @@ def _entry_point_cases():
         if kind == "ulysses":
             P = int(r.choice([2, 4, 8]))
             H = P * int(r.integers(1, 7))
-            Nq = Nkv = P * 64 * int(r.integers(1, 24))  # shards of whole key tiles
+            Nq = Nkv = P * int(r.integers(64, 1500))  # shards of at least a key tile
         if kind == "fp8":
             D, H, Nq, qscale = 128, min(H, 6), min(Nq, 4000), 1.0
             Nkv = Nq
