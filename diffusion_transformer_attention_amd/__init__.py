@@ -296,8 +296,8 @@ def dit_attn_fwd_ulysses(q, k, v, r, scale=None, out=None, lse=None, return_lse=
 
 
 def dit_attn_bwd(q, k, v, o, dout, lse, scale=None, dq=None, dk=None, dv=None, delta=None):
-    """Attention backward: q, o, dout bf16 [B,H,Nq,128]; k, v bf16 [B,H,Nkv,128];
-    lse float32 [B,H,Nq] from the forward.
+    """Attention backward: q, o, dout bf16 [B,H,Nq,D]; k, v bf16 [B,H,Nkv,D] (D = 32,
+    64 or 128); lse float32 [B,H,Nq] from the forward.
 
     Returns (dq [B,H,Nq,D], dk, dv [B,H,Nkv,D], delta [B,H,Nq]), all float32.
     """

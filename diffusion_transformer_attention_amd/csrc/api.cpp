@@ -235,7 +235,7 @@ int dit_attn_bwd(const void* q, const void* k, const void* v, const void* o, con
   if (B < 0 || H < 0 || Nq < 0 || Nkv < 0 || D <= 0) return DIT_EINVAL;
   if (!(isfinite(scale) && scale > 0.0f)) return DIT_EINVAL;
   if (dtype != DIT_BF16 || grad_dtype != DIT_F32) return DIT_EUNSUPPORTED;
-  if (D != 128) return DIT_EUNSUPPORTED;
+  if (D != 32 && D != 64 && D != 128) return DIT_EUNSUPPORTED;
   if (!size_ok(B, H, Nq, D) || !size_ok(B, H, Nkv, D)) return DIT_ERANGE;
   if (B == 0 || H == 0) return DIT_OK;
   if (Nq == 0 || Nkv == 0) return DIT_EINVAL;
@@ -245,7 +245,7 @@ int dit_attn_bwd(const void* q, const void* k, const void* v, const void* o, con
   if (!aligned(lse, 4) || !aligned(delta, 4)) return DIT_EALIGN;
   return map_launch(ditattn::launch_attn_bwd_bf16(
       q, k, v, o, dout, lse, delta, static_cast<float*>(dq), static_cast<float*>(dk),
-      static_cast<float*>(dv), B, H, Nq, Nkv, scale, static_cast<hipStream_t>(stream)));
+      static_cast<float*>(dv), B, H, Nq, Nkv, D, scale, static_cast<hipStream_t>(stream)));
 }
 
 int dit_rope_pack(const void* x_txt, const void* x_img, const float* cos_txt,

@@ -38,11 +38,12 @@
 //    each dP^T chain starting at -delta of the lane's query, so that it ends
 //    at dP - delta; software-pipelined so that the next step's products
 //    overlap this step's softmax and dQ^T products.
-// The tiles' 16-byte chunks are XOR-swizzled with 2(row & 7), the swizzle of
-// the forward kernel's V tile, so both read patterns are bank-conflict-free:
-// ds_read_b128 of 16 rows at one column, and ds_read_b64_tr_b16 of 8 rows x 2
-// chunks per 32 lanes.
-// Head dimension 128 only.
+// The tiles' 16-byte chunks are XOR-swizzled per row (swz), so that both read
+// patterns, ds_read_b128 of 16 rows at one column and ds_read_b64_tr_b16 of 8
+// rows x 2 chunks per 32 lanes, are bank-conflict-free (head dimension 32:
+// nearly so).
+// Head dimensions 32, 64 and 128; every kernel is a template on it, and a
+// smaller head dimension keeps the same loops with fewer channel steps.
 #include <math.h>
 
 #include "launch.h"
@@ -62,25 +63,40 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) float lds_f32;
 
-constexpr int D = 128;
-constexpr int ROWB = 2 * D;        // bytes per row
-constexpr int CPR = D / 8;         // 16-byte chunks per row
-constexpr int KS = D / 32;         // 32-wide k-steps over channels
-constexpr int DB = D / 16;         // 16-channel blocks
 constexpr int TR = 64;             // rows per LDS tile
-constexpr int TILE = TR * ROWB;    // 16 KB
-constexpr int PIECES = TILE / 1024;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int KEYS_PER_WG = 16 * kWaves;     // dkdv_kernel
 constexpr int QUERIES_PER_WG = 32 * kWaves;  // dq_kernel
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Chunk swizzle of the LDS tiles.  With it neither the row-major fragment
-// reads (ds_read_b128) nor the transposing reads (ds_read_b64_tr_b16) of
-// tr_frag meet a bank conflict; both patterns were counted on gfx950 with
-// SQ_LDS_BANK_CONFLICT.
-__device__ __forceinline__ int swz(int row) { return 2 * (row & 7); }
+// Sizes that follow from the head dimension D.
+template <int D_>
+struct G {
+  static constexpr int D = D_;
+  static constexpr int ROWB = 2 * D;                          // bytes per row
+  static constexpr int CPR = D / 8;                           // 16-byte chunks per row
+  static constexpr int KS = D / 32;                           // 32-wide k-steps over channels
+  static constexpr int DB = D / 16;                           // 16-channel blocks
+  static constexpr int TILE = TR * ROWB;                      // bytes per LDS tile
+  static constexpr int PIECES = TILE / 1024;                  // 1 KB load instructions per tile
+  static constexpr int NLD = (PIECES + kWaves - 1) / kWaves;  // of them per wave
+};
+
+// Chunk swizzle of the LDS tiles: LDS slot pc of row r holds chunk
+// pc ^ swz(r).  With D = 128 (one row per 256-byte bank sweep) and D = 64
+// (two) neither the row-major fragment reads (ds_read_b128) nor the
+// transposing reads (ds_read_b64_tr_b16) of tr_frag meet a bank conflict;
+// the D = 128 patterns were counted on gfx950 with SQ_LDS_BANK_CONFLICT, the
+// others chosen on the bank map fitted to those counts.  With D = 32 (four
+// rows per sweep, four chunks) no swizzle clears every pattern; this one
+// leaves the fewest.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if (D == 128) return 2 * (row & 7);
+  if (D == 64) return row & 6;
+  return ((row >> 1) & 2) | ((row >> 3) & 1);
+}
 
 __device__ __forceinline__ int remap_xcd(int i, int total) {
   const int x = i & 7, j = i >> 3;
@@ -104,15 +120,21 @@ __device__ __forceinline__ void tile_barrier() {
 // tile: LDS slot pc of row r holds chunk pc ^ swz(r).  The descriptor ends at
 // row min(nrows, r0 + TR), so rows past the end arrive as zeros (and its
 // 32-bit size stays within one tile).
-__device__ __forceinline__ void stage_rows(const __bf16* G, int r0, int nrows, lds_t* buf,
+// Each load instruction writes 1 KB; a tile smaller than kWaves KB leaves
+// the last waves idle.
+template <int D>
+__device__ __forceinline__ void stage_rows(const __bf16* M, int r0, int nrows, lds_t* buf,
                                            int wave, const int* voff) {
+  using g = G<D>;
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(G + (int64_t)r0 * D), (short)0, min(nrows - r0, TR) * ROWB, 0x00020000);
+      (void*)(M + (int64_t)r0 * D), (short)0, min(nrows - r0, TR) * g::ROWB, 0x00020000);
 #pragma unroll
-  for (int n = 0; n < PIECES / kWaves; ++n)
+  for (int n = 0; n < g::NLD; ++n) {
+    const int inst = n * kWaves + wave;
+    if (g::PIECES % kWaves != 0 && inst >= g::PIECES) break;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc, (__attribute__((address_space(3))) void*)(buf + (n * kWaves + wave) * 1024), 16, voff[n],
-        0, 0, 0);
+        rsrc, (__attribute__((address_space(3))) void*)(buf + inst * 1024), 16, voff[n], 0, 0, 0);
+  }
 }
 
 // Stage 64 floats (rows [r0, r0 + 64) of a row vector) into LDS, lane l -> row r0 + l.
@@ -123,47 +145,54 @@ __device__ __forceinline__ void stage_vec(const float* G, int r0, int nrows, lds
                                            4 * lane, 0, 0, 0);
 }
 
+template <int D>
 __device__ __forceinline__ void piece_offsets(int* voff, int wave, int lane) {
+  using g = G<D>;
 #pragma unroll
-  for (int n = 0; n < PIECES / kWaves; ++n) {
+  for (int n = 0; n < g::NLD; ++n) {
     const int p = (n * kWaves + wave) * 64 + lane;
-    const int row = p / CPR, pc = p % CPR;
-    voff[n] = row * ROWB + ((pc ^ swz(row)) << 4);
+    const int row = p / g::CPR, pc = p % g::CPR;
+    voff[n] = row * g::ROWB + ((pc ^ swz<D>(row)) << 4);
   }
 }
 
 // Byte offset, within a 16-row block, of the A-operand fragment of k-step ks
 // for a row-major tile: lane (c16, g) reads row c16, chunk 4ks + g.
+template <int D>
 __device__ __forceinline__ int a_off(int c16, int g, int ks) {
-  return c16 * ROWB + (((4 * ks + g) ^ swz(c16)) << 4);
+  return c16 * G<D>::ROWB + (((4 * ks + g) ^ swz<D>(c16)) << 4);
 }
 
 // Transposing read base: lane t of 16-lane group g reads row r = 4g + t/4,
 // channels 16db + 4(t%4) .. +3 (the second read is 16 rows further, same
-// swizzle), i.e. chunk 2db + a, a = (t%4)/2.  (2db + a) ^ swz(r) =
-// 2(db ^ (r & 7)) + a, so the channel block only flips bits 5-7 of the
-// in-row offset: block db is at trb ^ (32 db).
+// swizzle), i.e. chunk 2db + a, a = (t%4)/2.  Its in-row byte offset is
+// 16((2db + a) ^ swz(r)) = 32db ^ 16a ^ 16swz(r), so the channel block only
+// flips bits 5 and up of it: block db is at trb ^ (32 db).
+template <int D>
 __device__ __forceinline__ int tr_base(int lane) {
   const int t = lane & 15, g = lane >> 4;
   const int r = 4 * g + (t >> 2);
   const int a = (t & 3) >> 1;
-  return r * ROWB + 32 * (r & 7) + 16 * a + 8 * (t & 1);
+  return r * G<D>::ROWB + ((16 * a) ^ (16 * swz<D>(r))) + 8 * (t & 1);
 }
 
+template <int D>
 __device__ __forceinline__ bf16x8 tr_frag(const lds_t* base) {
   const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)base));
   const bf16x4 hi = __builtin_bit_cast(
-      bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 16 * ROWB)));
+      bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 16 * G<D>::ROWB)));
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
 // ---------------------------------------------------------------- delta
-// One 16-lane group per row: lane i holds channels 8i .. 8i+7.
+// One group of D/8 lanes per row: lane i holds channels 8i .. 8i+7.
+template <int D>
 __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ O,
                                                     const __bf16* __restrict__ dO,
                                                     float* __restrict__ delta, int64_t rows) {
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int i = threadIdx.x & 15;
+  constexpr int LPR = D / 8;  // lanes per row
+  const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + (threadIdx.x / LPR);
+  const int i = threadIdx.x % LPR;
   float s = 0.f;
   if (row < rows) {
     const bf16x8 o = *reinterpret_cast<const bf16x8*>(O + row * D + 8 * i);
@@ -171,10 +200,8 @@ __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ O
 #pragma unroll
     for (int j = 0; j < 8; ++j) s = fmaf((float)o[j], (float)d[j], s);
   }
-  s += __shfl_xor(s, 8, 16);
-  s += __shfl_xor(s, 4, 16);
-  s += __shfl_xor(s, 2, 16);
-  s += __shfl_xor(s, 1, 16);
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m /= 2) s += __shfl_xor(s, m, LPR);
   if (row < rows && i == 0) delta[row] = s;
 }
 
@@ -193,7 +220,9 @@ constexpr int kQStages = 4;
 // register plus a constant below 64 KB that the instruction encodes.  The
 // reads keep their stage array as their object, so the compiler still knows
 // they do not touch the stage being loaded.
+template <int D>
 struct KVCtx {
+  static constexpr int KS = G<D>::KS, DB = G<D>::DB;
   bf16x8 k[KS], v[KS];  // B operands: lane holds key c16, channels 32ks + 8g .. +7
   f32x4 dk[DB], dv[DB]; // -dK^T, dV^T blocks: lane holds channels 16db + 4g + r of key c16
   int qa[KS], oa[KS];   // row-major fragment (ks) of the Q / dO stages
@@ -204,7 +233,7 @@ struct KVCtx {
   float c;
   const __bf16 *Qb, *dOb;
   const float *Lb, *Db;
-  int voff[PIECES / kWaves];
+  int voff[G<D>::NLD];
   // stages (separate scalars: never an indexed array); a dO stage holds the
   // tile, then the tile's 64 LSE values, then its 64 delta values
   lds_t *q0, *q1, *q2, *q3, *o0, *o1, *o2, *o3;
@@ -220,20 +249,22 @@ __device__ __forceinline__ int stage_at(int PH, int t, int k) {
 }
 #define QST(x, i) pick4((x).q0, (x).q1, (x).q2, (x).q3, (i))
 #define OST(x, i) pick4((x).o0, (x).o1, (x).o2, (x).o3, (i))
-#define LST(x, i) reinterpret_cast<lds_f32*>(OST(x, i) + TILE)
-#define DST(x, i) reinterpret_cast<lds_f32*>(OST(x, i) + TILE + 4 * TR)
+#define LST(x, i) reinterpret_cast<lds_f32*>(OST(x, i) + G<D>::TILE)
+#define DST(x, i) reinterpret_cast<lds_f32*>(OST(x, i) + G<D>::TILE + 4 * TR)
 
 // S = Q K^T and delta - dP = delta + dO (-V)^T of one 32-query step,
 // unpipelined (first step).
-__device__ __forceinline__ void sdp_step(const KVCtx& x, f32x4 (&S)[2], f32x4 (&dP)[2], const lds_t* qs,
-                                         const lds_t* os, const lds_f32* dt) {
+template <int D>
+__device__ __forceinline__ void sdp_step(const KVCtx<D>& x, f32x4 (&S)[2], f32x4 (&dP)[2],
+                                         const lds_t* qs, const lds_t* os, const lds_f32* dt) {
+  constexpr int ROWB = G<D>::ROWB;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     S[qb] = f32x4{};
     dP[qb] = *reinterpret_cast<const lds_f32x4*>(dt + 16 * qb + 4 * x.g);
   }
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
+  for (int ks = 0; ks < G<D>::KS; ++ks)
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const bf16x8 aq = *reinterpret_cast<const lds_bf16x8*>(qs - x.qbase + 16 * qb * ROWB + x.qa[ks]);
@@ -244,31 +275,38 @@ __device__ __forceinline__ void sdp_step(const KVCtx& x, f32x4 (&S)[2], f32x4 (&
 }
 
 // dV^T += dO^T P and -dK^T += Q^T (-dS) of one step, unpipelined (last step).
-__device__ __forceinline__ void dvdk_step(KVCtx& x, bf16x8 pp, bf16x8 dsp, const lds_t* qs,
+template <int D>
+__device__ __forceinline__ void dvdk_step(KVCtx<D>& x, bf16x8 pp, bf16x8 dsp, const lds_t* qs,
                                           const lds_t* os) {
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    x.dv[db] = mfma16(tr_frag(os - x.obase + x.ot[db]), pp, x.dv[db]);
-    x.dk[db] = mfma16(tr_frag(qs - x.qbase + x.qt[db]), dsp, x.dk[db]);
+  for (int db = 0; db < G<D>::DB; ++db) {
+    x.dv[db] = mfma16(tr_frag<D>(os - x.obase + x.ot[db]), pp, x.dv[db]);
+    x.dk[db] = mfma16(tr_frag<D>(qs - x.qbase + x.qt[db]), dsp, x.dk[db]);
   }
 }
 
 // One slot: S / delta - dP of the next step into Sn / dPn (rows at qn / on,
 // delta at dtn), dV / -dK of the previous step from Pp / dSp (rows at qp /
 // op), P / -dS of this step from Sc / dPc into Pc / dSc (LSE at lt, query
-// index q0 of the step's row 0).  Group gi runs the S / dP MFMA gi (index i: ks = i / 4,
-// qb = (i / 2) % 2, S if i is even else dP), the dV / dK MFMA gi (db = gi / 2,
-// dV if gi is even else dK), and, in odd groups, score (qb, r) = ((gi-1)/8,
-// ((gi-1)/2) % 4) of this step; it issues the LDS reads that group gi + 1 needs.
-// The B operands pack query 4g + j (j < 4) and 16 + 4g + j - 4 (j >= 4) of
-// the step: k index 8g + j of v_mfma_f32_16x16x32_bf16.
-template <bool MASK>
-__device__ __forceinline__ void dkdv_slot(KVCtx& x, const f32x4 (&Sc)[2], const f32x4 (&dPc)[2],
+// index q0 of the step's row 0).  There are NG = D/8 groups, as many as S / dP
+// MFMAs and as dV / dK MFMAs.  Group gi runs the S / dP MFMA gi (index i: ks =
+// i / 4, qb = (i / 2) % 2, S if i is even else dP), the dV / dK MFMA gi (db =
+// gi / 2, dV if gi is even else dK) and a share of this step's 8 scores e
+// (qb = e / 4, r = e % 4): with 16 groups score gi / 2 in odd groups, with 8
+// score gi, with 4 scores 2gi and 2gi + 1; it issues the LDS reads that
+// group gi + 1 needs.  The B operands pack query 4g + j (j < 4) and
+// 16 + 4g + j - 4 (j >= 4) of the step: k index 8g + j of
+// v_mfma_f32_16x16x32_bf16.
+template <int D, bool MASK>
+__device__ __forceinline__ void dkdv_slot(KVCtx<D>& x, const f32x4 (&Sc)[2], const f32x4 (&dPc)[2],
                                           f32x4 (&Sn)[2], f32x4 (&dPn)[2], bf16x8 Pp, bf16x8 dSp,
                                           bf16x8& Pc, bf16x8& dSc, const lds_t* qn, const lds_t* on,
                                           const lds_t* qp, const lds_t* op, const lds_f32* lt,
                                           const lds_f32* dtn, int q0) {
-  constexpr int NG = 16;
+  constexpr int ROWB = G<D>::ROWB;
+  constexpr int NG = G<D>::CPR;
+  constexpr int SG = NG > 8 ? NG / 8 : 1;   // groups per scoring group
+  constexpr int EPG = NG < 8 ? 8 / NG : 1;  // scores per scoring group
   bf16x8 fa[NG], fc[NG];
   auto load_a = [&](int i) {
     const int ks = i / 4, qb = (i / 2) % 2;
@@ -277,7 +315,7 @@ __device__ __forceinline__ void dkdv_slot(KVCtx& x, const f32x4 (&Sc)[2], const 
   };
   auto load_c = [&](int j) {
     const int db = j / 2;
-    fc[j] = (j & 1) ? tr_frag(qp - x.qbase + x.qt[db]) : tr_frag(op - x.obase + x.ot[db]);
+    fc[j] = (j & 1) ? tr_frag<D>(qp - x.qbase + x.qt[db]) : tr_frag<D>(op - x.obase + x.ot[db]);
   };
   // LSE of this step's rows 16qb + 4g + r; the next step's dP chains start
   // at its delta.
@@ -312,33 +350,37 @@ __device__ __forceinline__ void dkdv_slot(KVCtx& x, const f32x4 (&Sc)[2], const 
       else
         x.dv[db] = mfma16(fc[gi], Pp, x.dv[db]);
     }
-    if (gi & 1) {
-      const int e = gi / 2, qb = e / 4, r = e % 4;
-      float sv = Sc[qb][r];
-      // Pin the element's work to its group (see the forward kernel).
-      asm volatile("" : "+v"(sv));
-      float pv = __builtin_amdgcn_exp2f(fmaf(sv, x.c, -lse[qb][r] * kLog2e));
-      if (MASK && q0 + 16 * qb + 4 * x.g + r >= x.Nq) pv = 0.f;
-      p[e] = pv;
-      ds[e] = pv * dPc[qb][r];  // -dS = p (delta - dP)
-      if (e & 1) {
-        bf16x2 pk = {(__bf16)p[e - 1], (__bf16)p[e]};
-        bf16x2 dk = {(__bf16)ds[e - 1], (__bf16)ds[e]};
-        asm volatile("" : "+v"(pk), "+v"(dk));
-        Pc[e - 1] = pk[0];
-        Pc[e] = pk[1];
-        dSc[e - 1] = dk[0];
-        dSc[e] = dk[1];
+    if (gi % SG == SG - 1) {
+#pragma unroll
+      for (int u = 0; u < EPG; ++u) {
+        const int e = (gi / SG) * EPG + u, qb = e / 4, r = e % 4;
+        float sv = Sc[qb][r];
+        // Pin the element's work to its group (see the forward kernel).
+        asm volatile("" : "+v"(sv));
+        float pv = __builtin_amdgcn_exp2f(fmaf(sv, x.c, -lse[qb][r] * kLog2e));
+        if (MASK && q0 + 16 * qb + 4 * x.g + r >= x.Nq) pv = 0.f;
+        p[e] = pv;
+        ds[e] = pv * dPc[qb][r];  // -dS = p (delta - dP)
+        if (e & 1) {
+          bf16x2 pk = {(__bf16)p[e - 1], (__bf16)p[e]};
+          bf16x2 dk = {(__bf16)ds[e - 1], (__bf16)ds[e]};
+          asm volatile("" : "+v"(pk), "+v"(dk));
+          Pc[e - 1] = pk[0];
+          Pc[e] = pk[1];
+          dSc[e - 1] = dk[0];
+          dSc[e] = dk[1];
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-__device__ __forceinline__ void stage_q_tile(const KVCtx& x, int t, int st) {
+template <int D>
+__device__ __forceinline__ void stage_q_tile(const KVCtx<D>& x, int t, int st) {
   const int r0 = t * TR;
-  stage_rows(x.Qb, r0, x.Nq, QST(x, st), x.wave, x.voff);
-  stage_rows(x.dOb, r0, x.Nq, OST(x, st), x.wave, x.voff);
+  stage_rows<D>(x.Qb, r0, x.Nq, QST(x, st), x.wave, x.voff);
+  stage_rows<D>(x.dOb, r0, x.Nq, OST(x, st), x.wave, x.voff);
   if (x.wave == 0) stage_vec(x.Lb, r0, x.Nq, LST(x, st), x.lane);
   if (x.wave == 1) stage_vec(x.Db, r0, x.Nq, DST(x, st), x.lane);
 }
@@ -346,29 +388,32 @@ __device__ __forceinline__ void stage_q_tile(const KVCtx& x, int t, int st) {
 // Query tile t = steps 2t and 2t+1.  On entry S0 / dP0 hold step 2t and
 // Pa / dSa hold step 2t-1; on exit S0 / dP0 hold step 2t+2 (past the last
 // tile: unused) and Pa / dSa hold step 2t+1.
-template <int PH, bool MASK>
-__device__ __forceinline__ void dkdv_tile(KVCtx& x, int t, f32x4 (&S0)[2], f32x4 (&dP0)[2],
+template <int D, int PH, bool MASK>
+__device__ __forceinline__ void dkdv_tile(KVCtx<D>& x, int t, f32x4 (&S0)[2], f32x4 (&dP0)[2],
                                           f32x4 (&S1)[2], f32x4 (&dP1)[2], bf16x8& Pa, bf16x8& dSa,
                                           bf16x8& Pb, bf16x8& dSb) {
+  constexpr int ROWB = G<D>::ROWB;
   tile_barrier();  // tile t+1 landed; every wave is done with tile t-2
   const int sc = stage_at(PH, t, 0), sn = stage_at(PH, t, 1), sp = stage_at(PH, t, 3);
-  if (t + 2 < x.ntiles) stage_q_tile(x, t + 2, stage_at(PH, t, 2));
+  if (t + 2 < x.ntiles) stage_q_tile<D>(x, t + 2, stage_at(PH, t, 2));
   const lds_t* qc = QST(x, sc);
   const lds_t* oc = OST(x, sc);
   const lds_f32* lt = LST(x, sc);
   const lds_f32* dt = DST(x, sc);
-  dkdv_slot<MASK>(x, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb, qc + 32 * ROWB, oc + 32 * ROWB,
-                  QST(x, sp) + 32 * ROWB, OST(x, sp) + 32 * ROWB, lt, dt + 32, t * TR);
-  dkdv_slot<MASK>(x, S1, dP1, S0, dP0, Pb, dSb, Pa, dSa, QST(x, sn), OST(x, sn), qc, oc, lt + 32,
-                  DST(x, sn), t * TR + 32);
+  dkdv_slot<D, MASK>(x, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb, qc + 32 * ROWB, oc + 32 * ROWB,
+                     QST(x, sp) + 32 * ROWB, OST(x, sp) + 32 * ROWB, lt, dt + 32, t * TR);
+  dkdv_slot<D, MASK>(x, S1, dP1, S0, dP0, Pb, dSb, Pa, dSa, QST(x, sn), OST(x, sn), qc, oc, lt + 32,
+                     DST(x, sn), t * TR + 32);
 }
 
+template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                  const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                  const float* __restrict__ LSE, const float* __restrict__ Dl,
                  float* __restrict__ dK, float* __restrict__ dV, int Nq, int Nkv, int n_ktiles,
                  int total, float c, float scale) {
+  constexpr int TILE = G<D>::TILE, ROWB = G<D>::ROWB, KS = G<D>::KS, DB = G<D>::DB;
   __shared__ __attribute__((aligned(1024))) char q0s[TILE];
   __shared__ __attribute__((aligned(1024))) char q1s[TILE];
   __shared__ __attribute__((aligned(1024))) char q2s[TILE];
@@ -388,7 +433,7 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15, g = lane >> 4;
 
-  KVCtx x;
+  KVCtx<D> x;
   x.g = g;
   x.lane = lane;
   x.wave = wave;
@@ -413,11 +458,11 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         bf16x8, __builtin_bit_cast(u32x4, *reinterpret_cast<const bf16x8*>(
                                               V + ((int64_t)bh * Nkv + krow) * D + 32 * ks + 8 * g)) ^
                     u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u});
-    x.qa[ks] = a_off(c16, g, ks) + x.qbase;
-    x.oa[ks] = a_off(c16, g, ks) + x.obase;
+    x.qa[ks] = a_off<D>(c16, g, ks) + x.qbase;
+    x.oa[ks] = a_off<D>(c16, g, ks) + x.obase;
     asm volatile("" : "+v"(x.qa[ks]), "+v"(x.oa[ks]));
   }
-  const int trb = tr_base(lane);
+  const int trb = tr_base<D>(lane);
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     x.dk[db] = f32x4{};
@@ -426,7 +471,7 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     x.ot[db] = (trb ^ (32 * db)) + x.obase;
     asm volatile("" : "+v"(x.qt[db]), "+v"(x.ot[db]));
   }
-  piece_offsets(x.voff, wave, lane);
+  piece_offsets<D>(x.voff, wave, lane);
 
   // The first slot multiplies P = dS = 0 by the stage of tile -1 (stage 3):
   // zero it so no stale Inf/NaN bit pattern can turn 0 * x into NaN.
@@ -434,8 +479,8 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     reinterpret_cast<lds_f32x4*>(x.q3)[i] = f32x4{};
     reinterpret_cast<lds_f32x4*>(x.o3)[i] = f32x4{};
   }
-  stage_q_tile(x, 0, 0);
-  if (x.ntiles > 1) stage_q_tile(x, 1, 1);
+  stage_q_tile<D>(x, 0, 0);
+  if (x.ntiles > 1) stage_q_tile<D>(x, 1, 1);
   tile_barrier();  // tiles 0 and 1 landed, stage 3 zeroed
   f32x4 S0[2], dP0[2], S1[2], dP1[2];
   bf16x8 Pa = bf16x8{}, dSa = bf16x8{}, Pb, dSb;
@@ -444,16 +489,16 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int nfull = partial ? x.ntiles - 1 : x.ntiles;
   int t = 0;
   for (; t + kQStages <= nfull; t += kQStages) {
-    dkdv_tile<0, false>(x, t, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb);
-    dkdv_tile<1, false>(x, t + 1, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb);
-    dkdv_tile<2, false>(x, t + 2, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb);
-    dkdv_tile<3, false>(x, t + 3, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb);
+    dkdv_tile<D, 0, false>(x, t, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb);
+    dkdv_tile<D, 1, false>(x, t + 1, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb);
+    dkdv_tile<D, 2, false>(x, t + 2, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb);
+    dkdv_tile<D, 3, false>(x, t + 3, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb);
   }
-  for (; t < nfull; ++t) dkdv_tile<-1, false>(x, t, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb);
-  if (partial) dkdv_tile<-1, true>(x, t, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb);
+  for (; t < nfull; ++t) dkdv_tile<D, -1, false>(x, t, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb);
+  if (partial) dkdv_tile<D, -1, true>(x, t, S0, dP0, S1, dP1, Pa, dSa, Pb, dSb);
   // dV / dK of the last step (rows 32 .. 63 of the last tile).
   const int sl = (x.ntiles - 1) % kQStages;
-  dvdk_step(x, Pa, dSa, QST(x, sl) + 32 * ROWB, OST(x, sl) + 32 * ROWB);
+  dvdk_step<D>(x, Pa, dSa, QST(x, sl) + 32 * ROWB, OST(x, sl) + 32 * ROWB);
 
   if (key < Nkv) {
     const int64_t base = ((int64_t)bh * Nkv + key) * D;
@@ -475,7 +520,9 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 // the slot before its first step (S^T) to the slot of its last (dQ^T), a V
 // tile only in the two slots before its steps: three stages each, tile t+2
 // loaded while t and t+1 are read.
+template <int D>
 struct QCtx {
+  static constexpr int KS = G<D>::KS, DB = G<D>::DB;
   bf16x8 q[2][KS], o[2][KS];  // B operands: lane holds query c16 of block qb, channels 32ks + 8g ..
   f32x4 dq[2][DB];            // dQ^T blocks: lane holds channels 16db + 4g + r of its query
   float lse2[2];
@@ -486,7 +533,7 @@ struct QCtx {
   int g, lane, wave, Nkv, ntiles;
   float c;
   const __bf16 *Kb, *Vb;
-  int voff[PIECES / kWaves];
+  int voff[G<D>::NLD];
   lds_t *k0, *k1, *k2, *v0, *v1, *v2;  // stages (separate scalars: never an indexed array)
 };
 
@@ -499,8 +546,10 @@ __device__ __forceinline__ T pick3(T a0, T a1, T a2, int i) { return i == 0 ? a0
 
 // S^T and dP^T of one 32-key step, unpipelined (first step): keys at rows
 // [0, 32) of kst / vst.
-__device__ __forceinline__ void sdpt_step(const QCtx& x, f32x4 (&S)[2][2], f32x4 (&dP)[2][2],
+template <int D>
+__device__ __forceinline__ void sdpt_step(const QCtx<D>& x, f32x4 (&S)[2][2], f32x4 (&dP)[2][2],
                                           const lds_t* kst, const lds_t* vst) {
+  constexpr int ROWB = G<D>::ROWB;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -511,7 +560,7 @@ __device__ __forceinline__ void sdpt_step(const QCtx& x, f32x4 (&S)[2][2], f32x4
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < G<D>::KS; ++ks) {
       const bf16x8 ak = *reinterpret_cast<const lds_bf16x8*>(kst - x.kbase + 16 * kb * ROWB + x.ka[ks]);
       const bf16x8 av = *reinterpret_cast<const lds_bf16x8*>(vst - x.vbase + 16 * kb * ROWB + x.va[ks]);
 #pragma unroll
@@ -524,24 +573,26 @@ __device__ __forceinline__ void sdpt_step(const QCtx& x, f32x4 (&S)[2][2], f32x4
 
 // One slot.  Sc / dPc: S^T, dP^T - delta of this step (keys key0 ..
 // key0 + 31, rows [0, 32) of kc); Sn / dPn: those of the next step (rows
-// [0, 32) of kn / vn).  Group gi < 8: S^T / dP^T MFMAs 2gi, 2gi + 1 of the
-// next step's key block 0 and scores 2gi, 2gi + 1 of this step; group gi >= 8:
-// those MFMAs for key block 1 and dQ^T MFMAs 2(gi - 8), 2(gi - 8) + 1.  MFMA
-// index i of a block: ks = i / 4, dP^T if (i / 2) is odd, qb = i % 2; score e:
-// qb = e / 8, kb = (e / 4) % 2, r = e % 4; dQ^T MFMA j: db = j / 2, qb = j % 2.
-template <bool MASK>
-__device__ __forceinline__ void dq_slot(QCtx& x, const f32x4 (&Sc)[2][2], const f32x4 (&dPc)[2][2],
+// [0, 32) of kn / vn).  NG = D/8 groups, NH = NG/2 = DB per half.  Group
+// gi < NH: S^T / dP^T MFMAs 2gi, 2gi + 1 of the next step's key block 0 and
+// this step's scores 16gi/NH .. 16(gi+1)/NH - 1; group gi >= NH: those MFMAs
+// for key block 1 and dQ^T MFMAs 2(gi - NH), 2(gi - NH) + 1.  MFMA index i of
+// a block: ks = i / 4, dP^T if (i / 2) is odd, qb = i % 2; score e: qb = e /
+// 8, kb = (e / 4) % 2, r = e % 4; dQ^T MFMA j: db = j / 2, qb = j % 2.
+template <int D, bool MASK>
+__device__ __forceinline__ void dq_slot(QCtx<D>& x, const f32x4 (&Sc)[2][2], const f32x4 (&dPc)[2][2],
                                         f32x4 (&Sn)[2][2], f32x4 (&dPn)[2][2], const lds_t* kc,
                                         const lds_t* kn, const lds_t* vn, int key0) {
-  constexpr int NG = 16;
+  constexpr int ROWB = G<D>::ROWB, DB = G<D>::DB;
+  constexpr int NG = G<D>::CPR, NH = NG / 2, EPG = 16 / NH;
   bf16x8 fa[NG], fc[DB];
   auto load_a = [&](int gi) {  // fragment used by the two MFMAs of group gi
-    const int kb = gi / 8, i = 2 * (gi % 8), ks = i / 4;
+    const int kb = gi / NH, i = 2 * (gi % NH), ks = i / 4;
     fa[gi] = ((i / 2) & 1)
                  ? *reinterpret_cast<const lds_bf16x8*>(vn - x.vbase + 16 * kb * ROWB + x.va[ks])
                  : *reinterpret_cast<const lds_bf16x8*>(kn - x.kbase + 16 * kb * ROWB + x.ka[ks]);
   };
-  auto load_c = [&](int db) { fc[db] = tr_frag(kc - x.kbase + x.kt[db]); };
+  auto load_c = [&](int db) { fc[db] = tr_frag<D>(kc - x.kbase + x.kt[db]); };
   bf16x8 dsp[2];
   float ds[16];
   load_a(0);
@@ -549,9 +600,9 @@ __device__ __forceinline__ void dq_slot(QCtx& x, const f32x4 (&Sc)[2][2], const 
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
     if (gi + 1 < NG) load_a(gi + 1);
-    if (gi >= 7 && gi - 7 < DB) load_c(gi - 7);  // used one group later
+    if (gi >= NH - 1 && gi - (NH - 1) < DB) load_c(gi - (NH - 1));  // used one group later
     {
-      const int kb = gi / 8, i0 = 2 * (gi % 8);
+      const int kb = gi / NH, i0 = 2 * (gi % NH);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int i = i0 + u, ks = i / 4, qb = i % 2;
@@ -561,16 +612,16 @@ __device__ __forceinline__ void dq_slot(QCtx& x, const f32x4 (&Sc)[2][2], const 
           Sn[kb][qb] = mfma16(fa[gi], x.q[qb][ks], ks ? Sn[kb][qb] : f32x4{});
       }
     }
-    if (gi < 8) {
+    if (gi < NH) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = 2 * gi + u, qb = e / 8, kb = (e / 4) % 2, r = e % 4;
+      for (int u = 0; u < EPG; ++u) {
+        const int e = EPG * gi + u, qb = e / 8, kb = (e / 4) % 2, r = e % 4;
         float sv = Sc[kb][qb][r];
         asm volatile("" : "+v"(sv));
         float p = __builtin_amdgcn_exp2f(fmaf(sv, x.c, -x.lse2[qb]));
         if (MASK && key0 + 16 * kb + 4 * x.g + r >= x.Nkv) p = 0.f;
         ds[e] = p * dPc[kb][qb][r];
-        if (u == 1) {
+        if (e & 1) {
           bf16x2 pk = {(__bf16)ds[e - 1], (__bf16)ds[e]};
           asm volatile("" : "+v"(pk));
           dsp[qb][4 * kb + r - 1] = pk[0];
@@ -581,7 +632,7 @@ __device__ __forceinline__ void dq_slot(QCtx& x, const f32x4 (&Sc)[2][2], const 
       // dQ^T += K^T dS^T; k index 8g + j <-> key 4g + j (j < 4), 16 + 4g + j - 4 (j >= 4).
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int j = 2 * (gi - 8) + u, db = j / 2, qb = j % 2;
+        const int j = 2 * (gi - NH) + u, db = j / 2, qb = j % 2;
         x.dq[qb][db] = mfma16(fc[db], dsp[qb], x.dq[qb][db]);
       }
     }
@@ -589,31 +640,35 @@ __device__ __forceinline__ void dq_slot(QCtx& x, const f32x4 (&Sc)[2][2], const 
   }
 }
 
-__device__ __forceinline__ void stage_kv_tile(const QCtx& x, int t, int st) {
-  stage_rows(x.Kb, t * TR, x.Nkv, KQST(x, st), x.wave, x.voff);
-  stage_rows(x.Vb, t * TR, x.Nkv, VQST(x, st), x.wave, x.voff);
+template <int D>
+__device__ __forceinline__ void stage_kv_tile(const QCtx<D>& x, int t, int st) {
+  stage_rows<D>(x.Kb, t * TR, x.Nkv, KQST(x, st), x.wave, x.voff);
+  stage_rows<D>(x.Vb, t * TR, x.Nkv, VQST(x, st), x.wave, x.voff);
 }
 
 // Key tile t = steps 2t and 2t+1.  On entry S0 / dP0 hold step 2t; on exit
 // they hold step 2t+2 (past the last tile: unused).
-template <int PH, bool MASK>
-__device__ __forceinline__ void dq_tile(QCtx& x, int t, f32x4 (&S0)[2][2], f32x4 (&dP0)[2][2],
+template <int D, int PH, bool MASK>
+__device__ __forceinline__ void dq_tile(QCtx<D>& x, int t, f32x4 (&S0)[2][2], f32x4 (&dP0)[2][2],
                                         f32x4 (&S1)[2][2], f32x4 (&dP1)[2][2]) {
+  constexpr int ROWB = G<D>::ROWB;
   tile_barrier();  // tile t+1 landed; every wave is done with tile t-1
   const int sc = kv_stage_at(PH, t, 0), sn = kv_stage_at(PH, t, 1);
-  if (t + 2 < x.ntiles) stage_kv_tile(x, t + 2, kv_stage_at(PH, t, 2));
+  if (t + 2 < x.ntiles) stage_kv_tile<D>(x, t + 2, kv_stage_at(PH, t, 2));
   const lds_t* kc = KQST(x, sc);
   const lds_t* vc = VQST(x, sc);
-  dq_slot<MASK>(x, S0, dP0, S1, dP1, kc, kc + 32 * ROWB, vc + 32 * ROWB, t * TR);
-  dq_slot<MASK>(x, S1, dP1, S0, dP0, kc + 32 * ROWB, KQST(x, sn), VQST(x, sn), t * TR + 32);
+  dq_slot<D, MASK>(x, S0, dP0, S1, dP1, kc, kc + 32 * ROWB, vc + 32 * ROWB, t * TR);
+  dq_slot<D, MASK>(x, S1, dP1, S0, dP0, kc + 32 * ROWB, KQST(x, sn), VQST(x, sn), t * TR + 32);
 }
 
+template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                const float* __restrict__ LSE, const float* __restrict__ Dl,
                float* __restrict__ dQ, int Nq, int Nkv, int n_qtiles, int total, float c,
                float scale) {
+  constexpr int TILE = G<D>::TILE, KS = G<D>::KS, DB = G<D>::DB;
   __shared__ __attribute__((aligned(1024))) char k0s[TILE];
   __shared__ __attribute__((aligned(1024))) char k1s[TILE];
   __shared__ __attribute__((aligned(1024))) char k2s[TILE];
@@ -628,7 +683,7 @@ void dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15, g = lane >> 4;
 
-  QCtx x;
+  QCtx<D> x;
   x.g = g;
   x.lane = lane;
   x.wave = wave;
@@ -659,33 +714,33 @@ void dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   }
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    x.ka[ks] = a_off(c16, g, ks) + x.kbase;
-    x.va[ks] = a_off(c16, g, ks) + x.vbase;
+    x.ka[ks] = a_off<D>(c16, g, ks) + x.kbase;
+    x.va[ks] = a_off<D>(c16, g, ks) + x.vbase;
     asm volatile("" : "+v"(x.ka[ks]), "+v"(x.va[ks]));
   }
-  const int trb = tr_base(lane);
+  const int trb = tr_base<D>(lane);
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     x.kt[db] = (trb ^ (32 * db)) + x.kbase;
     asm volatile("" : "+v"(x.kt[db]));
   }
-  piece_offsets(x.voff, wave, lane);
+  piece_offsets<D>(x.voff, wave, lane);
 
-  stage_kv_tile(x, 0, 0);
-  if (x.ntiles > 1) stage_kv_tile(x, 1, 1);
+  stage_kv_tile<D>(x, 0, 0);
+  if (x.ntiles > 1) stage_kv_tile<D>(x, 1, 1);
   tile_barrier();  // tiles 0 and 1 landed
   f32x4 S0[2][2], dP0[2][2], S1[2][2], dP1[2][2];
-  sdpt_step(x, S0, dP0, x.k0, x.v0);
+  sdpt_step<D>(x, S0, dP0, x.k0, x.v0);
   const bool partial = (Nkv % TR) != 0;
   const int nfull = partial ? x.ntiles - 1 : x.ntiles;
   int t = 0;
   for (; t + 3 <= nfull; t += 3) {
-    dq_tile<0, false>(x, t, S0, dP0, S1, dP1);
-    dq_tile<1, false>(x, t + 1, S0, dP0, S1, dP1);
-    dq_tile<2, false>(x, t + 2, S0, dP0, S1, dP1);
+    dq_tile<D, 0, false>(x, t, S0, dP0, S1, dP1);
+    dq_tile<D, 1, false>(x, t + 1, S0, dP0, S1, dP1);
+    dq_tile<D, 2, false>(x, t + 2, S0, dP0, S1, dP1);
   }
-  for (; t < nfull; ++t) dq_tile<-1, false>(x, t, S0, dP0, S1, dP1);
-  if (partial) dq_tile<-1, true>(x, t, S0, dP0, S1, dP1);
+  for (; t < nfull; ++t) dq_tile<D, -1, false>(x, t, S0, dP0, S1, dP1);
+  if (partial) dq_tile<D, -1, true>(x, t, S0, dP0, S1, dP1);
 
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -701,12 +756,14 @@ void dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
 }  // namespace
 
-hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
-                                const void* dout, const float* lse, float* delta, float* dq,
-                                float* dk, float* dv, int B, int H, int Nq, int Nkv, float scale,
-                                hipStream_t stream) {
+namespace {
+template <int D>
+hipError_t launch_bwd_d(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, float* delta, float* dq, float* dk,
+                        float* dv, int B, int H, int Nq, int Nkv, float scale, hipStream_t stream) {
   const int64_t rows = (int64_t)B * H * Nq;
-  const int64_t dgrid = (rows + 15) / 16;
+  constexpr int kRowsPerBlock = 256 / (D / 8);  // delta_kernel
+  const int64_t dgrid = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   const int n_ktiles = (Nkv + KEYS_PER_WG - 1) / KEYS_PER_WG;
   const int n_qtiles = (Nq + QUERIES_PER_WG - 1) / QUERIES_PER_WG;
   const int64_t kv_total = (int64_t)B * H * n_ktiles, q_total = (int64_t)B * H * n_qtiles;
@@ -718,17 +775,36 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
   const __bf16* Vp = static_cast<const __bf16*>(v);
   const __bf16* Op = static_cast<const __bf16*>(o);
   const __bf16* dOp = static_cast<const __bf16*>(dout);
-  hipLaunchKernelGGL(delta_kernel, dim3((unsigned)dgrid), dim3(256), 0, stream, Op, dOp, delta, rows);
+  hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)dgrid), dim3(256), 0, stream, Op, dOp, delta,
+                     rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dkdv_kernel, dim3((unsigned)kv_total), dim3(kThreads), 0, stream, Qp, Kp, Vp,
+  hipLaunchKernelGGL(dkdv_kernel<D>, dim3((unsigned)kv_total), dim3(kThreads), 0, stream, Qp, Kp, Vp,
                      dOp, lse, (const float*)delta, dk, dv, Nq, Nkv, n_ktiles, (int)kv_total, c,
                      scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dq_kernel, dim3((unsigned)q_total), dim3(kThreads), 0, stream, Qp, Kp, Vp, dOp,
+  hipLaunchKernelGGL(dq_kernel<D>, dim3((unsigned)q_total), dim3(kThreads), 0, stream, Qp, Kp, Vp, dOp,
                      lse, (const float*)delta, dq, Nq, Nkv, n_qtiles, (int)q_total, c, scale);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                                const void* dout, const float* lse, float* delta, float* dq,
+                                float* dk, float* dv, int B, int H, int Nq, int Nkv, int D,
+                                float scale, hipStream_t stream) {
+  switch (D) {
+    case 32:
+      return launch_bwd_d<32>(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, Nq, Nkv, scale, stream);
+    case 64:
+      return launch_bwd_d<64>(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, Nq, Nkv, scale, stream);
+    case 128:
+      return launch_bwd_d<128>(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, Nq, Nkv, scale,
+                               stream);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace ditattn

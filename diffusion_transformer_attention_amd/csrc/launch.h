@@ -58,12 +58,12 @@ hipError_t launch_quant_fp8(const void* x, void* codes, float* descale, int B, i
 hipError_t launch_quant_fp8_n(const void* const* x, void* const* codes, float* const* descale,
                               const int* N, int ntensors, int B, int H, int D, hipStream_t stream);
 
-// Backward, bf16 q/k/v/o/dout (head dim 128), float32 lse in, delta out
-// ([B,H,Nq]), float32 dq/dk/dv.
+// Backward, bf16 q/k/v/o/dout (head dim 32, 64 or 128), float32 lse in,
+// delta out ([B,H,Nq]), float32 dq/dk/dv.
 hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                                 const void* dout, const float* lse, float* delta, float* dq,
-                                float* dk, float* dv, int B, int H, int Nq, int Nkv, float scale,
-                                hipStream_t stream);
+                                float* dk, float* dv, int B, int H, int Nq, int Nkv, int D,
+                                float scale, hipStream_t stream);
 
 // One tensor of a joint-sequence pack: text part [B,Ht,Nt,D] (heads h0 ..
 // h0+H-1 used), image part [B,H,Ni,D], output [B,H,Nt+Ni,D], all bf16.  A

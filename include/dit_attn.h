@@ -185,7 +185,8 @@ int dit_attn_fwd_balanced_noalloc(const void* q, const void* k, const void* v, v
  *   dS_ij    = P_ij * (dout_i . v_j - delta_i)
  *   dv_j = sum_i P_ij dout_i,  dk_j = scale sum_i dS_ij q_i,  dq_i = scale sum_j dS_ij k_j
  *
- *   q, o, dout : bf16 [B,H,Nq,D];  k, v : bf16 [B,H,Nkv,D];  D must be 128
+ *   q, o, dout : bf16 [B,H,Nq,D];  k, v : bf16 [B,H,Nkv,D];  D is 32, 64 or 128
+ *                (else DIT_EUNSUPPORTED)
  *   lse        : float32 [B,H,Nq], the forward's LSE (required)
  *   delta      : float32 [B,H,Nq], written (rowsum(dout * o)); caller-owned
  *   dq         : float32 [B,H,Nq,D];  dk, dv : float32 [B,H,Nkv,D]  (written)

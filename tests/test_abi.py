@@ -174,7 +174,8 @@ def test_backward_validation(lib):
     def b(B=1, Nq=64, Nkv=64, D=128, dt=0, gdt=1, q=A, lse=A, delta=A, dq=A, scale=0.125):
         return lib.dit_attn_bwd(q, A, A, A, A, lse, delta, dq, A, A, B, 2, Nq, Nkv, D,
                                 ctypes.c_float(scale), dt, gdt, S)
-    assert b(D=64) == dta.DIT_EUNSUPPORTED     # head dim 128 only
+    assert b(D=80) == dta.DIT_EUNSUPPORTED     # head dims 32, 64, 128 only
+    assert b(D=256) == dta.DIT_EUNSUPPORTED
     assert b(dt=1) == dta.DIT_EUNSUPPORTED     # bf16 inputs only
     assert b(gdt=0) == dta.DIT_EUNSUPPORTED    # float32 gradients only
     assert b(Nq=0) == dta.DIT_EINVAL           # gradients of an empty problem are not a no-op

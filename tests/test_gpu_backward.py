@@ -41,9 +41,9 @@ def _check_grad(got, ref, name, what):
     assert ma <= GRAD_MAX_ABS_REL, f"{what} {name} max-abs {ma:.3e}"
 
 
-def _inputs(B, H, Nq, Nkv, seed):
-    qb, kb, vb = datagen.small_bf16(B, H, Nq, 128, seed=seed, Nkv=Nkv)
-    dob = datagen.small_bf16(B, H, Nq, 128, seed=seed + 1)[0]
+def _inputs(B, H, Nq, Nkv, seed, D=128):
+    qb, kb, vb = datagen.small_bf16(B, H, Nq, D, seed=seed, Nkv=Nkv)
+    dob = datagen.small_bf16(B, H, Nq, D, seed=seed + 1)[0]
     return qb, kb, vb, dob
 
 
@@ -71,6 +71,32 @@ def test_backward_small_full_compare(B, H, Nq, Nkv):
         _check_grad(to_f64(got), ref, n, what)
     dd = to_f64(delta) - rd
     assert np.linalg.norm(dd) <= 1e-2 * max(np.linalg.norm(rd), 1e-12)
+
+
+@pytest.mark.parametrize("D", [32, 64])
+@pytest.mark.parametrize("B,H,Nq,Nkv", [
+    (1, 2, 128, 128),
+    (2, 3, 300, 200),      # ragged query and key tiles
+    (1, 1, 1, 1),          # one token
+    (1, 1, 257, 1029),     # several workgroups each way, ragged
+    (1, 2, 640, 96),       # more query tiles than key tiles
+])
+def test_backward_head_dims(B, H, Nq, Nkv, D):
+    say("bwd D", D, B, H, Nq, Nkv)
+    qb, kb, vb, dob = _inputs(B, H, Nq, Nkv, seed=Nq * 7 + Nkv + D, D=D)
+    ins, (dq, dk, dv, delta) = _gpu_fwd_bwd(qb, kb, vb, dob)
+    rq, rk, rv, rd = oracle.attention_backward(f64(qb), f64(kb), f64(vb), f64(dob))
+    what = f"D{D} B{B} H{H} Nq{Nq} Nkv{Nkv}"
+    for got, ref, n in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+        assert tuple(got.shape[2:]) == ref.shape[2:]
+        _check_grad(to_f64(got), ref, n, what)
+    dd = to_f64(delta) - rd
+    assert np.linalg.norm(dd) <= 1e-2 * max(np.linalg.norm(rd), 1e-12)
+    # a second call gives the same bits
+    tq, tk, tv, tdo, O, L = ins
+    again = dta.dit_attn_bwd(tq, tk, tv, O, tdo, L)
+    for a, b, n in zip((dq, dk, dv, delta), again, ("dq", "dk", "dv", "delta")):
+        assert torch.equal(a, b), f"{what} {n} not repeatable"
 
 
 def test_backward_explicit_scale_and_large_scores():
