@@ -930,7 +930,11 @@ constexpr int kStoreInsts = QB * ((OUT_F32 ? Geo<D>::DB : Geo<D>::DB / 2) + 1);
 // even rows of another), after which group g holds the 8 channels
 // 16 (2p + (g & 1)) + 8 (g >> 1) .. +7 and each row's 4 lanes write its
 // channels [32p, 32p + 32) as 16-byte pieces: half the instructions, and
-// 64-byte row pieces instead of 32-byte ones.
+// 64-byte row pieces instead of 32-byte ones.  The output is stored
+// non-temporally (nothing in the kernel reads it back): the 64 KB of bf16 O a
+// unit writes then does not displace the K/V tiles the XCD's other units are
+// streaming through its L2 (cross attention over 512 keys 2.5% faster, image
+// share 1%, the long shapes unchanged).
 template <int D, bool OUT_F32, bool F8, bool SPLIT, int QB>
 __device__ __forceinline__ void store_tile(const Frags<D, F8, QB>& f, const TileInfo& ti, void* Oout,
                                            float* LSE, int Nq, const Layout& lay, int64_t qsstride,
@@ -948,8 +952,9 @@ __device__ __forceinline__ void store_tile(const Frags<D, F8, QB>& f, const Tile
     if (OUT_F32) {
 #pragma unroll
       for (int db = 0; db < Gm::DB; ++db)
-        *reinterpret_cast<f32x4*>(static_cast<float*>(Oout) + obase + db * 16 + 4 * g) =
-            f.o[qb][db] * inv;
+        __builtin_nontemporal_store(
+            f.o[qb][db] * inv,
+            reinterpret_cast<f32x4*>(static_cast<float*>(Oout) + obase + db * 16 + 4 * g));
     } else {
 #pragma unroll
       for (int p = 0; p < Gm::DB / 2; ++p) {
@@ -961,8 +966,8 @@ __device__ __forceinline__ void store_tile(const Frags<D, F8, QB>& f, const Tile
         const auto lo = __builtin_amdgcn_permlane16_swap(aw[0], bw[0], false, false);
         const auto hi = __builtin_amdgcn_permlane16_swap(aw[1], bw[1], false, false);
         const int ch = 32 * p + 16 * (g & 1) + 8 * (g >> 1);
-        *reinterpret_cast<u32x4*>(static_cast<__bf16*>(Oout) + obase + ch) =
-            u32x4{lo[0], hi[0], lo[1], hi[1]};
+        __builtin_nontemporal_store(u32x4{lo[0], hi[0], lo[1], hi[1]},
+                                    reinterpret_cast<u32x4*>(static_cast<__bf16*>(Oout) + obase + ch));
       }
     }
     // The LSE goes through a buffer descriptor over the block's 16 rows from
