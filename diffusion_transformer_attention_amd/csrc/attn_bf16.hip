@@ -930,11 +930,13 @@ constexpr int kStoreInsts = QB * ((OUT_F32 ? Geo<D>::DB : Geo<D>::DB / 2) + 1);
 // even rows of another), after which group g holds the 8 channels
 // 16 (2p + (g & 1)) + 8 (g >> 1) .. +7 and each row's 4 lanes write its
 // channels [32p, 32p + 32) as 16-byte pieces: half the instructions, and
-// 64-byte row pieces instead of 32-byte ones.  The output is stored
-// non-temporally (nothing in the kernel reads it back): the 64 KB of bf16 O a
-// unit writes then does not displace the K/V tiles the XCD's other units are
+// 64-byte row pieces instead of 32-byte ones.  The bf16 output is stored
+// non-temporally (nothing in the kernel reads it back): the 64 KB of O a unit
+// writes then does not displace the K/V tiles the XCD's other units are
 // streaming through its L2 (cross attention over 512 keys 2.5% faster, image
-// share 1%, the long shapes unchanged).
+// share 1%, the long shapes unchanged); the price is that a row's four
+// 64-byte pieces reach memory uncombined.  Float32 output (Ring partials)
+// gains nothing from it, so it is stored as usual.
 template <int D, bool OUT_F32, bool F8, bool SPLIT, int QB>
 __device__ __forceinline__ void store_tile(const Frags<D, F8, QB>& f, const TileInfo& ti, void* Oout,
                                            float* LSE, int Nq, const Layout& lay, int64_t qsstride,
@@ -952,9 +954,8 @@ __device__ __forceinline__ void store_tile(const Frags<D, F8, QB>& f, const Tile
     if (OUT_F32) {
 #pragma unroll
       for (int db = 0; db < Gm::DB; ++db)
-        __builtin_nontemporal_store(
-            f.o[qb][db] * inv,
-            reinterpret_cast<f32x4*>(static_cast<float*>(Oout) + obase + db * 16 + 4 * g));
+        *reinterpret_cast<f32x4*>(static_cast<float*>(Oout) + obase + db * 16 + 4 * g) =
+            f.o[qb][db] * inv;
     } else {
 #pragma unroll
       for (int p = 0; p < Gm::DB / 2; ++p) {
