@@ -9,7 +9,8 @@ from .ref import (attention, attention_rows, probabilities, split_kv, merge,
                   unshard_tokens, ulysses_attention, ulysses_send_bytes_per_rank,
                   default_scale, rope, round_bf16, joint_sequence,
                   joint_attention, E4M3_MAX, e4m3_decode, e4m3_round, e4m3_encode,
-                  quantize_fp8, attention_fp8)
+                  quantize_fp8, attention_fp8, LOG2E_F32, pow2_descale, quantize_fp8_mx,
+                  attention_fp8_mx)
 
 __all__ = ["attention", "attention_rows", "probabilities", "split_kv", "merge",
            "attention_backward", "attention_backward_rows", "attention_backward_keys",
@@ -17,4 +18,5 @@ __all__ = ["attention", "attention_rows", "probabilities", "split_kv", "merge",
            "unshard_tokens", "ulysses_attention", "ulysses_send_bytes_per_rank",
            "default_scale", "rope", "round_bf16", "joint_sequence",
            "joint_attention", "E4M3_MAX", "e4m3_decode", "e4m3_round", "e4m3_encode",
-           "quantize_fp8", "attention_fp8"]
+           "quantize_fp8", "attention_fp8", "LOG2E_F32", "pow2_descale", "quantize_fp8_mx",
+           "attention_fp8_mx"]

@@ -440,3 +440,66 @@ def attention_fp8(q_codes, k_codes, v, q_descale, k_descale, scale=None, rows=No
     if rows is not None:
         q = q[:, :, np.asarray(rows, dtype=np.int64)]
     return attention(q, k, v, scale)
+
+
+# --------------------------------------------------------------------------
+# FP8 attention, second reading: the scaling done by the fp8 matrix
+# instruction itself.  The same step ("Multi-GPU parallelism ...", "Combining:
+# what xDiT does": FP8 low precision on top of the split) read for hardware
+# whose fp8 products take power-of-two (E8M0) scales: each head of q and of k
+# gets a power-of-two scale, the smallest that brings its largest magnitude
+# within E4M3's 448, and the queries are first multiplied in float32 by the
+# softmax constant scale * log2(e), so that the scaled products are the
+# scores in base 2.  P and V stay in the model's type.
+# --------------------------------------------------------------------------
+LOG2E_F32 = np.float32(1.4426950408889634)
+
+
+def pow2_descale(amax):
+    """Per-head power-of-two scale for largest magnitudes ``amax`` (float32):
+    the smallest 2**e with amax <= 448 * 2**e, e >= -126; 1 where amax is 0."""
+    a = np.asarray(amax, dtype=np.float64)
+    safe = np.where(a > 0, a, E4M3_MAX)
+    e = np.ceil(np.log2(safe / E4M3_MAX)).astype(np.int64)
+    # exact correction of the floating-point log: 448 * 2**e is exact in float64
+    e = np.where(E4M3_MAX * np.ldexp(1.0, e) < safe, e + 1, e)
+    e = np.where(E4M3_MAX * np.ldexp(1.0, e - 1) >= safe, e - 1, e)
+    e = np.maximum(e, -126)
+    return np.where(a > 0, np.ldexp(1.0, e), 1.0).astype(np.float32)
+
+
+def quantize_fp8_mx(q, k, scale=None):
+    """Queries and keys [B,H,N,D] (float32 values) of one attention call ->
+    (q_codes, k_codes, q_descale, k_descale).
+
+    q' = float32(q * c0) with c0 = float32(scale) * float32(log2 e) (the
+    float32 product); k' = k.  Per (b, h): d = pow2_descale(max |x'|), codes =
+    E4M3 of x' / d (exact: d is a power of two).  ``scale`` defaults to
+    1/sqrt(D)."""
+    q32 = np.asarray(q, dtype=np.float32)
+    k32 = np.asarray(k, dtype=np.float32)
+    scale = default_scale(q32.shape[-1]) if scale is None else scale
+    c0 = np.float32(np.float32(scale) * LOG2E_F32)
+    out = []
+    for x in (q32 * c0, k32):
+        amax = np.abs(x).max(axis=(2, 3)) if x.size else np.zeros(x.shape[:2], np.float32)
+        d = pow2_descale(amax)
+        out.append((e4m3_encode(x.astype(np.float64) / d.astype(np.float64)[:, :, None, None]), d))
+    return out[0][0], out[1][0], out[0][1], out[1][1]
+
+
+def attention_fp8_mx(q_codes, k_codes, v, q_descale, k_descale, rows=None):
+    """Attention whose scores are in base 2: s_ij = q_descale * k_descale *
+    (q_i . k_j) of the decoded codes, P_ij = 2**s_ij / sum_j 2**s_ij, O = P V,
+    LSE (natural log) = ln 2 * log2 sum_j 2**s_ij."""
+    q = e4m3_decode(q_codes) * _f64(q_descale)[:, :, None, None]
+    k = e4m3_decode(k_codes) * _f64(k_descale)[:, :, None, None]
+    if rows is not None:
+        q = q[:, :, np.asarray(rows, dtype=np.int64)]
+    s2 = np.einsum("bhid,bhjd->bhij", q, k)
+    m = s2.max(axis=-1, keepdims=True)
+    w = np.exp2(s2 - m)
+    den = w.sum(axis=-1, keepdims=True)
+    O = np.einsum("bhij,bhjd->bhid", w / den, _f64(v))
+    lse = np.log(2.0) * (m[..., 0] + np.log2(den[..., 0]))
+    return O, lse
