@@ -27,8 +27,8 @@ EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_block", "dit_attn_fwd_balanced",
             "dit_attn_fwd_balanced_workspace", "dit_attn_fwd_balanced_noalloc",
             "dit_attn_fwd_ulysses", "dit_attn_bwd",
             "dit_attn_merge", "dit_rope_pack", "dit_attn_fwd_joint", "dit_quant_fp8",
-            "dit_quant_fp8_qk", "dit_attn_fwd_fp8", "ulysses_seq2head", "ulysses_head2seq", "dit_strerror",
-            "dit_abi_version")
+            "dit_quant_fp8_qk", "dit_attn_fwd_fp8", "dit_quant_fp8_qk_mx", "dit_attn_fwd_fp8_mx",
+            "ulysses_seq2head", "ulysses_head2seq", "dit_strerror", "dit_abi_version")
 
 _lib = None
 _lib_path = None
@@ -64,6 +64,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.dit_quant_fp8.argtypes = [P, P, P, I, I, I, I, P]
     lib.dit_quant_fp8_qk.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
     lib.dit_attn_fwd_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, I, P]
+    lib.dit_quant_fp8_qk_mx.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, P]
+    lib.dit_attn_fwd_fp8_mx.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P]
     lib.dit_rope_pack.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
     lib.dit_attn_fwd_joint.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P,
                                        I, I, I, I, I, I, I, F, P]
@@ -73,7 +75,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                  "dit_attn_fwd_balanced_workspace", "dit_attn_fwd_balanced_noalloc",
                  "dit_attn_fwd_ulysses", "dit_attn_bwd",
                  "dit_attn_merge", "dit_rope_pack", "dit_attn_fwd_joint", "dit_quant_fp8",
-                 "dit_quant_fp8_qk", "dit_attn_fwd_fp8", "ulysses_seq2head", "ulysses_head2seq", "dit_abi_version"):
+                 "dit_quant_fp8_qk", "dit_attn_fwd_fp8", "dit_quant_fp8_qk_mx", "dit_attn_fwd_fp8_mx",
+                 "ulysses_seq2head", "ulysses_head2seq", "dit_abi_version"):
         getattr(lib, name).restype = ctypes.c_int
     lib.dit_strerror.argtypes = [ctypes.c_int]
     lib.dit_strerror.restype = ctypes.c_char_p
@@ -473,12 +476,8 @@ def dit_quant_fp8(x, codes=None, descale=None):
     return c, ds
 
 
-def dit_quant_fp8_qk(q, k, q_codes=None, k_codes=None, q_descale=None, k_descale=None):
-    """dit_quant_fp8 of q [B,H,Nq,D] and k [B,H,Nkv,D] (bf16) in one call.
-
-    Returns (q_codes, k_codes, q_descale, k_descale).
-    """
-    lib = load_library()
+def _quant_qk_outputs(q, k, q_codes, k_codes, q_descale, k_descale):
+    """Shape checks and outputs of the paired quantizers."""
     for t, n in ((q, "q"), (k, "k")):
         _need(t, n, 4)
         if t.dtype != torch.bfloat16:
@@ -501,9 +500,36 @@ def dit_quant_fp8_qk(q, k, q_codes=None, k_codes=None, q_descale=None, k_descale
         if d.dtype != torch.float32 or tuple(d.shape) != (B, H):
             raise ValueError(f"{n} must be float32 [B,H]")
         ds.append(d)
+    return (B, H, Nq, Nkv, D), out, ds
+
+
+def dit_quant_fp8_qk(q, k, q_codes=None, k_codes=None, q_descale=None, k_descale=None):
+    """dit_quant_fp8 of q [B,H,Nq,D] and k [B,H,Nkv,D] (bf16) in one call.
+
+    Returns (q_codes, k_codes, q_descale, k_descale).
+    """
+    lib = load_library()
+    (B, H, Nq, Nkv, D), out, ds = _quant_qk_outputs(q, k, q_codes, k_codes, q_descale, k_descale)
     rc = lib.dit_quant_fp8_qk(_ptr(q), _ptr(k), _ptr(out[0]), _ptr(out[1]), _ptr(ds[0]), _ptr(ds[1]),
                               B, H, Nq, Nkv, D, _stream())
     _check(rc, "dit_quant_fp8_qk")
+    return out[0], out[1], ds[0], ds[1]
+
+
+def dit_quant_fp8_qk_mx(q, k, scale=None, q_codes=None, k_codes=None, q_descale=None,
+                        k_descale=None):
+    """q [B,H,Nq,D] and k [B,H,Nkv,D] (bf16) to E4M3 codes with power-of-two
+    descales, q first multiplied by scale * log2(e) (scale defaults to
+    1/sqrt(D)), for dit_attn_fwd_fp8_mx.
+
+    Returns (q_codes, k_codes, q_descale, k_descale).
+    """
+    lib = load_library()
+    (B, H, Nq, Nkv, D), out, ds = _quant_qk_outputs(q, k, q_codes, k_codes, q_descale, k_descale)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = lib.dit_quant_fp8_qk_mx(_ptr(q), _ptr(k), _ptr(out[0]), _ptr(out[1]), _ptr(ds[0]),
+                                 _ptr(ds[1]), B, H, Nq, Nkv, D, ctypes.c_float(scale), _stream())
+    _check(rc, "dit_quant_fp8_qk_mx")
     return out[0], out[1], ds[0], ds[1]
 
 
@@ -543,6 +569,46 @@ def dit_attn_fwd_fp8(q, k, v, q_descale, k_descale, scale=None, out_dtype=torch.
                               _ptr(lse), B, H, Nq, Nkv, D, ctypes.c_float(scale),
                               _dtype_code(o.dtype), _stream())
     _check(rc, "dit_attn_fwd_fp8")
+    return o, lse
+
+
+def dit_attn_fwd_fp8_mx(q, k, v, q_descale, k_descale, out_dtype=torch.bfloat16, out=None,
+                        lse=None, return_lse=True):
+    """Attention of codes from dit_quant_fp8_qk_mx (q [B,H,Nq,128], k
+    [B,H,Nkv,128], power-of-two float32 [B,H] descales; the softmax scale is
+    in the query codes) and bf16 v [B,H,Nkv,128]: base-2 scores
+    q_descale * k_descale * (q . k).
+
+    Returns (O [B,H,Nq,D] in out_dtype, LSE float32 [B,H,Nq] (natural log) or None).
+    """
+    lib = load_library()
+    _codes(q, "q")
+    _codes(k, "k")
+    _need(v, "v", 4)
+    B, H, Nq, D = q.shape
+    Nkv = k.shape[2]
+    if k.shape[:2] != q.shape[:2] or k.shape[3] != D or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k, v must be [B,H,Nkv,D] matching q")
+    if v.dtype != torch.bfloat16:
+        raise ValueError("v must be bf16")
+    for t, n in ((q_descale, "q_descale"), (k_descale, "k_descale")):
+        _need(t, n, 2)
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, H):
+            raise ValueError(f"{n} must be float32 [B,H]")
+    o = torch.empty((B, H, Nq, D), device=q.device, dtype=out_dtype) if out is None else out
+    _need(o, "out", 4)
+    if tuple(o.shape) != (B, H, Nq, D):
+        raise ValueError("out must be [B,H,Nq,D]")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Nq), device=q.device, dtype=torch.float32)
+    if lse is not None:
+        _need(lse, "lse", 3)
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq):
+            raise ValueError("lse must be float32 [B,H,Nq]")
+    rc = lib.dit_attn_fwd_fp8_mx(_ptr(q), _ptr(k), _ptr(v), _ptr(q_descale), _ptr(k_descale),
+                                 _ptr(o), _ptr(lse), B, H, Nq, Nkv, D, _dtype_code(o.dtype),
+                                 _stream())
+    _check(rc, "dit_attn_fwd_fp8_mx")
     return o, lse
 
 

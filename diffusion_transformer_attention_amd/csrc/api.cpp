@@ -352,6 +352,43 @@ int dit_attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q
                                              static_cast<hipStream_t>(stream)));
 }
 
+int dit_quant_fp8_qk_mx(const void* q, const void* k, void* q_codes, void* k_codes,
+                        float* q_descale, float* k_descale, int B, int H, int Nq, int Nkv, int D,
+                        float scale, void* stream) {
+  if (B < 0 || H < 0 || Nq < 0 || Nkv < 0 || D <= 0) return DIT_EINVAL;
+  if (!(isfinite(scale) && scale > 0.0f)) return DIT_EINVAL;
+  if (!supported_head_dim(D)) return DIT_EUNSUPPORTED;
+  if (!size_ok(B, H, Nq, D) || !size_ok(B, H, Nkv, D) || (int64_t)B * H > 0x7fffffff)
+    return DIT_ERANGE;
+  if (B == 0 || H == 0) return DIT_OK;
+  if (!q_descale || !k_descale || (Nq > 0 && (!q || !q_codes)) || (Nkv > 0 && (!k || !k_codes)))
+    return DIT_EINVAL;
+  if (!aligned(q_descale, 4) || !aligned(k_descale, 4)) return DIT_EALIGN;
+  if (Nq > 0 && (!aligned(q, 16) || !aligned(q_codes, 8))) return DIT_EALIGN;
+  if (Nkv > 0 && (!aligned(k, 16) || !aligned(k_codes, 8))) return DIT_EALIGN;
+  const float c0 = scale * 1.4426950408889634f;
+  return map_launch(ditattn::launch_quant_fp8_mx(q, k, q_codes, k_codes, q_descale, k_descale, B, H,
+                                                 Nq, Nkv, D, c0, static_cast<hipStream_t>(stream)));
+}
+
+int dit_attn_fwd_fp8_mx(const void* q, const void* k, const void* v, const float* q_descale,
+                        const float* k_descale, void* o, float* lse, int B, int H, int Nq, int Nkv,
+                        int D, int o_dtype, void* stream) {
+  if (B < 0 || H < 0 || Nq < 0 || Nkv < 0 || D <= 0) return DIT_EINVAL;
+  if (o_dtype != DIT_BF16 && o_dtype != DIT_F32) return DIT_EUNSUPPORTED;
+  if (D != 128) return DIT_EUNSUPPORTED;
+  if (!size_ok(B, H, Nq, D) || !size_ok(B, H, Nkv, D)) return DIT_ERANGE;
+  if (B == 0 || H == 0 || Nq == 0) return DIT_OK;
+  if (Nkv == 0) return DIT_EINVAL;
+  if (!q || !k || !v || !q_descale || !k_descale || !o) return DIT_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return DIT_EALIGN;
+  if (!aligned(q_descale, 4) || !aligned(k_descale, 4) || (lse && !aligned(lse, 4)))
+    return DIT_EALIGN;
+  return map_launch(ditattn::launch_attn_fp8_mx(q, k, v, q_descale, k_descale, o, lse, B, H, Nq,
+                                                Nkv, o_dtype == DIT_F32,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 int ulysses_seq2head(const void* in, void* out, int P, int B, int H, int N, int D, int elem_bytes,
                      void* stream) {
   return permute_common(in, out, P, B, H, N, D, elem_bytes, false, stream);

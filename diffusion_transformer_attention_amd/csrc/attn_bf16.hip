@@ -90,6 +90,7 @@ constexpr int kBN = 64;                 // keys per LDS tile (two 32-key slots)
 static_assert(kBM == kFwdQueryTile && kBN == kFwdKeyTile, "launch.h tile sizes");
 constexpr int kStages = 3;              // LDS stages for K and for V (tile t uses stage t % 3)
 constexpr float kMaxSum = 1099511627776.0f;  // 2^40: a larger row sum means the pass must be redone
+constexpr float kMinSum = 1.0f / kMaxSum;     // fp8 mode 2 without a reference max: a smaller one too
 
 template <int D>
 struct Geo {
@@ -122,11 +123,11 @@ __device__ __forceinline__ int swz_v(int row) {
 // 32g .. 32g+31 of its key row in A and of its query column in B: the
 // instruction pairs byte j of lane group g in A with the same byte of the
 // same group in B, checked on gfx950).
-template <int D, bool F8>
+template <int D, int F8>
 struct QKOps;
 
 template <int D>
-struct QKOps<D, false> {
+struct QKOps<D, 0> {
   using Frag = bf16x8;
   static constexpr int KS = D / 32;       // k-steps (fragments per 16-key block)
   static constexpr int ROWB = D * 2;      // bytes per K row
@@ -146,10 +147,11 @@ struct QKOps<D, false> {
   __device__ static f32x4 mma(Frag a, Frag b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
+  __device__ static f32x4 mma_s(Frag a, Frag b, f32x4 c, int, int) { return mma(a, b, c); }
 };
 
 template <int D>
-struct QKOps<D, true> {
+struct QKOps<D, 1> {
   static_assert(D == 128, "fp8 Q.K^T is built for head dim 128");
   using Frag = i32x8;
   static constexpr int KS = 1;
@@ -178,6 +180,19 @@ struct QKOps<D, true> {
   }
   __device__ static f32x4 mma(Frag a, Frag b, f32x4 c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  }
+  __device__ static f32x4 mma_s(Frag a, Frag b, f32x4 c, int, int) { return mma(a, b, c); }
+};
+
+// fp8 with power-of-two per-head scales (mode 2): the same operands, and the
+// instruction multiplies the products by 2^(sa - 127) * 2^(sb - 127) (E8M0
+// bytes sa for the keys, sb for the queries), so that with the softmax
+// constant folded into the query codes the accumulator holds base-2 scores.
+template <int D>
+struct QKOps<D, 2> : QKOps<D, 1> {
+  using Frag = typename QKOps<D, 1>::Frag;
+  __device__ static f32x4 mma_s(Frag a, Frag b, f32x4 c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
   }
 };
 
@@ -303,7 +318,7 @@ __device__ __forceinline__ void piece_offsets(int* voff, int wave, int lane, Swz
   }
 }
 
-template <int D, bool F8, int QB = kQB>
+template <int D, int F8, int QB = kQB>
 struct Frags {
   using QK = QKOps<D, F8>;
   f32x4 o[QB][Geo<D>::DB];           // O^T blocks: lane holds channels 16db+4g+r of its query
@@ -313,7 +328,7 @@ struct Frags {
 };
 
 // Everything one pass over the keys needs.
-template <int D, bool F8>
+template <int D, int F8>
 struct PassCtx {
   using QK = QKOps<D, F8>;
   const char* Kb;    // keys / values of this (b, h): segment 0
@@ -327,6 +342,7 @@ struct PassCtx {
   lds_t *v0, *v1, *v2;  // V stages
   int Nkv, ntiles, wave, lane, g;
   float c;
+  int sa, sb;       // E8M0 scales of the key and query products (fp8 mode 2)
   bool str;          // segments may end inside a tile (set from a template parameter)
   // Fragment offsets, each plus the LDS address of stage 0 and held in a
   // register the compiler cannot see through: a read of stage j is then
@@ -357,7 +373,7 @@ __device__ __forceinline__ lds_t* stage_of(lds_t* s0, lds_t* s1, lds_t* s2, int 
 
 // S^T of one 32-key step (rows [0, 32) at kst): S[kb][qb] holds keys
 // 16kb + 4g + r for the lane's query of block qb.
-template <int D, bool F8, int QB>
+template <int D, int F8, int QB>
 __device__ __forceinline__ void qk_step(f32x4 (&S)[2][QB], const lds_t* kst,
                                         const PassCtx<D, F8>& x, const Frags<D, F8, QB>& f) {
   using QK = QKOps<D, F8>;
@@ -371,7 +387,7 @@ __device__ __forceinline__ void qk_step(f32x4 (&S)[2][QB], const lds_t* kst,
     for (int kb = 0; kb < 2; ++kb) {
       const typename QK::Frag a = QK::load(kst - x.kbase + kb * 16 * QK::ROWB, x.kof[ks]);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) S[kb][qb] = QK::mma(a, f.q[qb][ks], S[kb][qb]);
+      for (int qb = 0; qb < QB; ++qb) S[kb][qb] = QK::mma_s(a, f.q[qb][ks], S[kb][qb], x.sa, x.sb);
     }
 }
 
@@ -406,7 +422,7 @@ __device__ __forceinline__ void rowmax_step(const f32x4 (&S)[2][QB], float (&m)[
 // (kb 1): MFMA k index 8g + j <-> key 4g + j (j < 4), 16 + 4g + j - 4 (j >= 4).
 // NOQK: the last slot of a pass, which has no next step: no QK^T MFMAs and
 // no K fragment reads.
-template <int D, bool F8, bool MASK, bool NOQK = false, int QB>
+template <int D, int F8, bool MASK, bool NOQK = false, bool FB = false, int QB>
 __device__ __forceinline__ void slot(Frags<D, F8, QB>& f, const f32x4 (&Sc)[2][QB], f32x4 (&Sn)[2][QB],
                                      const bf16x8 (&Pp)[QB], bf16x8 (&Pc)[QB],
                                      const lds_t* k_next, const lds_t* v_prev,
@@ -466,7 +482,7 @@ __device__ __forceinline__ void slot(Frags<D, F8, QB>& f, const f32x4 (&Sc)[2][Q
 #pragma unroll
     for (int i = g * NQK / NG; i < (g + 1) * NQK / NG; ++i) {
       const int ks = i / (2 * QB), kb = (i / QB) % 2, qb = i % QB;
-      if (!NOQK) Sn[kb][qb] = QK::mma(kf[ks * 2 + kb], f.q[qb][ks], Sn[kb][qb]);
+      if (!NOQK) Sn[kb][qb] = QK::mma_s(kf[ks * 2 + kb], f.q[qb][ks], Sn[kb][qb], x.sa, x.sb);
     }
 #pragma unroll
     for (int j = g * NPV / NG; j < (g + 1) * NPV / NG; ++j) {
@@ -487,7 +503,10 @@ __device__ __forceinline__ void slot(Frags<D, F8, QB>& f, const f32x4 (&Sc)[2][Q
       // slots, which leaves those slots' MFMAs with no VALU work to hide.
       asm volatile("" : "+v"(sv));
       if (MASK) sv = (key0 + 16 * kb + 4 * x.g + r < x.Nkv) ? sv : -INFINITY;
-      p[qb][4 * kb + r] = __builtin_amdgcn_exp2f(fmaf(sv, x.c, -mc[qb]));
+      // mode 2: sv is the base-2 score; the first attempt takes no reference
+      // max (m = 0), the exact-max pass (FB) subtracts the row's
+      p[qb][4 * kb + r] = __builtin_amdgcn_exp2f(
+          F8 == 2 ? (FB ? sv - f.m[qb] : sv) : fmaf(sv, x.c, -mc[qb]));
       if (e & 1) {
         const int j = 4 * kb + r - 1;
         const float p0 = p[qb][j], p1 = p[qb][j + 1];
@@ -508,7 +527,7 @@ __device__ __forceinline__ void slot(Frags<D, F8, QB>& f, const f32x4 (&Sc)[2][Q
 
 // Load the queries of the lane's rows (one row pointer per 16-row block) as
 // the Q^T operands.
-template <int D, bool F8, int QB>
+template <int D, int F8, int QB>
 __device__ __forceinline__ void load_queries(Frags<D, F8, QB>& f, const char* const (&rows)[2], int g) {
   using QK = QKOps<D, F8>;
 #pragma unroll
@@ -525,7 +544,7 @@ __device__ __forceinline__ void load_queries(Frags<D, F8, QB>& f, const char* co
 // tile, so there is no step 2t+2: its slot has no QK^T, and once the first
 // slot's QK^T has read the queries, the next unit's queries are loaded in
 // their place (when x.nqv), a tile and the epilogue ahead of their use.
-template <int D, bool F8, int PH, bool MASK, int WAITN = 0, bool LAST = false, int QB>
+template <int D, int F8, int PH, bool MASK, int WAITN = 0, bool LAST = false, bool FB = false, int QB>
 __device__ __forceinline__ void tile_trip(int t, Frags<D, F8, QB>& f, f32x4 (&S0)[2][QB], f32x4 (&S1)[2][QB],
                                           bf16x8 (&Pa)[QB], bf16x8 (&Pb)[QB],
                                           PassCtx<D, F8>& x) {
@@ -542,17 +561,17 @@ __device__ __forceinline__ void tile_trip(int t, Frags<D, F8, QB>& f, f32x4 (&S0
   const lds_t* vcur = VSTAGE(x, PH, t);
   const lds_t* vprev = VSTAGE(x, p2, t + 2);  // stage of tile t-1
   const int key0 = t * kBN;
-  slot<D, F8, MASK>(f, S0, S1, Pa, Pb, kcur + 32 * QK::ROWB, vprev + 32 * Gm::ROWB, x, key0);
+  slot<D, F8, MASK, false, FB>(f, S0, S1, Pa, Pb, kcur + 32 * QK::ROWB, vprev + 32 * Gm::ROWB, x, key0);
   if (LAST) {
     if (x.nqv) load_queries<D, F8>(f, x.nq, x.g);
-    slot<D, F8, MASK, true>(f, S1, S0, Pb, Pa, knext, vcur, x, key0 + 32);
+    slot<D, F8, MASK, true, FB>(f, S1, S0, Pb, Pa, knext, vcur, x, key0 + 32);
   } else {
-    slot<D, F8, MASK>(f, S1, S0, Pb, Pa, knext, vcur, x, key0 + 32);
+    slot<D, F8, MASK, false, FB>(f, S1, S0, Pb, Pa, knext, vcur, x, key0 + 32);
   }
 }
 
 // O^T += V^T P^T for one 32-key step (used once, after the loop).
-template <int D, bool F8, int QB>
+template <int D, int F8, int QB>
 __device__ __forceinline__ void pv_step(Frags<D, F8, QB>& f, const bf16x8 (&P)[QB], const lds_t* vst,
                                         const PassCtx<D, F8>& x) {
   using Gm = Geo<D>;
@@ -573,7 +592,7 @@ __device__ __forceinline__ void pv_step(Frags<D, F8, QB>& f, const bf16x8 (&P)[Q
 }
 
 // Stage the first K tiles (0 and 1) and V tile 0 of a pass.
-template <int D, bool F8>
+template <int D, int F8>
 __device__ __forceinline__ void stage_first(PassCtx<D, F8>& x) {
   using Gm = Geo<D>;
   using QK = QKOps<D, F8>;
@@ -584,13 +603,22 @@ __device__ __forceinline__ void stage_first(PassCtx<D, F8>& x) {
   stage_next<Gm::ROWB, Gm::PIECES>(x.vs, x.vjump, x.v0, x.wave, x.vld, x.str);
 }
 
+// Whether a row's pass must be redone with its exact max: its sum outgrew
+// the bound (or is not a number); in fp8 mode 2, whose first attempt takes
+// no reference max (m = 0, p = 2^s), also when the sum is tiny, all scores
+// far below zero.
+template <int F8>
+__device__ __forceinline__ bool row_needs_exact_max(float l) {
+  return !(l < kMaxSum) || (F8 == 2 && !(l > kMinSum));
+}
+
 // One full pass over the keys whose first tiles stage_first has issued: the
 // unmasked tiles (unrolled by the stage count), the partial last tile (if
 // any) with masking, then the PV of the last step.  Returns true if some
 // row's sum outgrew its reference.  NST > 0: the first tiles were issued
 // before the previous tile's NST output and LSE stores, so the first two
 // waits leave those stores in flight.
-template <int D, bool F8, int NST, int QB>
+template <int D, int F8, int NST, bool FB = false, int QB>
 __device__ __forceinline__ bool run_pass_body(Frags<D, F8, QB>& f, PassCtx<D, F8>& x) {
   using Gm = Geo<D>;
   constexpr bool PF = NST > 0;
@@ -618,24 +646,24 @@ __device__ __forceinline__ bool run_pass_body(Frags<D, F8, QB>& f, PassCtx<D, F8
   const int nmid = x.ntiles - 1;  // tiles before the last
   int t = 0;
   if (PF && nmid >= kStages) {  // no load is issued between the first wait and trip 0's
-    tile_trip<D, F8, 0, false, NST>(0, f, S0, S1, Pa, Pb, x);
-    tile_trip<D, F8, 1, false>(1, f, S0, S1, Pa, Pb, x);
-    tile_trip<D, F8, 2, false>(2, f, S0, S1, Pa, Pb, x);
+    tile_trip<D, F8, 0, false, NST, false, FB>(0, f, S0, S1, Pa, Pb, x);
+    tile_trip<D, F8, 1, false, 0, false, FB>(1, f, S0, S1, Pa, Pb, x);
+    tile_trip<D, F8, 2, false, 0, false, FB>(2, f, S0, S1, Pa, Pb, x);
     t = kStages;
   }
   for (; t + kStages <= nmid; t += kStages) {
-    tile_trip<D, F8, 0, false>(t, f, S0, S1, Pa, Pb, x);
-    tile_trip<D, F8, 1, false>(t + 1, f, S0, S1, Pa, Pb, x);
-    tile_trip<D, F8, 2, false>(t + 2, f, S0, S1, Pa, Pb, x);
+    tile_trip<D, F8, 0, false, 0, false, FB>(t, f, S0, S1, Pa, Pb, x);
+    tile_trip<D, F8, 1, false, 0, false, FB>(t + 1, f, S0, S1, Pa, Pb, x);
+    tile_trip<D, F8, 2, false, 0, false, FB>(t + 2, f, S0, S1, Pa, Pb, x);
   }
-  for (; t < nmid; ++t) tile_trip<D, F8, -1, false>(t, f, S0, S1, Pa, Pb, x);
+  for (; t < nmid; ++t) tile_trip<D, F8, -1, false, 0, false, FB>(t, f, S0, S1, Pa, Pb, x);
   // the last tile, masked whether or not it is partial (one instantiation
   // for both keeps the kernel within its registers)
-  tile_trip<D, F8, -1, true, 0, true>(t, f, S0, S1, Pa, Pb, x);
+  tile_trip<D, F8, -1, true, 0, true, FB>(t, f, S0, S1, Pa, Pb, x);
   pv_step<D, F8>(f, Pa, VSTAGE(x, -1, x.ntiles - 1) + 32 * Gm::ROWB, x);
   bool flag = false;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) flag |= !(quad_sum(f.l[qb]) < kMaxSum);
+  for (int qb = 0; qb < QB; ++qb) flag |= row_needs_exact_max<F8>(quad_sum(f.l[qb]));
   return flag;
 }
 
@@ -643,7 +671,7 @@ __device__ __forceinline__ bool run_pass_body(Frags<D, F8, QB>& f, PassCtx<D, F8
 // outgrew theirs (only when the fixed-reference loop flagged some row); the
 // other rows keep their first reference, so a row's result does not depend
 // on which rows share its tile.
-template <int D, bool F8, int QB>
+template <int D, int F8, int QB>
 __device__ __forceinline__ void exact_max_pass(Frags<D, F8, QB>& f, PassCtx<D, F8>& x) {
   using QK = QKOps<D, F8>;
   float m[QB];
@@ -667,7 +695,7 @@ __device__ __forceinline__ void exact_max_pass(Frags<D, F8, QB>& f, PassCtx<D, F
   __syncthreads();
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
-    if (!(quad_sum(f.l[qb]) < kMaxSum)) f.m[qb] = m[qb];
+    if (row_needs_exact_max<F8>(quad_sum(f.l[qb]))) f.m[qb] = m[qb];
 }
 
 // Where the tokens of one (b, h) live.  Contiguous [B,H,N,D] tensors are one
@@ -734,10 +762,10 @@ struct TileInfo {
   const char* Vb;
   const __bf16* qtxt;   // JOINT: the head's text and image queries
   const __bf16* qimg;
-  float c;              // softmax constant (F8: times the head's descales)
+  float c;              // softmax constant (F8: times the head's descales; mode 2: unused)
 };
 
-template <int D, bool F8, bool SPLIT, bool JOINT>
+template <int D, int F8, bool SPLIT, bool JOINT>
 __device__ __forceinline__ TileInfo tile_info(int u, int total, int n_qtiles, int Nkv, const Layout& lay,
                                               const void* K, const __bf16* V, float c,
                                               const float* qds, const float* kds, const Split& sp,
@@ -768,7 +796,7 @@ __device__ __forceinline__ TileInfo tile_info(int u, int total, int n_qtiles, in
   // segment starts are B*H*kseg rows apart; the jump is from one segment's end
   // (only key-split launches start inside a segment, and they have one)
   ti.vjump = ((int64_t)lay.B * lay.htot - 1) * lay.kseg * D * 2;
-  ti.c = F8 ? c * qds[ti.bh] * kds[ti.bh] : c;
+  ti.c = F8 == 1 ? c * qds[ti.bh] * kds[ti.bh] : c;
   ti.qtxt = ti.qimg = nullptr;
   if (JOINT) {  // contiguous layout: bh = b * H + h, head h of the image, h0 + h of the text
     const int64_t th = (int64_t)bb * ja.Ht + ja.h0 + hh, ih = (int64_t)bb * lay.htot + hh;
@@ -794,7 +822,7 @@ __device__ __forceinline__ TileInfo tile_info(int u, int total, int n_qtiles, in
 
 // The lane's query row pointers of a unit, one per 16-row block (rows past
 // Nq point at row Nq - 1).
-template <int D, bool F8, int QB>
+template <int D, int F8, int QB>
 __device__ __forceinline__ void query_rows(const char* (&rows)[2], const TileInfo& ti, const void* Q,
                                            int Nq, const Layout& lay, int64_t qsstride, int wave,
                                            int c16) {
@@ -813,7 +841,7 @@ __device__ __forceinline__ void query_rows(const char* (&rows)[2], const TileInf
 // first), turned by its part's rotary table when the part has one; the
 // fragment of k-step ks holds channel pairs 16 ks + 4 g .. +3 of the lane's
 // token, one per 32-bit word.
-template <int D, bool F8, bool JOINT, int QB>
+template <int D, int F8, bool JOINT, int QB>
 __device__ __forceinline__ void begin_tile(Frags<D, F8, QB>& f, PassCtx<D, F8>& x, const TileInfo& ti,
                                            const void* Q, int Nq, const Layout& lay,
                                            int64_t qsstride, int c16, const JointArgs& ja,
@@ -866,7 +894,7 @@ __device__ __forceinline__ void begin_tile(Frags<D, F8, QB>& f, PassCtx<D, F8>& 
 // would also wait for every outstanding vector memory operation, here the
 // next unit's query loads.  The words are next written a unit later, after
 // barriers every wave has passed, so no wave still reads them then.
-template <int D, bool F8>
+template <int D, int F8>
 __device__ __forceinline__ bool any_row_flagged(const PassCtx<D, F8>& x, bool flag) {
   const bool w = __builtin_amdgcn_ballot_w64(flag) != 0;
   if (x.lane == 0) x.anyw[x.wave] = w;
@@ -886,12 +914,12 @@ __device__ __forceinline__ bool any_row_flagged(const PassCtx<D, F8>& x, bool fl
 // with the LDS stages.
 // NST: output store instructions per wave still in flight from the previous
 // unit (0 for the first unit).
-template <int D, bool F8, int NST, int QB>
+template <int D, int F8, int NST, int QB>
 __device__ __forceinline__ void compute_tile(Frags<D, F8, QB>& f, PassCtx<D, F8>& x) {
   using Gm = Geo<D>;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    f.m[qb] = -INFINITY;
+    f.m[qb] = F8 == 2 ? 0.0f : -INFINITY;  // mode 2: no reference max on the first attempt
     f.l[qb] = 0.f;
     f.lb[qb] = f32x4{};
 #pragma unroll
@@ -909,7 +937,7 @@ __device__ __forceinline__ void compute_tile(Frags<D, F8, QB>& f, PassCtx<D, F8>
       for (int db = 0; db < Gm::DB; ++db) f.o[qb][db] = f32x4{};
     }
     stage_first<D, F8>(x);
-    run_pass_body<D, F8, 0>(f, x);
+    run_pass_body<D, F8, 0, F8 == 2>(f, x);
     __syncthreads();
   }
 }
@@ -937,7 +965,7 @@ constexpr int kStoreInsts = QB * ((OUT_F32 ? Geo<D>::DB : Geo<D>::DB / 2) + 1);
 // share 1%, the long shapes unchanged); the price is that a row's four
 // 64-byte pieces reach memory uncombined.  Float32 output (Ring partials)
 // gains nothing from it, so it is stored as usual.
-template <int D, bool OUT_F32, bool F8, bool SPLIT, int QB>
+template <int D, bool OUT_F32, int F8, bool SPLIT, int QB>
 __device__ __forceinline__ void store_tile(const Frags<D, F8, QB>& f, const TileInfo& ti, void* Oout,
                                            float* LSE, int Nq, const Layout& lay, int64_t qsstride,
                                            const Split& sp, int wave, int c16, int g) {
@@ -980,7 +1008,8 @@ __device__ __forceinline__ void store_tile(const Frags<D, F8, QB>& f, const Tile
                                : (int64_t)ti.bh * Nq + r0;
     const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
         LSE ? (void*)(LSE + lrow) : nullptr, (short)0, LSE ? 64 : 0, 0x00020000);
-    const float lse = (f.m[qb] * ti.c + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
+    const float lse = ((F8 == 2 ? f.m[qb] : f.m[qb] * ti.c) + __builtin_amdgcn_logf(l_tot)) *
+                      0.6931471805599453f;
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse), lr,
                                           g == 0 ? (qrow - r0) * 4 : (1 << 30), 0, 0);
   }
@@ -998,7 +1027,7 @@ __device__ __forceinline__ void store_tile(const Frags<D, F8, QB>& f, const Tile
 // per-(b, h) factors qds[bh] * kds[bh]; else q and k are bf16 and qds, kds
 // are unused.  SPLIT: a key-split launch, total_tiles is then the number of
 // units.
-template <int D, bool OUT_F32, bool F8, bool SPLIT = false, bool JOINT = false, int QB = kQB,
+template <int D, bool OUT_F32, int F8, bool SPLIT = false, bool JOINT = false, int QB = kQB,
           bool STR = false>
 __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const void* __restrict__ K,
                                               const __bf16* __restrict__ V, void* __restrict__ Oout,
@@ -1076,6 +1105,14 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
   int u = blockIdx.x;
   TileInfo ti =
       tile_info<D, F8, SPLIT, JOINT>(u, total_tiles, n_qtiles, Nkv, lay, K, V, c, qds, kds, sp, ja);
+  // fp8 mode 2: the descales are powers of two; their biased exponent fields
+  // are the E8M0 scales of the key and query products (127 = 2^0)
+  auto set_scales = [&](int bh) {
+    // (read into scalar registers: the head is the same for the whole workgroup)
+    x.sa = F8 == 2 ? __builtin_amdgcn_readfirstlane((int)((__float_as_uint(kds[bh]) >> 23) & 0xff)) : 127;
+    x.sb = F8 == 2 ? __builtin_amdgcn_readfirstlane((int)((__float_as_uint(qds[bh]) >> 23) & 0xff)) : 127;
+  };
+  set_scales(ti.bh);
   begin_tile<D, F8, JOINT>(f, x, ti, Q, Nq, lay, qsstride, c16, ja, true);
   point_next(u + gridDim.x);
   compute_tile<D, F8, 0>(f, x);
@@ -1086,6 +1123,7 @@ __device__ __forceinline__ void attn_fwd_body(const void* __restrict__ Q, const 
     if (more) {
       tn = tile_info<D, F8, SPLIT, JOINT>(un, total_tiles, n_qtiles, Nkv, lay, K, V, c, qds, kds,
                                           sp, ja);
+      set_scales(tn.bh);
       begin_tile<D, F8, JOINT>(f, x, tn, Q, Nq, lay, qsstride, c16, ja, !x.nqv);
     }
     // the next unit's loads stay ahead of this unit's stores
@@ -1123,14 +1161,17 @@ void attn_fwd_bf16_split_kernel(const __bf16* __restrict__ Q, const __bf16* __re
                                       nullptr, nullptr, sp);
 }
 
-template <bool OUT_F32>
+// MODE 1: any per-head descales, scores scale * qds * kds * (q . k);
+// MODE 2: power-of-two descales and the softmax constant folded into the
+// query codes, scores in base 2 qds * kds * (q . k) from the scaled product.
+template <bool OUT_F32, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void attn_fwd_fp8_kernel(const unsigned char* __restrict__ Q, const unsigned char* __restrict__ K,
                          const __bf16* __restrict__ V, void* __restrict__ Oout,
                          float* __restrict__ LSE, int Nq, int Nkv, int n_qtiles, int total_tiles,
                          float c, Layout lay, const float* __restrict__ qds,
                          const float* __restrict__ kds) {
-  attn_fwd_body<128, OUT_F32, true>(Q, K, V, Oout, LSE, Nq, Nkv, n_qtiles, total_tiles, c, lay,
+  attn_fwd_body<128, OUT_F32, MODE>(Q, K, V, Oout, LSE, Nq, Nkv, n_qtiles, total_tiles, c, lay,
                                     qds, kds);
 }
 
@@ -1213,14 +1254,14 @@ hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float*
   return hipGetLastError();
 }
 
-template <bool OUT_F32>
+template <bool OUT_F32, int MODE>
 hipError_t launch_fp8(const void* q, const void* k, const void* v, const float* qds,
                       const float* kds, void* o, float* lse, int Nq, int Nkv, float c,
                       const Layout& lay, hipStream_t stream) {
   const int n_qtiles = (Nq + kBM - 1) / kBM;
   const int64_t total = (int64_t)lay.B * lay.hg * n_qtiles;
   if (total > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<OUT_F32>), dim3(persistent_grid(total)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<OUT_F32, MODE>), dim3(persistent_grid(total)), dim3(kThreads), 0,
                      stream, static_cast<const unsigned char*>(q),
                      static_cast<const unsigned char*>(k), static_cast<const __bf16*>(v), o, lse,
                      Nq, Nkv, n_qtiles, (int)total, c, lay, qds, kds);
@@ -1326,8 +1367,16 @@ hipError_t launch_attn_fp8(const void* q, const void* k, const void* v, const fl
                            int Nkv, float scale, bool o_f32, hipStream_t stream) {
   const Layout lay{Nq, Nkv, H, H, 0, B, 0};
   const float c = scale * 1.4426950408889634f;
-  return o_f32 ? launch_fp8<true>(q, k, v, q_descale, k_descale, o, lse, Nq, Nkv, c, lay, stream)
-               : launch_fp8<false>(q, k, v, q_descale, k_descale, o, lse, Nq, Nkv, c, lay, stream);
+  return o_f32 ? launch_fp8<true, 1>(q, k, v, q_descale, k_descale, o, lse, Nq, Nkv, c, lay, stream)
+               : launch_fp8<false, 1>(q, k, v, q_descale, k_descale, o, lse, Nq, Nkv, c, lay, stream);
+}
+
+hipError_t launch_attn_fp8_mx(const void* q, const void* k, const void* v, const float* q_descale,
+                              const float* k_descale, void* o, float* lse, int B, int H, int Nq,
+                              int Nkv, bool o_f32, hipStream_t stream) {
+  const Layout lay{Nq, Nkv, H, H, 0, B, 0};
+  return o_f32 ? launch_fp8<true, 2>(q, k, v, q_descale, k_descale, o, lse, Nq, Nkv, 1.0f, lay, stream)
+               : launch_fp8<false, 2>(q, k, v, q_descale, k_descale, o, lse, Nq, Nkv, 1.0f, lay, stream);
 }
 
 hipError_t launch_attn_bf16_ulysses(const void* q, const void* k, const void* v, void* o,

@@ -50,6 +50,12 @@ hipError_t launch_attn_fp8(const void* q, const void* k, const void* v, const fl
                            const float* k_descale, void* o, float* lse, int B, int H, int Nq,
                            int Nkv, float scale, bool o_f32, hipStream_t stream);
 
+// The same with power-of-two descales, scores in base 2 (the queries' codes
+// carry scale * log2(e)): see dit_attn_fwd_fp8_mx.
+hipError_t launch_attn_fp8_mx(const void* q, const void* k, const void* v, const float* q_descale,
+                              const float* k_descale, void* o, float* lse, int B, int H, int Nq,
+                              int Nkv, bool o_f32, hipStream_t stream);
+
 // bf16 x [B,H,N,D] -> E4M3 codes [B,H,N,D] and float32 descale [B,H] (D % 8 == 0).
 hipError_t launch_quant_fp8(const void* x, void* codes, float* descale, int B, int H, int N, int D,
                             hipStream_t stream);
@@ -57,6 +63,11 @@ hipError_t launch_quant_fp8(const void* x, void* codes, float* descale, int B, i
 // three launches.
 hipError_t launch_quant_fp8_n(const void* const* x, void* const* codes, float* const* descale,
                               const int* N, int ntensors, int B, int H, int D, hipStream_t stream);
+// q and k of one attention call with power-of-two descales, q multiplied by
+// c0 = scale * log2(e) (float32) before it is scaled (dit_quant_fp8_qk_mx).
+hipError_t launch_quant_fp8_mx(const void* q, const void* k, void* q_codes, void* k_codes,
+                               float* q_descale, float* k_descale, int B, int H, int Nq, int Nkv,
+                               int D, float c0, hipStream_t stream);
 
 // Backward, bf16 q/k/v/o/dout (head dim 32, 64 or 128), float32 lse in,
 // delta out ([B,H,Nq]), float32 dq/dk/dv.

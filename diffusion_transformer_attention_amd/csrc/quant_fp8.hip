@@ -18,6 +18,12 @@
 // block would store the same value, so the order of these stores does not
 // matter).  HBM-bound: x is read twice and the codes written once (5 bytes
 // per element).
+// Power-of-two form (q and k of one attention call, for the fp8 product that
+// takes E8M0 scales): x' = float32(x * pre) with pre = scale * log2(e) for q
+// and 1 for k; descale = the smallest 2^e (e >= -126) with max |x'| <= 448 *
+// 2^e (1 for an all-zero head); code = E4M3(x' / descale), the quotient
+// exact.  max |x'| = float32(amax * pre), rounding being monotonic, so the
+// same amax pass serves.
 #include "launch.h"
 
 namespace ditattn {
@@ -38,7 +44,9 @@ struct QuantJob {
   unsigned* word[2];       // the descale buffers, as words
   int64_t vec_per_head[2];  // 16-byte vectors per head (0: empty tensor)
   int blocks[2];            // blocks per head of the pass
+  float pre[2];             // power-of-two form: factor applied to x first
   int ntensors, nbh;
+  int pow2;                 // power-of-two descales
 };
 
 // Block ids: tensor 0's heads first, then tensor 1's; within a tensor, head
@@ -105,9 +113,23 @@ __device__ __forceinline__ float descale_of(unsigned amax_bits) {
   return a > 0.0f ? __fdiv_rn(a, kE4M3Max) : 1.0f;
 }
 
+// Smallest power of two d (d >= 2^-126) with a <= 448 d, for a >= 0 (1 for
+// a = 0).  a = (1 + M 2^-23) 2^k and 448 = 1.75 2^8, so d = 2^(k-8) when
+// M <= 0.75 2^23 and 2^(k-7) otherwise; subnormal a takes 2^-126.
+__device__ __forceinline__ float pow2_descale_of(float a) {
+  if (!(a > 0.0f)) return 1.0f;
+  const unsigned bits = __float_as_uint(a);
+  const int E = (int)(bits >> 23), M = (int)(bits & 0x7fffffu);
+  int e = E == 0 ? -126 : (E - 127) - (M <= 0x600000 ? 8 : 7);
+  e = e < -126 ? -126 : e;
+  return __uint_as_float((unsigned)(e + 127) << 23);
+}
+
 // The head's descale from its word: an amax (top bit set) or the descale.
-__device__ __forceinline__ float descale_from_word(unsigned w) {
-  return (w & kAmaxTag) ? descale_of(w & ~kAmaxTag) : __uint_as_float(w);
+__device__ __forceinline__ float descale_from_word(unsigned w, float pre, int pow2) {
+  if (!(w & kAmaxTag)) return __uint_as_float(w);
+  const unsigned a = w & ~kAmaxTag;
+  return pow2 ? pow2_descale_of(__fmul_rn(__uint_as_float(a), pre)) : descale_of(a);
 }
 
 __device__ __forceinline__ float quotient(float v, float d) {
@@ -118,7 +140,10 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantJob j) {
   int t, bh, chunk;
   block_of(j, t, bh, chunk);
   const int64_t vph = j.vec_per_head[t];
-  const float d = descale_from_word(__atomic_load_n(j.word[t] + bh, __ATOMIC_RELAXED));
+  const float pre = j.pre[t];
+  const float d = descale_from_word(__atomic_load_n(j.word[t] + bh, __ATOMIC_RELAXED), pre, j.pow2);
+  // x' = x * pre in the power-of-two form (pre = 1 otherwise: x' = x exactly)
+  auto xv = [&](unsigned bits) { return __fmul_rn(__uint_as_float(bits), pre); };
   const u32x4* src = j.x[t] + (int64_t)bh * vph;
   u32x2* dst = j.codes[t] + (int64_t)bh * vph;
   u32x4 v[kVec];
@@ -135,11 +160,10 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantJob j) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const unsigned w0 = v[u][2 * h], w1 = v[u][2 * h + 1];
-        unsigned r = __builtin_amdgcn_cvt_pk_fp8_f32(quotient(__uint_as_float(w0 << 16), d),
-                                                     quotient(__uint_as_float(w0 & 0xffff0000u), d),
-                                                     0, false);
-        r = __builtin_amdgcn_cvt_pk_fp8_f32(quotient(__uint_as_float(w1 << 16), d),
-                                            quotient(__uint_as_float(w1 & 0xffff0000u), d), r, true);
+        unsigned r = __builtin_amdgcn_cvt_pk_fp8_f32(quotient(xv(w0 << 16), d),
+                                                     quotient(xv(w0 & 0xffff0000u), d), 0, false);
+        r = __builtin_amdgcn_cvt_pk_fp8_f32(quotient(xv(w1 << 16), d),
+                                            quotient(xv(w1 & 0xffff0000u), d), r, true);
         out[h] = r;
       }
       // streaming store: the codes are not read again by this call
@@ -154,12 +178,14 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantJob j) {
 
 }  // namespace
 
-hipError_t launch_quant_fp8_n(const void* const* x, void* const* codes, float* const* descale,
-                              const int* N, int ntensors, int B, int H, int D,
-                              hipStream_t stream) {
+namespace {
+hipError_t launch_quant(const void* const* x, void* const* codes, float* const* descale,
+                        const int* N, int ntensors, int B, int H, int D, const float* pre, int pow2,
+                        hipStream_t stream) {
   QuantJob j{};
   j.ntensors = ntensors;
   j.nbh = B * H;
+  j.pow2 = pow2;
   const int64_t per_block = (int64_t)kVec * kThreads;
   int64_t qblocks = 0, ablocks = 0;
   for (int t = 0; t < ntensors; ++t) {
@@ -167,6 +193,7 @@ hipError_t launch_quant_fp8_n(const void* const* x, void* const* codes, float* c
     j.codes[t] = static_cast<u32x2*>(codes[t]);
     j.word[t] = reinterpret_cast<unsigned*>(descale[t]);
     j.vec_per_head[t] = (int64_t)N[t] * D / 8;
+    j.pre[t] = pre[t];
     const int64_t bph = (j.vec_per_head[t] + per_block - 1) / per_block;
     if (bph * j.nbh > 0x3fffffff) return hipErrorInvalidValue;
     qblocks += bph * j.nbh;
@@ -186,10 +213,29 @@ hipError_t launch_quant_fp8_n(const void* const* x, void* const* codes, float* c
   }
   return hipGetLastError();
 }
+}  // namespace
+
+hipError_t launch_quant_fp8_n(const void* const* x, void* const* codes, float* const* descale,
+                              const int* N, int ntensors, int B, int H, int D,
+                              hipStream_t stream) {
+  const float one[2] = {1.0f, 1.0f};
+  return launch_quant(x, codes, descale, N, ntensors, B, H, D, one, 0, stream);
+}
 
 hipError_t launch_quant_fp8(const void* x, void* codes, float* descale, int B, int H, int N, int D,
                             hipStream_t stream) {
   return launch_quant_fp8_n(&x, &codes, &descale, &N, 1, B, H, D, stream);
+}
+
+hipError_t launch_quant_fp8_mx(const void* q, const void* k, void* q_codes, void* k_codes,
+                               float* q_descale, float* k_descale, int B, int H, int Nq, int Nkv,
+                               int D, float c0, hipStream_t stream) {
+  const void* x[2] = {q, k};
+  void* c[2] = {q_codes, k_codes};
+  float* ds[2] = {q_descale, k_descale};
+  const int n[2] = {Nq, Nkv};
+  const float pre[2] = {c0, 1.0f};
+  return launch_quant(x, c, ds, n, 2, B, H, D, pre, 1, stream);
 }
 
 }  // namespace ditattn

@@ -353,6 +353,46 @@ int dit_attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q
                      int D, float scale, int o_dtype, void* stream);
 
 /*
+ * FP8 with power-of-two scales, for the fp8 product that applies E8M0
+ * (power-of-two) scales itself ([HC]; this library's second reading of the
+ * FP8 step): the queries of one attention call are first multiplied in
+ * float32 by c0 = scale * log2(e) (c0 the float32 product of the two), so
+ * that the scaled products are the scores in base 2.  Per (b, h) and tensor,
+ * with x' = float32(x * c0) for q and x' = k for k:
+ *
+ *   descale[b,h] = the smallest power of two 2^e (e >= -126) with
+ *                  max |x'| <= 448 * 2^e over the head; 1 for an all-zero
+ *                  (or empty) head
+ *   code         = E4M3 of x' / descale (exact quotient), nearest-even
+ *
+ *   q : bf16 [B,H,Nq,D] -> q_codes uint8 [B,H,Nq,D], q_descale float32 [B,H]
+ *   k : bf16 [B,H,Nkv,D] -> k_codes uint8 [B,H,Nkv,D], k_descale float32 [B,H]
+ *   scale : the softmax scale dit_attn_fwd_fp8_mx will apply (> 0, finite)
+ * Three launches, as dit_quant_fp8_qk; alignment and errors as dit_quant_fp8_qk.
+ */
+int dit_quant_fp8_qk_mx(const void* q, const void* k, void* q_codes, void* k_codes,
+                        float* q_descale, float* k_descale, int B, int H, int Nq, int Nkv, int D,
+                        float scale, void* stream);
+
+/*
+ * Attention of codes from dit_quant_fp8_qk_mx ([HC], reading as above): the
+ * scores in base 2 are
+ *
+ *   s_ij = q_descale[b,h] * k_descale[b,h] * (q_i . k_j)   (codes decoded),
+ *
+ * P_ij = 2^s_ij / sum_j 2^s_ij, O = P V with P and V in bf16, LSE = ln 2 *
+ * log2 sum_j 2^s_ij (natural log).  The descales must be powers of two
+ * (normal floats), as dit_quant_fp8_qk_mx writes them: the kernel passes
+ * their exponents to the fp8 matrix instruction as its E8M0 scales and starts
+ * each score accumulation at minus the row's reference maximum, so the
+ * softmax needs no multiply.  Arguments as dit_attn_fwd_fp8 without `scale`
+ * (it is in the query codes).  D must be 128.
+ */
+int dit_attn_fwd_fp8_mx(const void* q, const void* k, const void* v, const float* q_descale,
+                        const float* k_descale, void* o, float* lse, int B, int H, int Nq, int Nkv,
+                        int D, int o_dtype, void* stream);
+
+/*
  * Ulysses sequence -> head exchange as it lands on one device ([HB] Ulysses
  * simulation, all_to_all_heads): P token shards become P head groups.
  *

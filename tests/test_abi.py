@@ -279,6 +279,34 @@ def test_attn_fp8_validation(lib):
     assert f(Nq=0) == dta.DIT_OK
 
 
+def test_quant_fp8_qk_mx_validation(lib):
+    def qk(q=A, k=A, qc=A, kc=A, qd=A, kd=A, B=1, H=2, Nq=64, Nkv=32, D=128, scale=0.125):
+        return lib.dit_quant_fp8_qk_mx(q, k, qc, kc, qd, kd, B, H, Nq, Nkv, D,
+                                       ctypes.c_float(scale), S)
+    assert qk(D=96) == dta.DIT_EUNSUPPORTED
+    assert qk(scale=0.0) == dta.DIT_EINVAL
+    assert qk(scale=float("inf")) == dta.DIT_EINVAL
+    assert qk(qd=NULL) == dta.DIT_EINVAL
+    assert qk(k=NULL) == dta.DIT_EINVAL
+    assert qk(kc=V(0x10004)) == dta.DIT_EALIGN
+    assert qk(q=MIS) == dta.DIT_EALIGN
+    assert qk(Nkv=-1) == dta.DIT_EINVAL
+    assert qk(B=0) == dta.DIT_OK
+    assert qk(B=2 ** 20, H=2 ** 12, Nq=1, Nkv=1, D=32) == dta.DIT_ERANGE
+
+
+def test_attn_fp8_mx_validation(lib):
+    def f(q=A, qd=A, kd=A, o=A, lse=A, Nq=64, Nkv=64, D=128, od=0):
+        return lib.dit_attn_fwd_fp8_mx(q, A, A, qd, kd, o, lse, 1, 2, Nq, Nkv, D, od, S)
+    assert f(D=64) == dta.DIT_EUNSUPPORTED
+    assert f(od=5) == dta.DIT_EUNSUPPORTED
+    assert f(qd=NULL) == dta.DIT_EINVAL
+    assert f(Nkv=0) == dta.DIT_EINVAL
+    assert f(q=MIS) == dta.DIT_EALIGN
+    assert f(kd=V(0x10002)) == dta.DIT_EALIGN
+    assert f(Nq=0) == dta.DIT_OK
+
+
 @pytest.mark.parametrize("fn", ["ulysses_seq2head", "ulysses_head2seq"])
 def test_permute_validation(lib, fn):
     f = getattr(lib, fn)
