@@ -27,7 +27,9 @@ attention alone; the cross leg times dit_attn_fwd_block of the 10-head share's
 32768 queries over 512 text keys.
 
 The fp8 leg quantizes the share's q and k per head to E4M3 (dit_quant_fp8_qk)
-and times dit_attn_fwd_fp8 on them (same FLOP count as the bf16 launch).  Two
+and times dit_attn_fwd_fp8 on them (same FLOP count as the bf16 launch), then
+the same with power-of-two scales and the softmax constant in the query codes
+(dit_quant_fp8_qk_mx, dit_attn_fwd_fp8_mx).  Two
 more bf16 forward legs: all 40 heads of the draw in one call, and the
 [1,10,75600,128] long-video shape.
 
@@ -361,7 +363,16 @@ def main():
                      "fp8_attn_TFLOPs": flops_launch / (fp8_ms * 1e-3) / 1e12,
                      "fp8_quant_qk_ms": quant_ms,
                      "fp8_quant_qk_GBps": qbytes / (quant_ms * 1e-3) / 1e9})
-        del qc, kc, fo, fl
+        # power-of-two form: the quantizer folds the softmax constant into q
+        mqc, mkc, mqd, mkd = dta.dit_quant_fp8_qk_mx(q0, k0, None, qc, kc, qd, kd)
+        mx_quant_ms = time_it(lambda: dta.dit_quant_fp8_qk_mx(q0, k0, None, mqc, mkc, mqd, mkd),
+                              reps=10)
+        mx_ms = time_it(lambda: dta.dit_attn_fwd_fp8_mx(mqc, mkc, v0, mqd, mkd, out=fo, lse=fl),
+                        reps=5)
+        legs.update({"fp8_mx_attn_ms": mx_ms,
+                     "fp8_mx_attn_TFLOPs": flops_launch / (mx_ms * 1e-3) / 1e12,
+                     "fp8_mx_quant_qk_ms": mx_quant_ms})
+        del qc, kc, fo, fl, mqc, mkc
 
         # single-pass ring-merge shape: all 40 heads of the [1,40,32768,128]
         # draw in one dit_attn_fwd (the full head count the ring blocks cover)
