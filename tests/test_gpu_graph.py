@@ -4,7 +4,8 @@ The entry points enqueue kernels only (no allocation, copy or memset) on the
 caller's stream, so a caller can capture a whole step once and replay it.
 The step captured here: the Ulysses round trip (seq2head, attention of each
 head group with LSE, head2seq), the backward of head group 0, per-head FP8
-quantization followed by FP8 attention, a joint text + image call and a
+quantization followed by FP8 attention, the paired quantizer with
+power-of-two scales followed by its FP8 attention, a joint text + image call and a
 work-balanced call that takes its key-split path (its device query runs
 under capture too).  It is
 replayed three times, with unrelated eager launches and synchronizations in
@@ -63,6 +64,12 @@ def _buffers(shards):
         "kd": torch.empty((B, H // P), device="cuda", dtype=torch.float32),
         "o8": torch.empty((B, H // P, N, D), device="cuda", dtype=torch.bfloat16),
         "l8": torch.empty((B, H // P, N), device="cuda", dtype=torch.float32),
+        "qcx": torch.empty((B, H // P, N, D), device="cuda", dtype=torch.uint8),
+        "kcx": torch.empty((B, H // P, N, D), device="cuda", dtype=torch.uint8),
+        "qdx": torch.empty((B, H // P), device="cuda", dtype=torch.float32),
+        "kdx": torch.empty((B, H // P), device="cuda", dtype=torch.float32),
+        "ox": torch.empty((B, H // P, N, D), device="cuda", dtype=torch.bfloat16),
+        "lx": torch.empty((B, H // P, N), device="cuda", dtype=torch.float32),
         "oj": torch.empty((B, H, 377, D), device="cuda", dtype=torch.bfloat16),
         "lj": torch.empty((B, H, 377), device="cuda", dtype=torch.float32),
         "ws": torch.empty((3, B, H, 377, D), device="cuda", dtype=torch.bfloat16),
@@ -86,13 +93,16 @@ def _step(shards, dout, joint, tabs, b):
     dta.dit_quant_fp8(q0, codes=b["qc"], descale=b["qd"])
     dta.dit_quant_fp8(k0, codes=b["kc"], descale=b["kd"])
     dta.dit_attn_fwd_fp8(b["qc"], b["kc"], v0, b["qd"], b["kd"], out=b["o8"], lse=b["l8"])
+    dta.dit_quant_fp8_qk_mx(q0, k0, q_codes=b["qcx"], k_codes=b["kcx"], q_descale=b["qdx"],
+                            k_descale=b["kdx"])
+    dta.dit_attn_fwd_fp8_mx(b["qcx"], b["kcx"], v0, b["qdx"], b["kdx"], out=b["ox"], lse=b["lx"])
     dta.dit_attn_fwd_joint(*joint[:6], *tabs, out=b["oj"], lse=b["lj"], workspace=b["ws"])
     dta.dit_attn_fwd_balanced(*joint[6], out=b["ob"], lse=b["lb"], workspace=b["wb"])
 
 
 def _snapshot(b):
-    keys = ("back", "lse", "dq", "dk", "dv", "delta", "qc", "kc", "qd", "kd", "o8", "l8", "oj", "lj",
-            "ob", "lb")
+    keys = ("back", "lse", "dq", "dk", "dv", "delta", "qc", "kc", "qd", "kd", "o8", "l8", "qcx",
+            "kcx", "qdx", "kdx", "ox", "lx", "oj", "lj", "ob", "lb")
     return {k: b[k].clone() for k in keys}
 
 
