@@ -369,6 +369,9 @@ int dit_attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q
  *   k : bf16 [B,H,Nkv,D] -> k_codes uint8 [B,H,Nkv,D], k_descale float32 [B,H]
  *   scale : the softmax scale dit_attn_fwd_fp8_mx will apply (> 0, finite)
  * Three launches, as dit_quant_fp8_qk; alignment and errors as dit_quant_fp8_qk.
+ * The products x * c0 must stay within float32's range (they do unless c0 > 1
+ * and |q| is within a factor c0 of the bf16 maximum): a head where one
+ * overflows gets unspecified codes and descale, as does a head holding NaN.
  */
 int dit_quant_fp8_qk_mx(const void* q, const void* k, void* q_codes, void* k_codes,
                         float* q_descale, float* k_descale, int B, int H, int Nq, int Nkv, int D,
